@@ -1,0 +1,553 @@
+/*
+ * TAH-Quant reference oracle — TEST INFRASTRUCTURE ONLY (see tah_ref.h).
+ *
+ * Source of every step: "TAH-Quant: Effective Activation Quantization in
+ * Pipeline Parallelism over Slow Network" (arXiv 2506.01352v2):
+ *   §3.1  tile-wise group quantization (tile of G contiguous channels per token,
+ *         own scale and zero-point per tile);
+ *   §3.2  allocation tiles, Eq. (1) normalized magnitudes, Eq. (2) entropy,
+ *         top-p% selection per sample, 1-bit width map;
+ *   §3.3  Eq. (3) outlier ratio vs tau, pivot swap P_d, Eq. (4) tile-local
+ *         Hadamard, asymmetric uniform quantizer, inverse by H^T;
+ *   §3.4  mixed precisions + metadata packed into one fixed-size uint8 stream;
+ *   Algorithm 1 (lines 4-5): sender quantizes, receiver dequantizes;
+ *   Appendix F: tau = 0 always transforms, tau = inf never does.
+ * The Sylvester ordering of H_G follows the Hadamard quantizer section of
+ * "Training Transformers with 4-bit Integers" (arXiv 2306.11987), and the
+ * low-nibble-first code order follows that paper's INT4 packing appendix.
+ *
+ * Readings where the pages leave a step open are listed in the design doc; the ones
+ * that change numbers are restated next to the code below.
+ *
+ * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared (no fast-math), so
+ * every fp32 operation rounds exactly once, in the order written.
+ */
+#include "tah_ref.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ε (Eq. 1), ς (Eq. 2) and ϱ (Eq. 3): "small positive constants". Reading: 2^-40 each. */
+static const float kEps = 0x1p-40f;
+static const float kSigma = 0x1p-40f;
+static const float kRho = 0x1p-40f;
+
+/* ------------------------------------------------------------------ */
+/* small helpers                                                      */
+/* ------------------------------------------------------------------ */
+
+static uint32_t f2u(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float u2f(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+static float bf16_to_f32(uint16_t h) { return u2f((uint32_t)h << 16); }
+
+/* fp32 -> bf16, round to nearest, ties to even (finite inputs). */
+static uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = f2u(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return (uint16_t)((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+/* Smallest bf16 value >= f, for f >= 0 finite. */
+static uint16_t f32_to_bf16_up(float f) {
+  uint32_t u = f2u(f);
+  if (u & 0xffffu) u = (u & 0xffff0000u) + 0x10000u;
+  return (uint16_t)(u >> 16);
+}
+
+static int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+
+static void put_u8(uint8_t* p, int64_t off, uint32_t v) { p[off] = (uint8_t)v; }
+static void put_u16(uint8_t* p, int64_t off, uint32_t v) {
+  p[off] = (uint8_t)v;
+  p[off + 1] = (uint8_t)(v >> 8);
+}
+static void put_u32(uint8_t* p, int64_t off, uint32_t v) {
+  for (int i = 0; i < 4; ++i) p[off + i] = (uint8_t)(v >> (8 * i));
+}
+static void put_u64(uint8_t* p, int64_t off, uint64_t v) {
+  for (int i = 0; i < 8; ++i) p[off + i] = (uint8_t)(v >> (8 * i));
+}
+static uint32_t get_u16(const uint8_t* p, int64_t off) { return (uint32_t)p[off] | ((uint32_t)p[off + 1] << 8); }
+static uint32_t get_u32(const uint8_t* p, int64_t off) {
+  uint32_t v = 0;
+  for (int i = 0; i < 4; ++i) v |= (uint32_t)p[off + i] << (8 * i);
+  return v;
+}
+
+static int ilog2(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+/* ------------------------------------------------------------------ */
+/* parameters and payload layout                                      */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Width pair and k (§3.2 "Top-p% tile selection"): the paper gives two widths,
+ * INT4 for the top p% of a sample's tiles by entropy and INT3 for the rest.
+ * Reading for a budget B over a candidate list: b_lo = largest candidate <= B,
+ * b_hi = smallest candidate > B (b_lo if none), and p = (B - b_lo)/(b_hi - b_lo),
+ * so k = floor(p * N) tiles of the N in a sample get b_hi and the average code
+ * width never exceeds B. The budget counts code bits only; the paper quotes its
+ * metadata bits separately (§3.4).
+ */
+int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tahref_plan* o) {
+  if (!p || !o) return TAHREF_ERR_INVALID_ARG;
+  memset(o, 0, sizeof(*o));
+  if (tokens < 0 || hidden <= 0) return TAHREF_ERR_INVALID_ARG;
+  int G = p->tile;
+  if (G < 8 || G > 128 || (G & (G - 1))) return TAHREF_ERR_INVALID_ARG;
+  if (hidden % G) return TAHREF_ERR_INVALID_ARG;
+  if (p->n_candidates < 1 || p->n_candidates > 4) return TAHREF_ERR_INVALID_ARG;
+  for (int i = 0; i < p->n_candidates; ++i) {
+    if (p->candidates[i] < 1 || p->candidates[i] > 8) return TAHREF_ERR_INVALID_ARG;
+    if (i > 0 && p->candidates[i] <= p->candidates[i - 1]) return TAHREF_ERR_INVALID_ARG;
+  }
+  if (!isfinite(p->bit_budget)) return TAHREF_ERR_INVALID_ARG;
+  if (isnan(p->tau) || p->tau < 0.0f) return TAHREF_ERR_INVALID_ARG;
+  if (p->tokens_per_sample < 0) return TAHREF_ERR_INVALID_ARG;
+  int64_t S = p->tokens_per_sample == 0 ? tokens : p->tokens_per_sample;
+  if (S > 0 && tokens % S) return TAHREF_ERR_INVALID_ARG;
+  if ((float)p->candidates[0] > p->bit_budget) return TAHREF_ERR_BUDGET_INFEASIBLE;
+
+  int b_lo = p->candidates[0], b_hi = -1;
+  for (int i = 0; i < p->n_candidates; ++i) {
+    if ((float)p->candidates[i] <= p->bit_budget) b_lo = p->candidates[i];
+    else if (b_hi < 0) b_hi = p->candidates[i];
+  }
+  if (b_hi < 0) b_hi = b_lo;
+
+  o->tokens = tokens;
+  o->hidden = hidden;
+  o->S = S;
+  o->nsamples = S > 0 ? tokens / S : 0;
+  o->G = G;
+  o->log2G = ilog2(G);
+  o->M = hidden / G;
+  o->tiles = tokens * o->M;
+  o->tiles_per_sample = S * o->M;
+  o->b_lo = b_lo;
+  o->b_hi = b_hi;
+  if (b_hi == b_lo || o->tiles_per_sample == 0) {
+    o->k = 0;
+  } else {
+    double kk = floor(((double)p->bit_budget - (double)b_lo) * (double)o->tiles_per_sample /
+                      (double)(b_hi - b_lo));
+    o->k = (int64_t)kk;
+  }
+  o->nblocks = (o->tiles + 63) / 64;
+  int64_t nhi = o->k * o->nsamples;
+  o->off_table = 256;
+  o->off_bitmap = align256(o->off_table + 4 * o->nblocks);
+  o->off_side = align256(o->off_bitmap + 8 * o->nblocks);
+  o->off_scale = align256(o->off_side + o->tiles);
+  o->off_zero = align256(o->off_scale + 2 * o->tiles);
+  o->off_codes = align256(o->off_zero + 4 * o->tiles);
+  o->code_bytes = (o->tiles * G * b_lo + nhi * G * (b_hi - b_lo)) / 8;
+  o->total = align256(o->off_codes + o->code_bytes);
+  return TAHREF_OK;
+}
+
+/* 128-byte header; bytes 128..255 of the first section are zero. */
+static void write_header(uint8_t* P, const tahref_plan* pl, const tahref_params* p, int x_dtype) {
+  memset(P, 0, 256);
+  put_u32(P, 0, 0x51484154u); /* "TAHQ" */
+  put_u16(P, 4, 1);
+  put_u8(P, 6, (uint32_t)x_dtype);
+  put_u8(P, 7, (uint32_t)pl->log2G);
+  put_u64(P, 8, (uint64_t)pl->tokens);
+  put_u64(P, 16, (uint64_t)pl->hidden);
+  put_u64(P, 24, (uint64_t)pl->S);
+  put_u32(P, 32, f2u(p->bit_budget));
+  put_u32(P, 36, f2u(p->tau));
+  put_u8(P, 40, (uint32_t)p->n_candidates);
+  for (int i = 0; i < p->n_candidates; ++i) put_u8(P, 41 + i, p->candidates[i]);
+  put_u8(P, 45, (uint32_t)pl->b_lo);
+  put_u8(P, 46, (uint32_t)pl->b_hi);
+  put_u64(P, 48, (uint64_t)pl->k);
+  put_u64(P, 56, (uint64_t)pl->tiles);
+  put_u64(P, 64, (uint64_t)pl->off_table);
+  put_u64(P, 72, (uint64_t)pl->off_bitmap);
+  put_u64(P, 80, (uint64_t)pl->off_side);
+  put_u64(P, 88, (uint64_t)pl->off_scale);
+  put_u64(P, 96, (uint64_t)pl->off_zero);
+  put_u64(P, 104, (uint64_t)pl->off_codes);
+  put_u64(P, 112, (uint64_t)pl->total);
+}
+
+/* ------------------------------------------------------------------ */
+/* per-tile building blocks                                           */
+/* ------------------------------------------------------------------ */
+
+/*
+ * log2 used by the entropy of Eq. (2) (the page writes "log"; any base ranks
+ * tiles the same way, and base 2 is cheap from the float exponent).
+ * u = m * 2^e with m in [0.5, 1) (frexp); f = 2m - 1 in [0, 1) (exact);
+ * log2(u) = (e - 1) + log2(1 + f), and log2(1 + f) is replaced by the
+ * degree-5 polynomial f*(c1 + f*(c2 + f*(c3 + f*(c4 + f*c5)))), a minimax
+ * fit on [0, 1] with absolute error below 1.5e-5. The "-1" is folded into the
+ * last Horner step. Every step is one fp32 rounding (fmaf), so the result is
+ * reproducible bit for bit. Domain: normal positive u (here u >= ς).
+ */
+float tahref_log2s(float u) {
+  static const float c1 = 0x1.7124acp+0f, c2 = -0x1.6b5948p-1f, c3 = 0x1.aba0f0p-2f,
+                     c4 = -0x1.91fd90p-3f, c5 = 0x1.7c0becp-5f;
+  int e;
+  float m = frexpf(u, &e);
+  float f = fmaf(m, 2.0f, -1.0f);
+  float t = c5;
+  t = fmaf(t, f, c4);
+  t = fmaf(t, f, c3);
+  t = fmaf(t, f, c2);
+  t = fmaf(t, f, c1);
+  t = fmaf(t, f, -1.0f);
+  return (float)e + t;
+}
+
+/*
+ * Unnormalized Sylvester-ordered fast Walsh-Hadamard transform, v <- H_G v,
+ * with H_G[i][j] = (-1)^popcount(i & j) (H_1 = [1], H_2k = [[H, H], [H, -H]]).
+ * Stage order h = 1, 2, ..., G/2; each butterfly maps (a, b) to (a + b, a - b).
+ * The 1/sqrt(G) of Eq. (4) is not applied: min/max asymmetric quantization is
+ * scale invariant, so the codes are those of the normalized transform, and the
+ * inverse applies the whole 1/G at the receiver (H_G is symmetric, H_G^2 = G I).
+ */
+void tahref_fwht(float* v, int G) {
+  for (int h = 1; h < G; h <<= 1)
+    for (int j = 0; j < G; ++j)
+      if ((j & h) == 0) {
+        float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+}
+
+/*
+ * Entropy of one allocation tile, Eq. (1)-(2):
+ *   p_k = |a_k| / (||a||_1 + ε),   H = -sum_k p_k log2(p_k + ς).
+ * Reading: Eq. (2) as printed has no minus sign, but the text says H is high
+ * for evenly spread energy and low for a sharp outlier, which is Shannon's
+ * entropy; the minus sign is restored.
+ * fp32 order: L1 summed left to right; r = 1/(L1 + ε) once; p_k = |a_k| * r;
+ * the sum of p_k * log2s(p_k + ς) accumulated left to right with fmaf;
+ * H = 0 - acc (so an exact zero is +0).
+ */
+float tahref_entropy(const float* alpha, int G) {
+  float l1 = 0.0f;
+  for (int k = 0; k < G; ++k) l1 = l1 + fabsf(alpha[k]);
+  float r = 1.0f / (l1 + kEps);
+  float acc = 0.0f;
+  for (int k = 0; k < G; ++k) {
+    float p = fabsf(alpha[k]) * r;
+    acc = fmaf(p, tahref_log2s(p + kSigma), acc);
+  }
+  return 0.0f - acc;
+}
+
+/*
+ * Outlier heuristic, Eq. (3): r = |a^(1)| / (|a^(2)| + ϱ), transform iff r > tau.
+ * m1 = largest |a_k|; d = the smallest index holding it (pivot, §3.3);
+ * m2 = largest |a_k| over k != d, so tied maxima give r ~ 1 and no transform.
+ * The ratio test is evaluated without a division as m1 > tau * (m2 + ϱ).
+ * tau = +inf never flags; tau = 0 flags every tile that is not all zero.
+ */
+int tahref_outlier(const float* alpha, int G, float tau, int* d_out, float* m1_out, float* m2_out) {
+  float m1 = fabsf(alpha[0]);
+  int d = 0;
+  for (int k = 1; k < G; ++k)
+    if (fabsf(alpha[k]) > m1) {
+      m1 = fabsf(alpha[k]);
+      d = k;
+    }
+  float m2 = 0.0f;
+  for (int k = 0; k < G; ++k)
+    if (k != d && fabsf(alpha[k]) > m2) m2 = fabsf(alpha[k]);
+  float thr = tau * (m2 + kRho);
+  if (d_out) *d_out = d;
+  if (m1_out) *m1_out = m1;
+  if (m2_out) *m2_out = m2;
+  return m1 > thr;
+}
+
+/*
+ * Asymmetric uniform quantizer at width b (§3.1, §3.3): per-tile zero-point
+ * lo = min y and step s from the range, codes q_k in [0, 2^b - 1].
+ *   lo = min y, hi = max y (both + 0 so a -0 becomes +0);
+ *   s32 = (hi - lo) / (2^b - 1);  s = smallest bf16 >= s32 (the stored scale);
+ *   s = 0 when it is below 2^-126 (a range that underflows is stored as constant);
+ *   inv = s > 0 ? 1/s : 0;
+ *   q_k = round-half-even of the exact product (y_k - lo) * inv, clamped to [0, 2^b - 1].
+ * The clamp never binds for finite input (the step is rounded up), but it is
+ * written out so the definition is total.
+ */
+void tahref_quantize(const float* y, int G, int b, float* lo_out, float* s_out, uint32_t* q) {
+  float lo = y[0], hi = y[0];
+  for (int k = 1; k < G; ++k) {
+    if (y[k] < lo) lo = y[k];
+    if (y[k] > hi) hi = y[k];
+  }
+  lo = lo + 0.0f;
+  hi = hi + 0.0f;
+  const uint32_t L = (1u << b) - 1u;
+  float s32 = (hi - lo) / (float)L;
+  float s = bf16_to_f32(f32_to_bf16_up(s32));
+  if (!(s >= 0x1p-126f)) s = 0.0f;
+  float inv = s > 0.0f ? 1.0f / s : 0.0f;
+  for (int k = 0; k < G; ++k) {
+    float t = y[k] - lo;
+    double v = nearbyint((double)t * (double)inv); /* product of two fp32 is exact in double */
+    if (v < 0.0) v = 0.0;
+    if (v > (double)L) v = (double)L;
+    q[k] = (uint32_t)v;
+  }
+  *lo_out = lo;
+  *s_out = s;
+}
+
+/*
+ * Receiver side (Algorithm 1 line 5; inverse of §3.3 by H^T):
+ *   yhat_k = fmaf(q_k, s, lo);
+ *   flagged tile: z = H_G yhat, x'_k = z_k * (1/G) (exact), then undo the pivot swap;
+ *   otherwise x = yhat.
+ */
+void tahref_dequantize(const uint32_t* q, int G, float s, float lo, int flag, int d, float* xhat) {
+  for (int k = 0; k < G; ++k) xhat[k] = fmaf((float)q[k], s, lo);
+  if (flag) {
+    tahref_fwht(xhat, G);
+    const float invG = 1.0f / (float)G;
+    for (int k = 0; k < G; ++k) xhat[k] = xhat[k] * invG;
+    float t = xhat[0];
+    xhat[0] = xhat[d];
+    xhat[d] = t;
+  }
+}
+
+/*
+ * Top-p% selection of one sample (§3.2): rank the N tiles by entropy, highest
+ * first; the first k get the higher width. Reading: equal entropies rank the
+ * lower tile index first, so the selection is unique.
+ */
+typedef struct {
+  float h;
+  int64_t u;
+} hkey;
+
+static int cmp_hkey(const void* a, const void* b) {
+  const hkey* x = (const hkey*)a;
+  const hkey* y = (const hkey*)b;
+  if (x->h > y->h) return -1;
+  if (x->h < y->h) return 1;
+  return (x->u < y->u) ? -1 : (x->u > y->u);
+}
+
+int tahref_allocate(const float* H, int64_t N, int64_t k, uint8_t* hi) {
+  hkey* keys = (hkey*)malloc(sizeof(hkey) * (size_t)(N > 0 ? N : 1));
+  if (!keys) return TAHREF_ERR_INVALID_ARG;
+  for (int64_t u = 0; u < N; ++u) {
+    keys[u].h = H[u];
+    keys[u].u = u;
+    hi[u] = 0;
+  }
+  qsort(keys, (size_t)N, sizeof(hkey), cmp_hkey);
+  for (int64_t i = 0; i < k && i < N; ++i) hi[keys[i].u] = 1;
+  free(keys);
+  return TAHREF_OK;
+}
+
+/* ------------------------------------------------------------------ */
+/* whole tensor                                                       */
+/* ------------------------------------------------------------------ */
+
+/* Tile t of the [tokens, hidden] tensor: row t / M, channels (t % M) * G ... + G - 1 (§3.1). */
+static void load_tile(const void* x, int dtype, const tahref_plan* pl, int64_t t, float* a) {
+  int64_t row = t / pl->M, m = t % pl->M;
+  int64_t base = row * pl->hidden + m * pl->G;
+  if (dtype == TAHREF_F32) {
+    const float* xf = (const float*)x;
+    for (int k = 0; k < pl->G; ++k) a[k] = xf[base + k];
+  } else {
+    const uint16_t* xh = (const uint16_t*)x;
+    for (int k = 0; k < pl->G; ++k) a[k] = bf16_to_f32(xh[base + k]);
+  }
+}
+
+/* Entropy of every tile, then the per-sample selection. */
+static int entropy_and_widths(const void* x, int dtype, const tahref_plan* pl, float* H, uint8_t* hi) {
+  float a[128];
+  for (int64_t t = 0; t < pl->tiles; ++t) {
+    load_tile(x, dtype, pl, t, a);
+    H[t] = tahref_entropy(a, pl->G);
+  }
+  for (int64_t s = 0; s < pl->nsamples; ++s) {
+    int64_t first = s * pl->tiles_per_sample;
+    int rc = tahref_allocate(H + first, pl->tiles_per_sample, pl->k, hi + first);
+    if (rc) return rc;
+  }
+  return TAHREF_OK;
+}
+
+int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden, const tahref_params* p,
+                      float* H, uint8_t* flag, uint8_t* pivot, uint8_t* hi, float* lo, float* scale) {
+  if (x_dtype != TAHREF_F32 && x_dtype != TAHREF_BF16) return TAHREF_ERR_INVALID_ARG;
+  tahref_plan pl;
+  int rc = tahref_plan_make(tokens, hidden, p, &pl);
+  if (rc) return rc;
+  rc = entropy_and_widths(x, x_dtype, &pl, H, hi);
+  if (rc) return rc;
+  float a[128];
+  uint32_t q[128];
+  for (int64_t t = 0; t < pl.tiles; ++t) {
+    load_tile(x, x_dtype, &pl, t, a);
+    int d;
+    int f = tahref_outlier(a, pl.G, p->tau, &d, NULL, NULL);
+    if (f) {
+      float tmp = a[0];
+      a[0] = a[d];
+      a[d] = tmp;
+      tahref_fwht(a, pl.G);
+    }
+    int b = hi[t] ? pl.b_hi : pl.b_lo;
+    tahref_quantize(a, pl.G, b, &lo[t], &scale[t], q);
+    flag[t] = (uint8_t)f;
+    pivot[t] = (uint8_t)d;
+  }
+  return TAHREF_OK;
+}
+
+/*
+ * Encoder (Algorithm 1 line 4): entropy and widths (§3.2), then per tile the
+ * outlier test, pivot swap and Hadamard (§3.3), quantization, and packing of
+ * codes and metadata into one fixed-size byte stream (§3.4).
+ *
+ * Payload (little-endian, sections start on 256-byte boundaries):
+ *   header (128 B, zero padded to 256) | block table: u32 count of b_hi tiles
+ *   before each run of 64 tiles | width map: u32 words, bit t%32 of word t/32
+ *   is 1 iff tile t has b_hi (2 words per 64 tiles) | side byte per tile:
+ *   bit 7 = transformed, bits 0..6 = pivot d | scale per tile: bf16 bits |
+ *   zero-point per tile: fp32 | codes: one block of G*b/8 bytes per tile in
+ *   tile order, code k at stream bits [k*b, k*b + b), least significant bit
+ *   first (bit i of the block is bit i%8 of byte i/8). Padding bytes are zero.
+ */
+int tahref_encode(const void* x, int x_dtype, int64_t tokens, int64_t hidden, const tahref_params* p,
+                  uint8_t* P, size_t cap) {
+  if (x_dtype != TAHREF_F32 && x_dtype != TAHREF_BF16) return TAHREF_ERR_INVALID_ARG;
+  tahref_plan pl;
+  int rc = tahref_plan_make(tokens, hidden, p, &pl);
+  if (rc) return rc;
+  if (!P || (tokens > 0 && !x)) return TAHREF_ERR_INVALID_ARG;
+  if ((int64_t)cap < pl.total) return TAHREF_ERR_BUFFER_TOO_SMALL;
+  memset(P, 0, (size_t)pl.total);
+  write_header(P, &pl, p, x_dtype);
+
+  float* H = (float*)malloc(sizeof(float) * (size_t)(pl.tiles + 1));
+  uint8_t* hi = (uint8_t*)malloc((size_t)(pl.tiles + 1));
+  if (!H || !hi) {
+    free(H);
+    free(hi);
+    return TAHREF_ERR_INVALID_ARG;
+  }
+  rc = entropy_and_widths(x, x_dtype, &pl, H, hi);
+  if (rc) {
+    free(H);
+    free(hi);
+    return rc;
+  }
+
+  float a[128];
+  uint32_t q[128];
+  int64_t code_off = pl.off_codes;
+  int64_t hi_count = 0;
+  for (int64_t t = 0; t < pl.tiles; ++t) {
+    if (t % 64 == 0) put_u32(P, pl.off_table + 4 * (t / 64), (uint32_t)hi_count);
+    if (hi[t]) {
+      int64_t w = pl.off_bitmap + 4 * (t / 32);
+      put_u32(P, w, get_u32(P, w) | (1u << (t % 32)));
+      ++hi_count;
+    }
+    load_tile(x, x_dtype, &pl, t, a);
+    int d;
+    int f = tahref_outlier(a, pl.G, p->tau, &d, NULL, NULL);
+    if (f) {
+      float tmp = a[0];
+      a[0] = a[d];
+      a[d] = tmp;
+      tahref_fwht(a, pl.G);
+    }
+    int b = hi[t] ? pl.b_hi : pl.b_lo;
+    float lo, s;
+    tahref_quantize(a, pl.G, b, &lo, &s, q);
+    put_u8(P, pl.off_side + t, (uint32_t)((f ? 0x80 : 0) | d));
+    put_u16(P, pl.off_scale + 2 * t, f2u(s) >> 16);
+    put_u32(P, pl.off_zero + 4 * t, f2u(lo));
+    for (int k = 0; k < pl.G; ++k)
+      for (int i = 0; i < b; ++i) {
+        int64_t bit = (int64_t)k * b + i;
+        if ((q[k] >> i) & 1u) P[code_off + bit / 8] |= (uint8_t)(1u << (bit % 8));
+      }
+    code_off += (int64_t)pl.G * b / 8;
+  }
+  free(H);
+  free(hi);
+  return TAHREF_OK;
+}
+
+/*
+ * Decoder (Algorithm 1 line 5). The shape and parameters come from the caller
+ * (pipeline stages know them statically); the header must agree with them.
+ * Code blocks are located by a running sum over the width map in tile order;
+ * the block table is checked against that sum.
+ */
+int tahref_decode(const uint8_t* P, size_t len, int64_t tokens, int64_t hidden, const tahref_params* p,
+                  void* y, int y_dtype) {
+  if (y_dtype != TAHREF_F32 && y_dtype != TAHREF_BF16) return TAHREF_ERR_INVALID_ARG;
+  tahref_plan pl;
+  int rc = tahref_plan_make(tokens, hidden, p, &pl);
+  if (rc) return rc;
+  if (!P || (tokens > 0 && !y)) return TAHREF_ERR_INVALID_ARG;
+  if ((int64_t)len < pl.total) return TAHREF_ERR_BUFFER_TOO_SMALL;
+  uint8_t expect[256];
+  write_header(expect, &pl, p, P[6]);
+  if (P[6] > 1 || memcmp(expect, P, 256) != 0) return TAHREF_ERR_BAD_PAYLOAD;
+
+  float xhat[128];
+  uint32_t q[128];
+  int64_t code_off = pl.off_codes;
+  int64_t hi_count = 0;
+  for (int64_t t = 0; t < pl.tiles; ++t) {
+    if (t % 64 == 0 && get_u32(P, pl.off_table + 4 * (t / 64)) != (uint32_t)hi_count)
+      return TAHREF_ERR_BAD_PAYLOAD;
+    int hi = (get_u32(P, pl.off_bitmap + 4 * (t / 32)) >> (t % 32)) & 1u;
+    hi_count += hi;
+    int b = hi ? pl.b_hi : pl.b_lo;
+    uint32_t side = P[pl.off_side + t];
+    int f = (side >> 7) & 1, d = side & 0x7f;
+    if (d >= pl.G) return TAHREF_ERR_BAD_PAYLOAD;
+    float s = bf16_to_f32((uint16_t)get_u16(P, pl.off_scale + 2 * t));
+    float lo = u2f(get_u32(P, pl.off_zero + 4 * t));
+    for (int k = 0; k < pl.G; ++k) {
+      q[k] = 0;
+      for (int i = 0; i < b; ++i) {
+        int64_t bit = (int64_t)k * b + i;
+        q[k] |= (uint32_t)((P[code_off + bit / 8] >> (bit % 8)) & 1u) << i;
+      }
+    }
+    code_off += (int64_t)pl.G * b / 8;
+    tahref_dequantize(q, pl.G, s, lo, f, d, xhat);
+    int64_t row = t / pl.M, m = t % pl.M;
+    int64_t base = row * pl.hidden + m * pl.G;
+    if (y_dtype == TAHREF_F32) {
+      float* yf = (float*)y;
+      for (int k = 0; k < pl.G; ++k) yf[base + k] = xhat[k];
+    } else {
+      uint16_t* yh = (uint16_t*)y;
+      for (int k = 0; k < pl.G; ++k) yh[base + k] = f32_to_bf16_rne(xhat[k]);
+    }
+  }
+  if (hi_count != pl.k * pl.nsamples) return TAHREF_ERR_BAD_PAYLOAD;
+  return TAHREF_OK;
+}

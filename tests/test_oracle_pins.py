@@ -1,0 +1,431 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Each test checks an oracle routine against something other than itself: a
+closed form, a library routine (numpy, scipy), brute force on tiny inputs, or a
+tile worked out by hand (tests/golden/worked_tiles.json). Sources:
+TAH-Quant (arXiv 2506.01352v2) Sec. 3.1-3.4 and Appendix F; the Sylvester
+Hadamard construction and low-nibble-first packing from arXiv 2306.11987.
+"""
+
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.stats
+
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "worked_tiles.json")
+POLY_BOUND = 1.45e-5  # minimax error of the degree-5 polynomial for log2(1 + f) on [0, 1]
+LOG2_BOUND = 2.0e-5  # log2s over [2^-64, 2^64]: POLY_BOUND plus fp32 rounding of the result
+
+
+def sylvester(G):
+    H = np.array([[1]], dtype=np.int64)
+    while H.shape[0] < G:
+        H = np.block([[H, H], [H, -H]])
+    return H
+
+
+# ---------------------------------------------------------------- log2 ----
+def test_log2s_exact_at_powers_of_two(ref):
+    for e in range(-60, 20):
+        assert ref.log2s([2.0**e])[0] == np.float32(e)
+
+
+def test_log2s_error_bound(ref):
+    g = np.random.default_rng(1)
+    u = np.concatenate([g.uniform(2.0**-40, 1.0, 4000), np.exp2(g.uniform(-40, 1, 4000)),
+                        1.0 - np.exp2(-g.uniform(1, 24, 500))]).astype(np.float32)
+    got = ref.log2s(u)
+    err = np.abs(got.astype(np.float64) - np.log2(u.astype(np.float64)))
+    assert np.all(err <= POLY_BOUND + np.spacing(np.abs(got)) + 2.0**-24)
+    assert err.max() <= LOG2_BOUND
+    m = (u >= 0.5) & (u < 2.0)
+    assert err[m].max() <= POLY_BOUND + 2.0**-23
+
+
+# ---------------------------------------------------------------- Hadamard --
+@pytest.mark.parametrize("G", [2, 8, 16, 32, 64, 128])
+def test_sylvester_orthogonal_and_matches_scipy(G):
+    H = sylvester(G)
+    assert np.array_equal(H @ H.T, G * np.eye(G, dtype=np.int64))
+    assert np.array_equal(H, scipy.linalg.hadamard(G))
+    i, j = np.meshgrid(np.arange(G), np.arange(G), indexing="ij")
+    pop = np.vectorize(lambda v: bin(v).count("1"))(i & j)
+    assert np.array_equal(H, np.where(pop % 2 == 0, 1, -1))
+
+
+@pytest.mark.parametrize("G", [8, 16, 32, 64, 128])
+def test_fwht_equals_dense_product_on_integers(ref, G):
+    g = np.random.default_rng(G)
+    H = scipy.linalg.hadamard(G)
+    for _ in range(20):
+        x = g.integers(-1000, 1000, G)
+        y = ref.fwht(x.astype(np.float32))
+        assert np.array_equal(y.astype(np.int64), H @ x)
+        # H is symmetric and H^2 = G I: the transform twice scales by G
+        assert np.array_equal(ref.fwht(y).astype(np.int64), G * x)
+
+
+@pytest.mark.parametrize("G", [32, 64, 128])
+def test_fwht_fp32_error_vs_fp64_dense(ref, G):
+    g = np.random.default_rng(7)
+    H = scipy.linalg.hadamard(G).astype(np.float64)
+    for _ in range(50):
+        x = g.standard_normal(G).astype(np.float32) * 10
+        y = ref.fwht(x).astype(np.float64)
+        exact = H @ x.astype(np.float64)
+        bound = math.log2(G) * np.abs(x).sum() * 2.0**-24 * 1.01
+        assert np.abs(y - exact).max() <= bound
+
+
+# ---------------------------------------------------------------- entropy ----
+@pytest.mark.parametrize("G", [8, 32, 64, 128])
+def test_entropy_closed_forms(ref, G):
+    tol = LOG2_BOUND * 1.01 + 1e-6
+    assert abs(ref.entropy(np.full(G, 0.37, np.float32)) - math.log2(G)) <= tol
+    assert abs(ref.entropy(-np.full(G, 3.0, np.float32)) - math.log2(G)) <= tol
+    one_hot = np.zeros(G, np.float32)
+    one_hot[G // 3] = -7.5
+    assert ref.entropy(one_hot) == 0.0
+    for m in (2, 4, 5):
+        spikes = np.zeros(G, np.float32)
+        spikes[np.arange(m) * (G // m)] = 2.0
+        assert abs(ref.entropy(spikes) - math.log2(m)) <= tol
+    half = np.zeros(G, np.float32)
+    half[:3] = [2.0, 1.0, 1.0]
+    assert abs(ref.entropy(half) - 1.5) <= tol
+    assert ref.entropy(np.zeros(G, np.float32)) == 0.0
+
+
+def test_entropy_matches_scipy_shannon(ref):
+    g = np.random.default_rng(3)
+    for G in (32, 64, 128):
+        for _ in range(100):
+            a = (g.standard_normal(G) * np.exp(g.standard_normal())).astype(np.float32)
+            a[g.integers(0, G)] *= 50
+            p = np.abs(a.astype(np.float64))
+            want = scipy.stats.entropy(p / p.sum(), base=2)
+            assert abs(ref.entropy(a) - want) <= LOG2_BOUND * 1.01 + G * 2e-7
+            # sign and order of a tile do not matter beyond rounding
+            assert abs(ref.entropy(-a[::-1]) - want) <= LOG2_BOUND * 1.01 + G * 2e-7
+
+
+def test_entropy_high_for_spread_low_for_spike(ref):
+    # Sec. 3.2: high when energy is spread evenly, low for a sharp outlier
+    g = np.random.default_rng(5)
+    flat = g.uniform(0.9, 1.1, 64).astype(np.float32)
+    spiky = flat.copy()
+    spiky[10] = 500
+    assert ref.entropy(flat) > 5.9
+    p = np.abs(spiky.astype(np.float64))
+    assert abs(ref.entropy(spiky) - scipy.stats.entropy(p / p.sum(), base=2)) <= LOG2_BOUND
+    assert ref.entropy(spiky) < ref.entropy(flat) / 4
+
+
+# ---------------------------------------------------------------- outlier ----
+def test_outlier_against_numpy_sort(ref):
+    g = np.random.default_rng(11)
+    for _ in range(400):
+        G = int(g.choice([8, 32, 64]))
+        a = g.standard_normal(G).astype(np.float32)
+        if g.random() < 0.5:
+            a[g.integers(0, G)] *= 10
+        if g.random() < 0.2:  # tied maxima
+            a[g.integers(0, G)] = a[np.argmax(np.abs(a))]
+        mag = np.abs(a)
+        d_np = int(np.argmax(mag))  # first occurrence of the max
+        m2_np = np.sort(np.delete(mag, d_np))[-1]
+        for tau in (0.0, 2.0, 4.0, math.inf):
+            f, d, m1, m2 = ref.outlier(a, tau)
+            assert d == d_np and m1 == mag.max() and m2 == m2_np
+            want = bool(mag.max() > np.float32(np.float32(tau) * np.float32(m2_np + np.float32(2.0**-40))))
+            assert f == want
+
+
+def test_outlier_tau_semantics(ref):
+    a = np.array([0.1, 0.1, 0.1, 3.0, 0.1, 0.1, 0.1, 0.1], np.float32)
+    assert ref.outlier(a, 0.0)[0] and ref.outlier(a, 2.0)[0]
+    assert not ref.outlier(a, math.inf)[0]
+    z = np.zeros(8, np.float32)
+    assert not ref.outlier(z, 0.0)[0]  # tau = 0 flags every tile that is not all zero
+    flat = np.ones(8, np.float32)
+    assert ref.outlier(flat, 0.0)[0] and not ref.outlier(flat, 2.0)[0]
+    # ratio exactly tau is not "exceeding" tau
+    edge = np.array([4.0, 2.0, 0, 0, 0, 0, 0, 0], np.float32)
+    assert not ref.outlier(edge, 2.0)[0]
+    edge[0] = np.nextafter(np.float32(4.0), np.float32(5.0))
+    assert ref.outlier(edge, 2.0)[0]
+
+
+# ---------------------------------------------------------------- quantizer ----
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_quantizer_bounds(ref, b):
+    g = np.random.default_rng(b)
+    L = 2**b - 1
+    for _ in range(200):
+        y = (g.standard_normal(64) * np.exp(g.standard_normal()) + g.standard_normal() * 5).astype(np.float32)
+        lo, s, q = ref.quantize(y, b)
+        assert lo == y.min()
+        assert q.max() <= L and q.min() == 0
+        assert np.float32(s).view(np.uint32) & 0xFFFF == 0  # a bf16 value
+        assert s >= (np.float64(y.max()) - np.float64(y.min())) / L * (1 - 2**-23)
+        yhat = ref.dequantize(q, s, lo, False, 0)
+        err = np.abs(yhat.astype(np.float64) - y.astype(np.float64))
+        assert err.max() <= s / 2 * (1 + 2**-20) + 4 * np.spacing(np.abs(y).max())
+
+
+def test_quantizer_error_shrinks_with_bits(ref):
+    g = np.random.default_rng(9)
+    y = (g.standard_normal((300, 64))).astype(np.float32)
+    prev = None
+    for b in (1, 2, 3, 4, 5, 6, 7, 8):
+        worst = 0.0
+        for row in y:
+            lo, s, q = ref.quantize(row, b)
+            worst = max(worst, float(np.abs(ref.dequantize(q, s, lo, False, 0) - row).max()))
+        if prev is not None:
+            assert worst < prev * 0.75
+        prev = worst
+
+
+def test_constant_tile_is_exact(ref):
+    y = np.full(64, -3.25, np.float32)
+    lo, s, q = ref.quantize(y, 3)
+    assert s == 0 and lo == -3.25 and not q.any()
+    assert np.array_equal(ref.dequantize(q, s, lo, False, 0), y)
+
+
+def test_one_hot_tile_transforms_to_constant_and_decodes_exactly(ref):
+    # swap moves the pivot to index 0; column 0 of H is all ones (Sylvester order),
+    # so c e_0 maps to the constant vector c 1: zero range, exact reconstruction
+    for G in (8, 32, 64, 128):
+        for d in (0, 1, G // 2 + 1, G - 1):
+            a = np.zeros(G, np.float32)
+            a[d] = -13.0
+            f, dd, _, _ = ref.outlier(a, 2.0)
+            assert f and dd == d
+            x = a.copy()
+            x[0], x[d] = x[d], x[0]
+            y = ref.fwht(x)
+            assert np.all(y == -13.0)
+            lo, s, q = ref.quantize(y, 3)
+            assert s == 0
+            assert np.array_equal(ref.dequantize(q, s, lo, True, d), a)
+
+
+def test_swap_is_an_involution_and_transform_inverts(ref):
+    g = np.random.default_rng(13)
+    for G in (32, 64, 128):
+        for _ in range(50):
+            a = g.standard_normal(G).astype(np.float32)
+            d = int(g.integers(0, G))
+            x = a.copy()
+            x[0], x[d] = x[d], x[0]
+            x[0], x[d] = x[d], x[0]
+            assert np.array_equal(x, a)
+            # 8-bit codec through the transform: ||x - xhat||_2 <= s/2 (orthogonality)
+            x = a.copy()
+            x[0], x[d] = x[d], x[0]
+            y = ref.fwht(x)
+            lo, s, q = ref.quantize(y, 8)
+            xh = ref.dequantize(q, s, lo, True, d)
+            assert np.linalg.norm(xh.astype(np.float64) - a) <= s / 2 * 1.001 + G * 1e-6 * np.abs(y).max()
+
+
+# ---------------------------------------------------------------- worked tiles ----
+def test_worked_tiles_by_hand(ref):
+    data = json.load(open(GOLDEN))
+    for t in data["tiles"]:
+        x = np.array(t["x"], np.float32)
+        f, d, m1, m2 = ref.outlier(x, t["tau"])
+        assert (f, d, float(m1), float(m2)) == (t["flag"], t["pivot"], t["m1"], t["m2"])
+        y = x.copy()
+        if f:
+            y[0], y[d] = y[d], y[0]
+            y = ref.fwht(y)
+            assert y.tolist() == t["y_transformed"]
+        lo, s, q = ref.quantize(y, t["bits"])
+        assert float(lo) == t["lo"] and float(s) == t["scale"]
+        assert int(np.float32(s).view(np.uint32) >> 16) == t["scale_bf16_bits"]
+        assert q.tolist() == t["codes"]
+        assert ref.dequantize(q, s, lo, f, d).tolist() == t["decoded"]
+        assert abs(ref.entropy(x) - t["entropy_exact"]) <= LOG2_BOUND * 1.01
+
+
+def test_worked_tile_payload_bytes(ref):
+    # the flagged worked tile as a 1 x 8 tensor with tile 8 at 3 bits
+    t = json.load(open(GOLDEN))["tiles"][0]
+    x = np.array([t["x"]], np.float32)
+    p = synth.Params(tile=8, tokens_per_sample=0, bit_budget=3.0, candidates=(3,), tau=2.0)
+    P = ref.encode(x, p)
+    pl = ref.plan(1, 8, p)
+    assert P[pl["off_side"]] == 0x80 | 1
+    assert int(P[pl["off_scale"]]) | (int(P[pl["off_scale"] + 1]) << 8) == t["scale_bf16_bits"]
+    assert P[pl["off_zero"]:pl["off_zero"] + 4].view(np.float32)[0] == 3.0
+    # codes 7,0,0,7,0,7,7,0 at 3 bits each, least significant bit first:
+    # bits 0-2 = 111, 9-11 = 111, 15-17 = 111, 18-20 = 111 -> 0x1F8E07 little-endian
+    assert P[pl["off_codes"]:pl["off_codes"] + 3].tolist() == [0x07, 0x8E, 0x1F]
+    y = ref.decode(P, 1, 8, p)
+    assert y[0].tolist() == t["decoded"]
+
+
+def test_nibble_order_low_first(ref):
+    # 4-bit codes: the first element sits in the low nibble (INT4 packing order of arXiv 2306.11987)
+    x = np.array([[0, 15, 0, 15, 0, 15, 0, 15, 1, 2, 3, 4, 5, 6, 7, 8]], np.float32)
+    p = synth.Params(tile=8, tokens_per_sample=0, bit_budget=4.0, candidates=(4,), tau=math.inf)
+    P = ref.encode(x, p)
+    pl = ref.plan(1, 16, p)
+    # tile 0: lo = 0, s = 1 -> codes = values -> bytes 0xF0 x4
+    assert P[pl["off_codes"]:pl["off_codes"] + 4].tolist() == [0xF0] * 4
+    # tile 1: lo = 1, range 7 -> s = 7/15 rounded up; codes of 1 and 8 are 0 and 15
+    c = P[pl["off_codes"] + 4:pl["off_codes"] + 8]
+    assert c[0] & 0xF == 0 and c[3] >> 4 == 15
+
+
+# ---------------------------------------------------------------- allocation ----
+def test_allocation_brute_force(ref):
+    g = np.random.default_rng(17)
+    for trial in range(300):
+        N = int(g.integers(1, 11))
+        H = g.choice([0.5, 1.0, 1.5, 2.0, 2.5], N).astype(np.float32) if trial % 2 else g.random(N).astype(np.float32)
+        for k in range(N + 1):
+            hi = ref.allocate(H, k)
+            best = None
+            for sub in itertools.combinations(range(N), k):  # lexicographic order
+                v = float(sum(np.float64(H[i]) for i in sub))
+                if best is None or v > best[0] + 1e-12:
+                    best = (v, sub)
+            want = np.zeros(N, np.uint8)
+            want[list(best[1])] = 1
+            assert np.array_equal(hi, want), (H, k)
+
+
+@pytest.mark.parametrize("N,budget,cands,blo,bhi,k", [
+    (32768, 3.5, (2, 3, 4, 8), 3, 4, 16384),
+    (1048576, 3.8, (3, 4, 8), 3, 4, 838860),  # the pages' default 80% INT4 + 20% INT3
+    (32768, 5.0, (3, 4, 8), 4, 8, 8192),
+    (32768, 2.5, (2, 3, 4, 8), 2, 3, 16384),
+    (4096, 4.0, (3, 4, 8), 4, 8, 0),
+    (1048576, 3.0, (3, 4, 8), 3, 4, 0),
+    (100, 9.0, (2, 4), 4, 4, 0),
+])
+def test_width_pair_and_k(ref, N, budget, cands, blo, bhi, k):
+    p = synth.Params(tile=64, tokens_per_sample=0, bit_budget=budget, candidates=cands, tau=2.0)
+    pl = ref.plan(N // 32 if N % 32 == 0 else N, 2048 if N % 32 == 0 else 64, p)
+    assert pl["tiles_per_sample"] == N
+    assert (pl["b_lo"], pl["b_hi"], pl["k"]) == (blo, bhi, k)
+    # budget conservation: the average code width never exceeds the budget, and
+    # one more upgraded tile would exceed it
+    total = (N - k) * blo + k * bhi
+    assert total <= budget * N + 1e-9
+    if bhi > blo:
+        assert total + (bhi - blo) > budget * N
+
+
+def test_budget_errors(ref):
+    with pytest.raises(ref.OracleError) as e:
+        ref.plan(4, 64, synth.Params(tile=64, bit_budget=2.5, candidates=(3, 4)))
+    assert e.value.code == 4
+    for bad in (dict(tile=48), dict(tile=4), dict(candidates=(4, 3)), dict(candidates=(0, 3)), dict(candidates=(3, 9)),
+                dict(candidates=()), dict(tau=float("nan")), dict(bit_budget=float("nan")), dict(tokens_per_sample=3)):
+        with pytest.raises(ref.OracleError) as e:
+            ref.plan(4, 128, synth.Params(**{**dict(tile=64, bit_budget=3.5, candidates=(3, 4)), **bad}))
+        assert e.value.code == 1
+
+
+# ---------------------------------------------------------------- payload ----
+def test_plan_layout_numbers(ref):
+    # hand-computed: 4096 tiles of 32 at 4 bits; sections on 256-byte boundaries
+    w = synth.workload("c1_256x512_f32_g32")
+    pl = ref.plan(w.tokens, w.hidden, w.params)
+    assert (pl["off_table"], pl["off_bitmap"], pl["off_side"], pl["off_scale"], pl["off_zero"], pl["off_codes"], pl["total"]) == (
+        256, 512, 1024, 5120, 13312, 29696, 95232)
+    # 8192 x 8192 at G = 64, all 3-bit: 1,048,576 tiles x 24 bytes of codes
+    w = synth.workload("c5_8192x8192_bf16_g64")
+    pl = ref.plan(w.tokens, w.hidden, w.params)
+    assert pl["code_bytes"] == 25165824 and pl["k"] == 0
+    # paper default 80/20 split at the same shape: 838,860 tiles get 4 bits
+    w = synth.workload("x2_c5_budget3p8")
+    pl = ref.plan(w.tokens, w.hidden, w.params)
+    assert pl["code_bytes"] == 1048576 * 24 + 838860 * 8
+
+
+def test_payload_fixed_shape(ref):
+    p = synth.Params(tile=32, tokens_per_sample=16, bit_budget=3.5, candidates=(3, 4, 8), tau=2.0)
+    a = synth.random_tensor(64, 256, synth.F32, 1)
+    b = synth.random_tensor(64, 256, synth.F32, 2, scale=100, n_out=3, mult=40)
+    Pa, Pb = ref.encode(a, p), ref.encode(b, p)
+    assert Pa.size == Pb.size
+    assert np.array_equal(Pa[:256], Pb[:256])
+    pl = ref.plan(64, 256, p)
+    # every sample upgrades exactly k tiles
+    bm = np.unpackbits(Pa[pl["off_bitmap"]:pl["off_bitmap"] + 4 * ((pl["tiles"] + 31) // 32)], bitorder="little")
+    per = bm[:pl["tiles"]].reshape(pl["nsamples"], -1).sum(1)
+    assert np.all(per == pl["k"]) and pl["k"] == 64
+
+
+def test_scale_invariance(ref):
+    p = synth.Params(tile=64, tokens_per_sample=8, bit_budget=3.5, candidates=(3, 4), tau=2.0)
+    x = synth.random_tensor(32, 512, synth.F32, 4, n_out=6, mult=30)
+    P1 = ref.encode(x, p)
+    P2 = ref.encode((x * np.float32(8.0)).astype(np.float32), p)
+    pl = ref.plan(32, 512, p)
+    n = pl["tiles"]
+    assert np.array_equal(P1[pl["off_bitmap"]:pl["off_side"]], P2[pl["off_bitmap"]:pl["off_side"]])
+    assert np.array_equal(P1[pl["off_side"]:pl["off_side"] + n], P2[pl["off_side"]:pl["off_side"] + n])
+    assert np.array_equal(P1[pl["off_codes"]:], P2[pl["off_codes"]:])
+    s1 = (P1[pl["off_scale"]:pl["off_scale"] + 2 * n].view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    s2 = (P2[pl["off_scale"]:pl["off_scale"] + 2 * n].view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    assert np.array_equal(s1 * 8, s2)
+    z1 = P1[pl["off_zero"]:pl["off_zero"] + 4 * n].view(np.float32)
+    z2 = P2[pl["off_zero"]:pl["off_zero"] + 4 * n].view(np.float32)
+    assert np.array_equal(z1 * 8, z2)
+
+
+def test_codec_roundtrip_error_bound(ref):
+    # whole tensor: per element |x - xhat| <= s/2 on plain tiles; ||.||_2 <= s/2 on transformed tiles
+    p = synth.Params(tile=32, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0)
+    x = synth.random_tensor(48, 256, synth.F32, 6, n_out=5, mult=60)
+    P = ref.encode(x, p)
+    y = ref.decode(P, 48, 256, p)
+    st = ref.tile_stats(x, p)
+    xt = x.reshape(-1, 32).astype(np.float64)
+    yt = y.reshape(-1, 32).astype(np.float64)
+    for i in range(xt.shape[0]):
+        s = float(st["scale"][i])
+        slack = 1e-6 * (1 + np.abs(xt[i]).max()) * 32
+        if st["flag"][i]:
+            assert np.linalg.norm(xt[i] - yt[i]) <= s / 2 * 1.001 + slack
+        else:
+            assert np.abs(xt[i] - yt[i]).max() <= s / 2 * 1.001 + slack
+    assert st["flag"].any() and not st["flag"].all()
+
+
+def test_decode_rejects_bad_header(ref):
+    p = synth.Params(tile=32, tokens_per_sample=0, bit_budget=3.0, candidates=(3,), tau=2.0)
+    x = synth.random_tensor(4, 64, synth.F32, 8)
+    P = ref.encode(x, p)
+    for off in (0, 8, 16, 45, 112):
+        Q = P.copy()
+        Q[off] ^= 1
+        with pytest.raises(ref.OracleError) as e:
+            ref.decode(Q, 4, 64, p)
+        assert e.value.code == 5
+    with pytest.raises(ref.OracleError):
+        ref.decode(P, 4, 64, synth.Params(tile=32, bit_budget=3.0, candidates=(3,), tau=4.0))
+
+
+def test_bf16_input_widens_exactly(ref):
+    p = synth.Params(tile=32, tokens_per_sample=0, bit_budget=3.0, candidates=(3,), tau=2.0)
+    xb = synth.random_tensor(8, 128, synth.BF16, 9, n_out=2, mult=20)
+    xf = synth.bf16_bits_to_f32(xb).reshape(8, 128)
+    Pb, Pf = ref.encode(xb, p), ref.encode(xf, p)
+    assert Pb[6] == 1 and Pf[6] == 0
+    Pb[6] = 0
+    assert np.array_equal(Pb, Pf)
