@@ -1,0 +1,273 @@
+"""MI355X TAH-Quant activation codec: Python binding of ``lib/libtah.so``.
+
+Argument marshalling only: every step of the codec runs in the HIP kernels
+behind the C ABI declared in ``include/tah.h``. PyTorch supplies device memory
+and the current HIP stream. There is no CPU fallback: importing this package
+fails loudly if the HIP library has not been built.
+
+Functions mirror the C ABI names (``tah_encode`` -> ``encode`` ...). Tensors are
+``[tokens, hidden]`` bf16 or fp32 on a ROCm device; payloads are uint8 device
+tensors of ``payload_bytes(...)`` bytes.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+from ._build import LIB_PATH, build  # noqa: F401  (build is re-exported for __graft_entry__)
+
+TAH_DTYPE_F32 = 0
+TAH_DTYPE_BF16 = 1
+
+STATUS_NAMES = {
+    0: "TAH_OK",
+    1: "TAH_ERR_INVALID_ARG",
+    2: "TAH_ERR_UNSUPPORTED",
+    3: "TAH_ERR_BUFFER_TOO_SMALL",
+    4: "TAH_ERR_BUDGET_INFEASIBLE",
+    5: "TAH_ERR_BAD_PAYLOAD",
+    6: "TAH_ERR_HIP",
+}
+
+# Every symbol include/tah.h declares.
+EXPORTS = (
+    "tah_params_default",
+    "tah_payload_bytes",
+    "tah_workspace_bytes",
+    "tah_encode",
+    "tah_decode",
+    "tah_roundtrip",
+    "tah_tile_entropy",
+    "tah_workspace_entropy",
+    "tah_read_device_status",
+    "tah_status_string",
+    "tah_abi_version",
+)
+
+
+class TahError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {STATUS_NAMES.get(code, code)}")
+        self.code = code
+
+
+@dataclasses.dataclass(frozen=True)
+class TahParams:
+    """Codec parameters (see tah_params_t): tile G, ranking scope S in tokens
+    (0 = all tokens), average code-bit budget, candidate widths, outlier tau."""
+
+    tile: int = 64
+    tokens_per_sample: int = 0
+    bit_budget: float = 3.8
+    candidates: tuple = (3, 4)
+    tau: float = 2.0
+
+
+class _CParams(ctypes.Structure):
+    _fields_ = [
+        ("tile", ctypes.c_int32),
+        ("tokens_per_sample", ctypes.c_int32),
+        ("bit_budget", ctypes.c_float),
+        ("n_candidates", ctypes.c_int32),
+        ("candidates", ctypes.c_uint8 * 4),
+        ("tau", ctypes.c_float),
+    ]
+
+
+def _cparams(p) -> _CParams:
+    c = _CParams()
+    c.tile = int(p.tile)
+    c.tokens_per_sample = int(p.tokens_per_sample)
+    c.bit_budget = float(p.bit_budget)
+    cands = tuple(int(v) for v in p.candidates)
+    if len(cands) > 4:
+        raise TahError(1, "at most 4 candidate widths")
+    c.n_candidates = len(cands)
+    for i in range(4):
+        c.candidates[i] = cands[i] if i < len(cands) else 0
+    c.tau = float(p.tau)
+    return c
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the HIP library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"TAH-Quant HIP library not built: {LIB_PATH} (run __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.POINTER
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        L.tah_params_default.argtypes = [P(_CParams)]
+        L.tah_params_default.restype = None
+        for f in ("tah_payload_bytes", "tah_workspace_bytes", "tah_workspace_entropy"):
+            getattr(L, f).argtypes = [i64, i64, P(_CParams), P(sz)]
+            getattr(L, f).restype = ctypes.c_int
+        L.tah_encode.argtypes = [vp, ctypes.c_int, i64, i64, P(_CParams), vp, sz, vp, sz, vp]
+        L.tah_encode.restype = ctypes.c_int
+        L.tah_decode.argtypes = [vp, sz, i64, i64, P(_CParams), vp, ctypes.c_int, vp, sz, vp]
+        L.tah_decode.restype = ctypes.c_int
+        L.tah_roundtrip.argtypes = [vp, ctypes.c_int, i64, i64, P(_CParams), vp, sz, vp, ctypes.c_int, vp, sz, vp]
+        L.tah_roundtrip.restype = ctypes.c_int
+        L.tah_tile_entropy.argtypes = [vp, ctypes.c_int, i64, i64, P(_CParams), vp, vp, sz, vp]
+        L.tah_tile_entropy.restype = ctypes.c_int
+        L.tah_read_device_status.argtypes = [vp, vp, P(ctypes.c_int32)]
+        L.tah_read_device_status.restype = ctypes.c_int
+        L.tah_status_string.argtypes = [ctypes.c_int]
+        L.tah_status_string.restype = ctypes.c_char_p
+        L.tah_abi_version.argtypes = []
+        L.tah_abi_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def _check(rc: int, what: str) -> None:
+    if rc != 0:
+        raise TahError(rc, what)
+
+
+def _dtype_code(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return TAH_DTYPE_F32
+    if t == torch.bfloat16:
+        return TAH_DTYPE_BF16
+    raise TahError(1, f"unsupported dtype {t}")
+
+
+def _torch_dtype(code: int) -> torch.dtype:
+    return torch.float32 if code == TAH_DTYPE_F32 else torch.bfloat16
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _size_query(fn: str, tokens: int, hidden: int, p) -> int:
+    out = ctypes.c_size_t()
+    cp = _cparams(p)
+    _check(getattr(lib(), fn)(int(tokens), int(hidden), ctypes.byref(cp), ctypes.byref(out)), fn)
+    return int(out.value)
+
+
+def payload_bytes(tokens: int, hidden: int, p) -> int:
+    return _size_query("tah_payload_bytes", tokens, hidden, p)
+
+
+def workspace_bytes(tokens: int, hidden: int, p) -> int:
+    return _size_query("tah_workspace_bytes", tokens, hidden, p)
+
+
+def workspace_entropy_offset(tokens: int, hidden: int, p) -> int:
+    return _size_query("tah_workspace_entropy", tokens, hidden, p)
+
+
+def params_default() -> TahParams:
+    c = _CParams()
+    lib().tah_params_default(ctypes.byref(c))
+    return TahParams(c.tile, c.tokens_per_sample, c.bit_budget, tuple(c.candidates[: c.n_candidates]), c.tau)
+
+
+def abi_version() -> int:
+    return int(lib().tah_abi_version())
+
+
+def status_string(code: int) -> str:
+    return lib().tah_status_string(int(code)).decode()
+
+
+def _shape(x: torch.Tensor):
+    if x.dim() != 2:
+        raise TahError(1, "expected a [tokens, hidden] tensor")
+    if not x.is_contiguous():
+        raise TahError(1, "tensor must be contiguous")
+    return int(x.shape[0]), int(x.shape[1])
+
+
+def alloc_workspace(tokens: int, hidden: int, p, device=None) -> torch.Tensor:
+    return torch.empty(max(workspace_bytes(tokens, hidden, p), 256), dtype=torch.uint8, device=device or "cuda")
+
+
+def alloc_payload(tokens: int, hidden: int, p, device=None) -> torch.Tensor:
+    return torch.empty(payload_bytes(tokens, hidden, p), dtype=torch.uint8, device=device or "cuda")
+
+
+def encode(x: torch.Tensor, p, payload: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """tah_encode: x [tokens, hidden] -> payload (uint8 device tensor)."""
+    tokens, hidden = _shape(x)
+    if payload is None:
+        payload = alloc_payload(tokens, hidden, p, x.device)
+    if ws is None:
+        ws = alloc_workspace(tokens, hidden, p, x.device)
+    cp = _cparams(p)
+    rc = lib().tah_encode(_ptr(x), _dtype_code(x.dtype), tokens, hidden, ctypes.byref(cp), _ptr(payload),
+                          payload.numel(), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "tah_encode")
+    return payload
+
+
+def decode(payload: torch.Tensor, tokens: int, hidden: int, p, y_dtype: torch.dtype = torch.float32,
+           y: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """tah_decode: payload -> y [tokens, hidden] (y_dtype)."""
+    if y is None:
+        y = torch.empty((tokens, hidden), dtype=y_dtype, device=payload.device)
+    if ws is None:
+        ws = alloc_workspace(tokens, hidden, p, payload.device)
+    cp = _cparams(p)
+    rc = lib().tah_decode(_ptr(payload), payload.numel(), int(tokens), int(hidden), ctypes.byref(cp), _ptr(y),
+                          _dtype_code(y.dtype), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "tah_decode")
+    return y
+
+
+def roundtrip(x: torch.Tensor, p, y_dtype: torch.dtype | None = None, payload: torch.Tensor | None = None,
+              y: torch.Tensor | None = None, ws: torch.Tensor | None = None, write_payload: bool = True,
+              stream=None):
+    """tah_roundtrip: encode and decode in one pass. Returns (y, payload or None)."""
+    tokens, hidden = _shape(x)
+    if y is None:
+        y = torch.empty((tokens, hidden), dtype=y_dtype or x.dtype, device=x.device)
+    if payload is None and write_payload:
+        payload = alloc_payload(tokens, hidden, p, x.device)
+    if ws is None:
+        ws = alloc_workspace(tokens, hidden, p, x.device)
+    cp = _cparams(p)
+    rc = lib().tah_roundtrip(_ptr(x), _dtype_code(x.dtype), tokens, hidden, ctypes.byref(cp), _ptr(payload),
+                             payload.numel() if payload is not None else 0, _ptr(y), _dtype_code(y.dtype), _ptr(ws),
+                             ws.numel(), _stream(stream))
+    _check(rc, "tah_roundtrip")
+    return y, payload
+
+
+def tile_entropy(x: torch.Tensor, p, h: torch.Tensor | None = None, ws: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """tah_tile_entropy: fp32 entropy of each of the tokens*hidden/G tiles."""
+    tokens, hidden = _shape(x)
+    if h is None:
+        h = torch.empty(tokens * (hidden // int(p.tile)), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = alloc_workspace(tokens, hidden, p, x.device)
+    cp = _cparams(p)
+    rc = lib().tah_tile_entropy(_ptr(x), _dtype_code(x.dtype), tokens, hidden, ctypes.byref(cp), _ptr(h), _ptr(ws),
+                                ws.numel(), _stream(stream))
+    _check(rc, "tah_tile_entropy")
+    return h
+
+
+def read_device_status(ws: torch.Tensor, stream=None) -> int:
+    out = ctypes.c_int32()
+    _check(lib().tah_read_device_status(_ptr(ws), _stream(stream), ctypes.byref(out)), "tah_read_device_status")
+    return int(out.value)

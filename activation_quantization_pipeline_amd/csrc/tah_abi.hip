@@ -1,0 +1,318 @@
+// Host side of the C ABI (include/tah.h): argument validation, the per-call
+// plan (width pair and k of §3.2, payload layout of §3.4, workspace layout) and
+// the launch sequence. Validation happens before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "tah_internal.hpp"
+
+namespace tah {
+
+static int64_t align256(int64_t v) { return (v + 255) & ~(int64_t)255; }
+
+static int ilog2(int v) {
+  int l = 0;
+  while ((1 << l) < v) ++l;
+  return l;
+}
+
+static int bit_width(uint64_t v) {
+  int b = 0;
+  while (v) {
+    ++b;
+    v >>= 1;
+  }
+  return b;
+}
+
+// Shape and parameter checks, width pair, k and all offsets.
+static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t* p, Plan* o) {
+  if (!p || !o) return TAH_ERR_INVALID_ARG;
+  memset(o, 0, sizeof(*o));
+  if (tokens < 0 || hidden <= 0) return TAH_ERR_INVALID_ARG;
+  const int G = p->tile;
+  if (G < 8 || G > 128 || (G & (G - 1)) || hidden % G) return TAH_ERR_INVALID_ARG;
+  if (p->n_candidates < 1 || p->n_candidates > 4) return TAH_ERR_INVALID_ARG;
+  for (int i = 0; i < p->n_candidates; ++i) {
+    if (p->candidates[i] < 1 || p->candidates[i] > 8) return TAH_ERR_INVALID_ARG;
+    if (i > 0 && p->candidates[i] <= p->candidates[i - 1]) return TAH_ERR_INVALID_ARG;
+  }
+  if (!isfinite(p->bit_budget) || isnan(p->tau) || p->tau < 0.0f || p->tokens_per_sample < 0)
+    return TAH_ERR_INVALID_ARG;
+  const int64_t S = p->tokens_per_sample == 0 ? tokens : p->tokens_per_sample;
+  if (S > 0 && tokens % S) return TAH_ERR_INVALID_ARG;
+  if ((float)p->candidates[0] > p->bit_budget) return TAH_ERR_BUDGET_INFEASIBLE;
+  // tile indices of a sample and block-table counts are 32-bit on the device
+  const int64_t M = hidden / G;
+  if (tokens > 0 && (M > ((int64_t)1 << 40) / tokens || S * M >= ((int64_t)1 << 31) ||
+                     tokens * M >= ((int64_t)1 << 40)))
+    return TAH_ERR_UNSUPPORTED;
+
+  int b_lo = p->candidates[0], b_hi = -1;
+  for (int i = 0; i < p->n_candidates; ++i) {
+    if ((float)p->candidates[i] <= p->bit_budget) b_lo = p->candidates[i];
+    else if (b_hi < 0) b_hi = p->candidates[i];
+  }
+  if (b_hi < 0) b_hi = b_lo;
+
+  o->tokens = tokens;
+  o->hidden = hidden;
+  o->S = S;
+  o->nsamples = S > 0 ? tokens / S : 0;
+  o->M = M;
+  o->tiles = tokens * M;
+  o->N = S * M;
+  o->G = G;
+  o->log2G = ilog2(G);
+  o->b_lo = b_lo;
+  o->b_hi = b_hi;
+  o->k = (b_hi == b_lo || o->N == 0)
+             ? 0
+             : (int64_t)floor(((double)p->bit_budget - (double)b_lo) * (double)o->N / (double)(b_hi - b_lo));
+  o->tau = p->tau;
+  o->budget = p->bit_budget;
+  o->n_candidates = p->n_candidates;
+  for (int i = 0; i < 4; ++i) o->candidates[i] = i < p->n_candidates ? p->candidates[i] : 0;
+  o->nblocks = (o->tiles + 63) / 64;
+
+  const int64_t nhi = o->k * o->nsamples;
+  o->off_table = 256;
+  o->off_bitmap = align256(o->off_table + 4 * o->nblocks);
+  o->off_side = align256(o->off_bitmap + 8 * o->nblocks);
+  o->off_scale = align256(o->off_side + o->tiles);
+  o->off_zero = align256(o->off_scale + 2 * o->tiles);
+  o->off_codes = align256(o->off_zero + 4 * o->tiles);
+  o->code_bytes = (o->tiles * G * b_lo + nhi * G * (b_hi - b_lo)) / 8;
+  o->total = align256(o->off_codes + o->code_bytes);
+
+  const bool mixed = o->k > 0;
+  int64_t w = 0;
+  o->ws_status = w;
+  w += 256;
+  o->ws_counter = w;
+  w += 256;
+  o->ws_state = w;
+  w = align256(w + (int64_t)sizeof(SampleState) * (mixed ? o->nsamples : 0));
+  o->ws_hist = w;
+  w = align256(w + 4 * kBins * (mixed ? o->nsamples : 0));
+  o->ws_H = w;
+  w = align256(w + 4 * o->tiles);
+  o->ws_blockcnt = w;
+  w = align256(w + 4 * (mixed ? o->nblocks : 0));
+  o->ws_table = w;
+  w = align256(w + 4 * (mixed ? o->nblocks : 0));
+  o->ws_bitmap = w;
+  w = align256(w + 8 * (mixed ? o->nblocks : 0));
+  o->ws_total = w;
+
+  // radix-select passes: three digits of the 32-bit entropy key, then enough
+  // digits of the tile index to order tied entropies
+  o->npasses = 0;
+  if (mixed) {
+    o->passes[o->npasses++] = SelectPass{0, 21, 11, 0};
+    o->passes[o->npasses++] = SelectPass{0, 10, 11, 0};
+    o->passes[o->npasses++] = SelectPass{0, 0, 10, 1};
+    const int nb = bit_width((uint64_t)(o->N - 1));
+    for (int top = ((nb + kDigitBits - 1) / kDigitBits) * kDigitBits; top > 0; top -= kDigitBits)
+      o->passes[o->npasses++] = SelectPass{1, top - kDigitBits, kDigitBits, 0};
+  }
+  return TAH_OK;
+}
+
+void make_header(const Plan& pl, Header* h) {
+  uint8_t b[128];
+  memset(b, 0, sizeof(b));
+  auto put = [&](int off, const void* src, int n) { memcpy(b + off, src, n); };
+  const uint32_t magic = 0x51484154u;  // "TAHQ"
+  const uint16_t ver = 1;
+  const uint8_t dt = (uint8_t)pl.x_dtype, lg = (uint8_t)pl.log2G;
+  put(0, &magic, 4);
+  put(4, &ver, 2);
+  put(6, &dt, 1);
+  put(7, &lg, 1);
+  put(8, &pl.tokens, 8);
+  put(16, &pl.hidden, 8);
+  put(24, &pl.S, 8);
+  put(32, &pl.budget, 4);
+  put(36, &pl.tau, 4);
+  const uint8_t nc = (uint8_t)pl.n_candidates, bl = (uint8_t)pl.b_lo, bh = (uint8_t)pl.b_hi;
+  put(40, &nc, 1);
+  put(41, pl.candidates, 4);
+  put(45, &bl, 1);
+  put(46, &bh, 1);
+  put(48, &pl.k, 8);
+  put(56, &pl.tiles, 8);
+  put(64, &pl.off_table, 8);
+  put(72, &pl.off_bitmap, 8);
+  put(80, &pl.off_side, 8);
+  put(88, &pl.off_scale, 8);
+  put(96, &pl.off_zero, 8);
+  put(104, &pl.off_codes, 8);
+  put(112, &pl.total, 8);
+  memcpy(h->w, b, 128);
+}
+
+// Byte ranges of the payload that no section covers; the encoder zeroes them.
+void make_pads(const Plan& pl, PadRanges* pr) {
+  const int64_t ends[7][2] = {
+      {128, pl.off_table},
+      {pl.off_table + 4 * pl.nblocks, pl.off_bitmap},
+      {pl.off_bitmap + 8 * pl.nblocks, pl.off_side},
+      {pl.off_side + pl.tiles, pl.off_scale},
+      {pl.off_scale + 2 * pl.tiles, pl.off_zero},
+      {pl.off_zero + 4 * pl.tiles, pl.off_codes},
+      {pl.off_codes + pl.code_bytes, pl.total},
+  };
+  pr->n = 0;
+  for (int i = 0; i < 7; ++i)
+    if (ends[i][1] > ends[i][0]) {
+      pr->off[pr->n] = ends[i][0];
+      pr->len[pr->n] = (int32_t)(ends[i][1] - ends[i][0]);
+      ++pr->n;
+    }
+}
+
+static tah_status_t hip_status(hipError_t e) { return e == hipSuccess ? TAH_OK : TAH_ERR_HIP; }
+
+static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+static bool gpu_tile_ok(int G) { return G == 32 || G == 64 || G == 128; }
+
+static tah_status_t run_encode(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden,
+                               const tah_params_t* p, void* payload, size_t payload_cap, void* y,
+                               tah_dtype_t y_dtype, bool want_y, void* ws, size_t ws_cap, void* stream) {
+  Plan pl;
+  tah_status_t rc = make_plan(tokens, hidden, p, &pl);
+  if (rc != TAH_OK) return rc;
+  if (x_dtype != TAH_DTYPE_F32 && x_dtype != TAH_DTYPE_BF16) return TAH_ERR_INVALID_ARG;
+  if (want_y && y_dtype != TAH_DTYPE_F32 && y_dtype != TAH_DTYPE_BF16) return TAH_ERR_INVALID_ARG;
+  if (!gpu_tile_ok(pl.G)) return TAH_ERR_UNSUPPORTED;
+  if (!ws || !aligned16(ws) || (payload && !aligned16(payload))) return TAH_ERR_INVALID_ARG;
+  if (!want_y && !payload) return TAH_ERR_INVALID_ARG;
+  if (pl.tiles > 0 && (!x || !aligned16(x) || (want_y && (!y || !aligned16(y))))) return TAH_ERR_INVALID_ARG;
+  if (payload && payload_cap < (size_t)pl.total) return TAH_ERR_BUFFER_TOO_SMALL;
+  if (ws_cap < (size_t)pl.ws_total) return TAH_ERR_BUFFER_TOO_SMALL;
+  pl.x_dtype = x_dtype;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const bool mixed = pl.k > 0;
+  if (mixed && pl.tiles > 0) {
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, true, st);
+    if (e != hipSuccess) return hip_status(e);
+    e = launch_select(pl, payload, ws, st);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  return hip_status(launch_encode(pl, x, payload, want_y ? y : nullptr, y_dtype, ws, st, mixed && pl.tiles > 0));
+}
+
+}  // namespace tah
+
+using namespace tah;
+
+extern "C" {
+
+void tah_params_default(tah_params_t* p) {
+  if (!p) return;
+  memset(p, 0, sizeof(*p));
+  p->tile = 64;
+  p->tokens_per_sample = 0;
+  p->bit_budget = 3.8f;
+  p->n_candidates = 2;
+  p->candidates[0] = 3;
+  p->candidates[1] = 4;
+  p->tau = 2.0f;
+}
+
+tah_status_t tah_payload_bytes(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* out) {
+  Plan pl;
+  tah_status_t rc = make_plan(tokens, hidden, p, &pl);
+  if (rc != TAH_OK) return rc;
+  if (!out) return TAH_ERR_INVALID_ARG;
+  *out = (size_t)pl.total;
+  return TAH_OK;
+}
+
+tah_status_t tah_workspace_bytes(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* out) {
+  Plan pl;
+  tah_status_t rc = make_plan(tokens, hidden, p, &pl);
+  if (rc != TAH_OK) return rc;
+  if (!out) return TAH_ERR_INVALID_ARG;
+  *out = (size_t)pl.ws_total;
+  return TAH_OK;
+}
+
+tah_status_t tah_workspace_entropy(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* offset) {
+  Plan pl;
+  tah_status_t rc = make_plan(tokens, hidden, p, &pl);
+  if (rc != TAH_OK) return rc;
+  if (!offset) return TAH_ERR_INVALID_ARG;
+  *offset = (size_t)pl.ws_H;
+  return TAH_OK;
+}
+
+tah_status_t tah_encode(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden, const tah_params_t* p,
+                        void* payload, size_t payload_cap, void* ws, size_t ws_cap, void* stream) {
+  if (!payload) return TAH_ERR_INVALID_ARG;
+  return run_encode(x, x_dtype, tokens, hidden, p, payload, payload_cap, nullptr, TAH_DTYPE_F32, false, ws, ws_cap,
+                    stream);
+}
+
+tah_status_t tah_roundtrip(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden, const tah_params_t* p,
+                           void* payload, size_t payload_cap, void* y, tah_dtype_t y_dtype, void* ws, size_t ws_cap,
+                           void* stream) {
+  return run_encode(x, x_dtype, tokens, hidden, p, payload, payload_cap, y, y_dtype, true, ws, ws_cap, stream);
+}
+
+tah_status_t tah_decode(const void* payload, size_t payload_len, int64_t tokens, int64_t hidden, const tah_params_t* p,
+                        void* y, tah_dtype_t y_dtype, void* ws, size_t ws_cap, void* stream) {
+  Plan pl;
+  tah_status_t rc = make_plan(tokens, hidden, p, &pl);
+  if (rc != TAH_OK) return rc;
+  if (y_dtype != TAH_DTYPE_F32 && y_dtype != TAH_DTYPE_BF16) return TAH_ERR_INVALID_ARG;
+  if (!gpu_tile_ok(pl.G)) return TAH_ERR_UNSUPPORTED;
+  if (!payload || !aligned16(payload) || !ws || !aligned16(ws)) return TAH_ERR_INVALID_ARG;
+  if (pl.tiles > 0 && (!y || !aligned16(y))) return TAH_ERR_INVALID_ARG;
+  if (payload_len < (size_t)pl.total) return TAH_ERR_BUFFER_TOO_SMALL;
+  if (ws_cap < (size_t)pl.ws_total) return TAH_ERR_BUFFER_TOO_SMALL;
+  return hip_status(launch_decode(pl, payload, y, y_dtype, ws, static_cast<hipStream_t>(stream)));
+}
+
+tah_status_t tah_tile_entropy(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden,
+                              const tah_params_t* p, float* h, void* ws, size_t ws_cap, void* stream) {
+  Plan pl;
+  tah_status_t rc = make_plan(tokens, hidden, p, &pl);
+  if (rc != TAH_OK) return rc;
+  if (x_dtype != TAH_DTYPE_F32 && x_dtype != TAH_DTYPE_BF16) return TAH_ERR_INVALID_ARG;
+  if (!gpu_tile_ok(pl.G)) return TAH_ERR_UNSUPPORTED;
+  if (!ws || !aligned16(ws)) return TAH_ERR_INVALID_ARG;
+  if (pl.tiles > 0 && (!x || !aligned16(x) || !h || ((uintptr_t)h & 3u))) return TAH_ERR_INVALID_ARG;
+  if (ws_cap < (size_t)pl.ws_total) return TAH_ERR_BUFFER_TOO_SMALL;
+  if (pl.tiles == 0) return TAH_OK;
+  pl.x_dtype = x_dtype;
+  return hip_status(launch_stats(pl, x, h, ws, false, static_cast<hipStream_t>(stream)));
+}
+
+tah_status_t tah_read_device_status(const void* ws, void* stream, int32_t* out) {
+  if (!ws || !out) return TAH_ERR_INVALID_ARG;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(st) != hipSuccess) return TAH_ERR_HIP;
+  if (hipMemcpy(out, ws, sizeof(int32_t), hipMemcpyDeviceToHost) != hipSuccess) return TAH_ERR_HIP;
+  return TAH_OK;
+}
+
+const char* tah_status_string(tah_status_t s) {
+  switch (s) {
+    case TAH_OK: return "ok";
+    case TAH_ERR_INVALID_ARG: return "invalid argument";
+    case TAH_ERR_UNSUPPORTED: return "unsupported on this device build";
+    case TAH_ERR_BUFFER_TOO_SMALL: return "buffer too small";
+    case TAH_ERR_BUDGET_INFEASIBLE: return "bit budget below the smallest candidate width";
+    case TAH_ERR_BAD_PAYLOAD: return "payload header does not match shape/params";
+    case TAH_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int tah_abi_version(void) { return TAH_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,70 @@
+// Internal declarations of the MI355X TAH-Quant library: the per-call plan
+// (shape, width pair, payload and workspace layout) and the kernel launchers.
+// Nothing here is part of the C ABI (include/tah.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tah.h"
+
+namespace tah {
+
+// Histogram digits of the per-sample radix select (see tah_select.hip).
+constexpr int kDigitBits = 11;
+constexpr int kBins = 1 << kDigitBits;
+constexpr int kMaxPasses = 6;
+
+struct SelectPass {
+  int32_t kind;   // 0: entropy key digit, 1: tile-index digit among tied entropies
+  int32_t shift;  // lowest bit of the digit
+  int32_t width;  // digit width in bits
+  int32_t last_h; // 1 on the last entropy pass
+};
+
+struct Plan {
+  int64_t tokens, hidden, S, nsamples, M, tiles, N, nblocks;
+  int32_t G, log2G, b_lo, b_hi;
+  int64_t k;  // tiles per sample with b_hi
+  int32_t x_dtype;
+  float tau, budget;
+  int32_t n_candidates;
+  uint8_t candidates[4];
+  // payload layout
+  int64_t off_table, off_bitmap, off_side, off_scale, off_zero, off_codes, code_bytes, total;
+  // workspace layout
+  int64_t ws_status, ws_state, ws_counter, ws_hist, ws_H, ws_blockcnt, ws_table, ws_bitmap, ws_total;
+  int32_t npasses;
+  SelectPass passes[kMaxPasses];
+};
+
+// Per-sample selection state, device resident.
+struct SampleState {
+  uint32_t key;     // orderable entropy key prefix; the k-th largest key once the entropy passes end
+  uint32_t upos;    // tile-index prefix among tied keys; the last selected tied index at the end
+  int64_t r;        // rank still to place (1-based) inside the current prefix
+  int32_t tie_all;  // 1: every tile with the threshold key is selected
+  int32_t pad;
+};
+
+struct Header {
+  uint32_t w[32];  // the 128 header bytes
+};
+
+struct PadRanges {
+  int64_t off[8];
+  int32_t len[8];
+  int32_t n;
+};
+
+// Launchers (return hipSuccess or the launch error).
+hipError_t launch_encode(const Plan& pl, const void* x, void* payload, void* y, int y_dtype, void* ws,
+                         hipStream_t st, bool mixed);
+hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, bool init_select, hipStream_t st);
+hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st);
+hipError_t launch_decode(const Plan& pl, const void* payload, void* y, int y_dtype, void* ws, hipStream_t st);
+
+void make_header(const Plan& pl, Header* h);
+void make_pads(const Plan& pl, PadRanges* pr);
+
+}  // namespace tah

@@ -1,0 +1,151 @@
+/*
+ * tah.h — C ABI of the MI355X (gfx950) TAH-Quant activation codec.
+ *
+ * TAH-Quant (Tile-wise Adaptive Hadamard Quantization) compresses the
+ * activation tensor that one pipeline stage sends to the next:
+ *   "TAH-Quant: Effective Activation Quantization in Pipeline Parallelism over
+ *    Slow Network" (arXiv 2506.01352v2), Sections 3.1-3.5 and Algorithm 1.
+ * The sender runs tah_encode (Algorithm 1, line 4), the receiver tah_decode
+ * (line 5); tah_roundtrip does both in one pass over the tensor.
+ *
+ * Tensor view: x and y are row-major [tokens, hidden], tokens = B * S
+ * (micro-batch times sequence), hidden = C channels (§3.1). Each token's
+ * channels split into tiles of G contiguous channels; tile t covers row
+ * t / (hidden / G), channels (t % (hidden / G)) * G ... + G - 1.
+ *
+ * Conventions for every call:
+ *   - x, y, payload and ws are DEVICE pointers (HIP), 16-byte aligned, owned by
+ *     the caller, who keeps them alive until the stream has completed the work.
+ *     The library allocates and frees nothing and keeps no pointer after return.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Work is
+ *     enqueued asynchronously; no call synchronizes except
+ *     tah_read_device_status.
+ *   - Arguments are validated on the host before anything is enqueued; an
+ *     invalid call returns a status other than TAH_OK and enqueues nothing.
+ *     A failed kernel launch returns TAH_ERR_HIP.
+ *   - Non-finite inputs, and inputs with G * max|x| at or above FLT_MAX, give
+ *     undefined (but finite-time, in-bounds) results.
+ *   - Calls that share one workspace must not run concurrently.
+ */
+#ifndef TAH_H
+#define TAH_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TAH_ABI_VERSION 1
+
+typedef enum { TAH_DTYPE_F32 = 0, TAH_DTYPE_BF16 = 1 } tah_dtype_t;
+
+typedef enum {
+  TAH_OK = 0,
+  TAH_ERR_INVALID_ARG = 1,       /* bad shape, pointer or parameter */
+  TAH_ERR_UNSUPPORTED = 2,       /* valid for the format, not built for the GPU (tile not 32/64/128) */
+  TAH_ERR_BUFFER_TOO_SMALL = 3,  /* payload_cap / ws_cap / payload_len below the required size */
+  TAH_ERR_BUDGET_INFEASIBLE = 4, /* bit_budget below the smallest candidate width */
+  TAH_ERR_BAD_PAYLOAD = 5,       /* payload header disagrees with shape/params (device status word) */
+  TAH_ERR_HIP = 6                /* a HIP runtime call or kernel launch failed */
+} tah_status_t;
+
+/*
+ * Codec parameters.
+ *   tile: G, the quantization tile (§3.1) and allocation tile A = G (§3.2,
+ *     the paper's default). A power of two dividing hidden; the GPU kernels are
+ *     built for 32, 64 and 128 (the format allows 8..128).
+ *   tokens_per_sample: S, the ranking scope of the top-p% selection (§3.2:
+ *     tiles are ranked within each sample); 0 = all tokens form one sample.
+ *     tokens % S must be 0.
+ *   bit_budget: average code bits per element of each sample, metadata
+ *     excluded. The two candidates around it, b_lo <= budget < b_hi, are used:
+ *     the k = floor((budget - b_lo) * N / (b_hi - b_lo)) highest-entropy tiles
+ *     of a sample (N tiles) get b_hi, the rest b_lo (§3.2, INT4 for the top p%,
+ *     INT3 for the rest).
+ *   n_candidates, candidates: 1..4 widths, strictly increasing, each 1..8.
+ *   tau: outlier threshold of Eq. (3) (§3.3, default 2.0); 0 transforms every
+ *     non-zero tile, +INFINITY none (Appendix F). Must be >= 0 and not NaN.
+ */
+typedef struct {
+  int32_t tile;
+  int32_t tokens_per_sample;
+  float bit_budget;
+  int32_t n_candidates;
+  uint8_t candidates[4];
+  float tau;
+} tah_params_t;
+
+/* Fills the paper's defaults (§5.1): G = A = 64, 80% INT4 + 20% INT3
+ * (budget 3.8 over {3, 4}), tau = 2, one sample. */
+void tah_params_default(tah_params_t* p);
+
+/*
+ * Size in bytes of the payload for this shape and parameters. The payload is a
+ * fixed-shape uint8 stream (§3.4): its size depends only on (tokens, hidden,
+ * params), never on the values. Layout (little-endian, sections on 256-byte
+ * boundaries): 128-byte header (magic "TAHQ", version, shape, params, section
+ * offsets) | u32 count of b_hi tiles before each run of 64 tiles | width map,
+ * one bit per tile (1 = b_hi) | side byte per tile (bit 7: Hadamard applied,
+ * bits 0-6: pivot index) | bf16 scale per tile | fp32 zero-point per tile |
+ * code blocks of G*b/8 bytes in tile order, codes least-significant-bit first.
+ */
+tah_status_t tah_payload_bytes(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* out);
+
+/* Size in bytes of the device workspace the calls below need for this shape
+ * (per-tile entropies, selection state, the device status word). */
+tah_status_t tah_workspace_bytes(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* out);
+
+/*
+ * Encode x [tokens, hidden] (x_dtype) into payload (payload_cap bytes, at least
+ * tah_payload_bytes). Per tile: entropy (Eq. 1-2), width by per-sample ranking
+ * (§3.2), outlier test (Eq. 3), pivot swap and Hadamard (Eq. 4) on flagged
+ * tiles, asymmetric quantization, packing (§3.4). Per-tile entropies are left
+ * in the workspace (tah_workspace_entropy gives their offset).
+ */
+tah_status_t tah_encode(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden, const tah_params_t* p,
+                        void* payload, size_t payload_cap, void* ws, size_t ws_cap, void* stream);
+
+/*
+ * Decode payload (payload_len bytes) into y [tokens, hidden] (y_dtype; bf16 is
+ * rounded to nearest even) — Algorithm 1, line 5: unpack, dequantize, apply
+ * H^T / G and undo the pivot swap on flagged tiles. The shape and params must
+ * be those of the encode: the device checks the payload header against them
+ * and, on a mismatch, writes TAH_ERR_BAD_PAYLOAD to the workspace status word
+ * and leaves y untouched (read it with tah_read_device_status).
+ */
+tah_status_t tah_decode(const void* payload, size_t payload_len, int64_t tokens, int64_t hidden, const tah_params_t* p,
+                        void* y, tah_dtype_t y_dtype, void* ws, size_t ws_cap, void* stream);
+
+/*
+ * Encode and decode in one pass: y receives exactly what tah_decode would
+ * produce from the payload tah_encode writes. payload may be NULL (then
+ * payload_cap is ignored and nothing is written to it).
+ */
+tah_status_t tah_roundtrip(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden, const tah_params_t* p,
+                           void* payload, size_t payload_cap, void* y, tah_dtype_t y_dtype, void* ws, size_t ws_cap,
+                           void* stream);
+
+/*
+ * Per-tile entropy only (Eq. 1-2, §3.2): h[t] for each of the tokens*hidden/G
+ * tiles, fp32, device pointer. Needs the same workspace as tah_encode.
+ */
+tah_status_t tah_tile_entropy(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden,
+                              const tah_params_t* p, float* h, void* ws, size_t ws_cap, void* stream);
+
+/* Byte offset inside the workspace of the fp32 per-tile entropies written by
+ * tah_encode and tah_roundtrip. */
+tah_status_t tah_workspace_entropy(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* offset);
+
+/* Waits for `stream`, then copies the device status word of the last
+ * tah_decode on this workspace into *out (TAH_OK or TAH_ERR_BAD_PAYLOAD). */
+tah_status_t tah_read_device_status(const void* ws, void* stream, int32_t* out);
+
+const char* tah_status_string(tah_status_t s);
+int tah_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TAH_H */

@@ -1,0 +1,99 @@
+"""Host-only checks of the C-ABI library: it loads, exports every symbol that
+include/tah.h declares, and rejects bad arguments before touching a device.
+No compute call is made here (no GPU in this environment)."""
+
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import activation_quantization_pipeline_amd as tah
+import synth
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tah.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tah_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = tah.lib()
+    names = declared_functions()
+    assert len(names) >= 11
+    assert set(names) == set(tah.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+    assert tah.abi_version() == 1
+
+
+def test_params_default_is_paper_default():
+    p = tah.params_default()
+    assert (p.tile, p.candidates, p.tau) == (64, (3, 4), 2.0)
+    assert abs(p.bit_budget - 3.8) < 1e-6
+
+
+def test_sizes_match_oracle_layout(ref):
+    for name in list(synth.WORKLOADS) + list(synth.COVERAGE):
+        w = synth.workload(name)
+        pl = ref.plan(w.tokens, w.hidden, w.params)
+        assert tah.payload_bytes(w.tokens, w.hidden, w.params) == pl["total"], name
+        assert tah.workspace_bytes(w.tokens, w.hidden, w.params) >= 4 * pl["tiles"]
+
+
+def test_status_strings():
+    for c in range(7):
+        assert tah.status_string(c)
+
+
+def _call_encode(p, tokens=4, hidden=128, x=16, payload=16, ws=16, pcap=1 << 20, wcap=1 << 20, dtype=1):
+    cp = tah._cparams(p)
+    return tah.lib().tah_encode(ctypes.c_void_p(x), dtype, tokens, hidden, ctypes.byref(cp), ctypes.c_void_p(payload),
+                                pcap, ctypes.c_void_p(ws), wcap, ctypes.c_void_p(0))
+
+
+def test_argument_errors_without_device():
+    good = tah.TahParams(tile=64, bit_budget=3.5, candidates=(3, 4))
+    bad = [
+        (dict(tile=48), 1), (dict(tile=256), 1), (dict(candidates=(4, 3)), 1), (dict(candidates=(0, 3)), 1),
+        (dict(candidates=(3, 9)), 1), (dict(tau=math.nan), 1), (dict(tau=-1.0), 1), (dict(bit_budget=math.nan), 1),
+        (dict(bit_budget=math.inf), 1), (dict(tokens_per_sample=3), 1), (dict(bit_budget=2.0), 4),
+        (dict(tile=16), 2), (dict(tile=8), 2),
+    ]
+    for over, code in bad:
+        fields = {**good.__dict__, **over}
+        assert _call_encode(tah.TahParams(**fields)) == code, over
+    # shape and pointer errors
+    assert _call_encode(good, hidden=100) == 1
+    assert _call_encode(good, tokens=-1) == 1
+    assert _call_encode(good, x=0) == 1
+    assert _call_encode(good, x=8) == 1  # not 16-byte aligned
+    assert _call_encode(good, payload=0) == 1
+    assert _call_encode(good, ws=0) == 1
+    assert _call_encode(good, dtype=7) == 1
+    assert _call_encode(good, pcap=10) == 3
+    assert _call_encode(good, wcap=10) == 3
+
+
+def test_decode_argument_errors_without_device():
+    p = tah.TahParams(tile=64, bit_budget=3.0, candidates=(3,))
+    cp = tah._cparams(p)
+    L = tah.lib()
+    need = tah.payload_bytes(4, 128, p)
+    v = ctypes.c_void_p
+    assert L.tah_decode(v(16), need - 1, 4, 128, ctypes.byref(cp), v(16), 0, v(16), 1 << 20, v(0)) == 3
+    assert L.tah_decode(v(0), need, 4, 128, ctypes.byref(cp), v(16), 0, v(16), 1 << 20, v(0)) == 1
+    assert L.tah_decode(v(16), need, 4, 128, ctypes.byref(cp), v(16), 5, v(16), 1 << 20, v(0)) == 1
+    assert L.tah_decode(v(16), need, 4, 128, ctypes.byref(cp), v(0), 0, v(16), 1 << 20, v(0)) == 1
+
+
+def test_payload_size_is_shape_only(ref):
+    p = tah.TahParams(tile=64, tokens_per_sample=1024, bit_budget=3.5, candidates=(2, 3, 4, 8))
+    n1 = tah.payload_bytes(4096, 2048, p)
+    assert n1 == tah.payload_bytes(4096, 2048, p)
+    # no tokens: every section is empty, only the 256-byte header section is left
+    assert tah.payload_bytes(0, 2048, p) == ref.plan(0, 2048, p)["total"] == 256

@@ -1,0 +1,293 @@
+"""GPU-vs-oracle parity of the TAH-Quant HIP path, through the C ABI.
+
+Bar (BASELINE the benchmark spec): width bits, side bytes, scale bits, zero-points and
+packed codes bit-exact; decoded fp32 within 1e-5 * tile scale. The fp32
+operation order is shared by specification, so every payload byte and every
+decoded value is expected to be identical; the tests require exactly that,
+and on a mismatch report which payload section and how many elements differ.
+
+The workloads run at their full sizes (4096 x 2048 ... 16384 x 5120), element
+by element, with the launch configuration the benchmark times.
+"""
+
+import functools
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import activation_quantization_pipeline_amd as tah
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+SECTIONS = ("table", "bitmap", "side", "scale", "zero", "codes")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(x: np.ndarray) -> torch.Tensor:
+    if x.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def to_host(t: torch.Tensor) -> np.ndarray:
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def section_report(P, R, pl):
+    bounds = [("header", 0, 256), ("table", pl["off_table"], pl["off_bitmap"]), ("bitmap", pl["off_bitmap"], pl["off_side"]),
+              ("side", pl["off_side"], pl["off_scale"]), ("scale", pl["off_scale"], pl["off_zero"]),
+              ("zero", pl["off_zero"], pl["off_codes"]), ("codes", pl["off_codes"], pl["total"])]
+    out = []
+    for name, a, b in bounds:
+        d = int(np.count_nonzero(P[a:b] != R[a:b]))
+        if d:
+            first = a + int(np.flatnonzero(P[a:b] != R[a:b])[0])
+            out.append(f"{name}: {d} bytes differ (first at {first})")
+    return "; ".join(out)
+
+
+def assert_payload_equal(P, R, pl, what):
+    assert P.shape == R.shape, f"{what}: size {P.shape} vs {R.shape}"
+    if not np.array_equal(P, R):
+        pytest.fail(f"{what}: payload differs from the oracle: {section_report(P, R, pl)}")
+
+
+def assert_decoded_equal(y, y_ref, R, pl, what):
+    if np.array_equal(y.view(np.uint32) if y.dtype == np.float32 else y,
+                      y_ref.view(np.uint32) if y_ref.dtype == np.float32 else y_ref):
+        return
+    # report against the bar: |diff| <= 1e-5 * tile scale
+    G = pl["G"]
+    s = (R[pl["off_scale"]:pl["off_scale"] + 2 * pl["tiles"]].view(np.uint16).astype(np.uint32) << 16).view(np.float32)
+    yf = y.astype(np.float32) if y.dtype == np.float32 else synth.bf16_bits_to_f32(y)
+    rf = y_ref.astype(np.float32) if y_ref.dtype == np.float32 else synth.bf16_bits_to_f32(y_ref)
+    diff = np.abs(yf.reshape(-1, G).astype(np.float64) - rf.reshape(-1, G))
+    bad = int(np.count_nonzero(diff > 1e-5 * s[:, None]))
+    pytest.fail(f"{what}: decoded values differ from the oracle in {int(np.count_nonzero(diff))} elements, "
+                f"{bad} beyond 1e-5 * scale")
+
+
+@functools.lru_cache(maxsize=1)
+def workload_case(name, seed):
+    w = synth.workload(name)
+    x = synth.generate(name, seed)
+    R = oracle.encode(x, w.params)
+    pl = oracle.plan(w.tokens, w.hidden, w.params)
+    return w, x, R, pl
+
+
+WORKLOADS = list(synth.WORKLOADS) + list(synth.COVERAGE)
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
+def test_workload_parity(name):
+    w, x, R, pl = workload_case(name, 0)
+    p = w.params
+    say(f"[parity] {name}: {w.tokens}x{w.hidden} tile {p.tile} budget {p.bit_budget} cands {p.candidates} "
+        f"tau {p.tau} k={pl['k']}")
+    xt = to_dev(x)
+    ws = tah.alloc_workspace(w.tokens, w.hidden, p)
+
+    say(f"[parity] {name}: encode")
+    P = to_host(tah.encode(xt, p, ws=ws))
+    torch.cuda.synchronize()
+    assert_payload_equal(P, R, pl, f"{name} encode")
+
+    say(f"[parity] {name}: entropy in workspace vs oracle")
+    off = tah.workspace_entropy_offset(w.tokens, w.hidden, p)
+    H = ws[off:off + 4 * pl["tiles"]].cpu().numpy().view(np.float32)
+    rng = np.random.default_rng(1)
+    idx = rng.choice(pl["tiles"], size=min(4000, pl["tiles"]), replace=False)
+    xf = x.astype(np.float32) if x.dtype == np.float32 else synth.bf16_bits_to_f32(x)
+    tiles = xf.reshape(-1, p.tile)
+    H_ref = np.array([oracle.entropy(tiles[i]) for i in idx], np.float32)
+    assert np.array_equal(H[idx].view(np.uint32), H_ref.view(np.uint32))
+
+    say(f"[parity] {name}: oracle decode")
+    y_ref = oracle.decode(R, w.tokens, w.hidden, p, oracle.F32)
+
+    say(f"[parity] {name}: decode of the oracle payload (fp32)")
+    y = to_host(tah.decode(to_dev(R), w.tokens, w.hidden, p, torch.float32, ws=ws))
+    torch.cuda.synchronize()
+    assert tah.read_device_status(ws) == 0
+    assert_decoded_equal(y, y_ref, R, pl, f"{name} decode")
+
+    say(f"[parity] {name}: fused round trip (fp32 out)")
+    y2, P2 = tah.roundtrip(xt, p, torch.float32, ws=ws)
+    assert_payload_equal(to_host(P2), R, pl, f"{name} roundtrip payload")
+    assert_decoded_equal(to_host(y2), y_ref, R, pl, f"{name} roundtrip")
+    del y2, P2
+
+    if w.dtype == synth.BF16:
+        say(f"[parity] {name}: fused round trip (bf16 out, the benchmarked launch)")
+        y_ref16 = oracle.decode(R, w.tokens, w.hidden, p, oracle.BF16)
+        y3, _ = tah.roundtrip(xt, p, torch.bfloat16, ws=ws)
+        assert_decoded_equal(to_host(y3), y_ref16, R, pl, f"{name} roundtrip bf16")
+        say(f"[parity] {name}: decode (bf16 out)")
+        y4 = to_host(tah.decode(to_dev(R), w.tokens, w.hidden, p, torch.bfloat16, ws=ws))
+        assert_decoded_equal(y4, y_ref16, R, pl, f"{name} decode bf16")
+
+
+@pytest.mark.parametrize("name", ["c2_4096x2048_bf16_g64", "c1_256x512_f32_g32"])
+@pytest.mark.parametrize("seed", [1, 2, 3, 4])
+def test_seed_sweep(name, seed):
+    w = synth.workload(name)
+    x = synth.generate(name, seed)
+    say(f"[seeds] {name} seed {seed}")
+    R = oracle.encode(x, w.params)
+    pl = oracle.plan(w.tokens, w.hidden, w.params)
+    y_ref = oracle.decode(R, w.tokens, w.hidden, w.params)
+    y, P = tah.roundtrip(to_dev(x), w.params, torch.float32)
+    assert_payload_equal(to_host(P), R, pl, f"{name} seed {seed}")
+    assert_decoded_equal(to_host(y), y_ref, R, pl, f"{name} seed {seed}")
+
+
+def run_case(x, p, what):
+    """encode, decode and round trip of one small tensor against the oracle."""
+    tokens, hidden = x.shape
+    say(f"[edge] {what}: {tokens}x{hidden} {x.dtype} tile {p.tile} S {p.tokens_per_sample} budget {p.bit_budget} "
+        f"cands {p.candidates} tau {p.tau}")
+    R = oracle.encode(x, p)
+    pl = oracle.plan(tokens, hidden, p)
+    xt = to_dev(x)
+    P = to_host(tah.encode(xt, p))
+    torch.cuda.synchronize()
+    assert_payload_equal(P, R, pl, what)
+    y_ref = oracle.decode(R, tokens, hidden, p)
+    y = to_host(tah.decode(to_dev(R), tokens, hidden, p, torch.float32))
+    assert_decoded_equal(y, y_ref, R, pl, what + " decode")
+    y2, P2 = tah.roundtrip(xt, p, torch.float32)
+    assert_payload_equal(to_host(P2), R, pl, what + " roundtrip")
+    assert_decoded_equal(to_host(y2), y_ref, R, pl, what + " roundtrip")
+    y3, P3 = tah.roundtrip(xt, p, torch.float32, write_payload=False)
+    assert P3 is None
+    assert_decoded_equal(to_host(y3), y_ref, R, pl, what + " roundtrip without payload")
+    return R, y_ref
+
+
+P = tah.TahParams
+
+
+@pytest.mark.parametrize("tile", [32, 64, 128])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_ragged_shapes(tile, dtype):
+    # tile counts that are not multiples of the 64-tile wave or the workgroup
+    for tokens, mult in ((1, 5), (3, 5), (7, 9), (65, 3), (300, 7)):
+        x = synth.random_tensor(tokens, tile * mult, dtype, tokens + mult, n_out=2, mult=25)
+        run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0),
+                 f"ragged t{tokens} m{mult} mixed")
+        run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=4.0, candidates=(4, 8), tau=2.0),
+                 f"ragged t{tokens} m{mult} uniform")
+
+
+@pytest.mark.parametrize("S", [1, 3, 16])
+def test_many_small_samples(S):
+    # samples whose tile count is not a multiple of 64 (ranking scope crosses waves)
+    x = synth.random_tensor(48, 320, synth.BF16, S, n_out=3, mult=30)
+    run_case(x, P(tile=64, tokens_per_sample=S, bit_budget=3.5, candidates=(2, 3, 4, 8), tau=2.0), f"S={S}")
+    run_case(x, P(tile=32, tokens_per_sample=S, bit_budget=2.2, candidates=(2, 3), tau=2.0), f"S={S} tile32")
+
+
+@pytest.mark.parametrize("lo,hi", [(1, 2), (2, 3), (3, 4), (4, 8), (5, 6), (6, 7), (7, 8), (1, 8)])
+@pytest.mark.parametrize("tile", [32, 64, 128])
+def test_every_width(lo, hi, tile):
+    x = synth.random_tensor(40, 4 * tile, synth.F32, lo * 10 + hi, n_out=2, mult=20)
+    run_case(x, P(tile=tile, tokens_per_sample=8, bit_budget=lo + 0.3, candidates=(lo, hi), tau=2.0),
+             f"widths {lo}/{hi}")
+
+
+@pytest.mark.parametrize("tau", [0.0, 2.0, 4.0, math.inf])
+def test_tau_semantics(tau):
+    x = synth.random_tensor(64, 512, synth.BF16, 7, n_out=5, mult=40)
+    R, _ = run_case(x, P(tile=64, tokens_per_sample=0, bit_budget=3.8, candidates=(3, 4), tau=tau), f"tau={tau}")
+    pl = oracle.plan(64, 512, P(tile=64, bit_budget=3.8, candidates=(3, 4), tau=tau))
+    side = R[pl["off_side"]:pl["off_side"] + pl["tiles"]]
+    if tau == 0.0:
+        assert np.all(side >> 7 == 1)
+    if tau == math.inf:
+        assert not np.any(side >> 7)
+
+
+def test_ties_all_zero_and_repeated_tiles():
+    # every tile has entropy 0: the selection keeps the lowest indices
+    z = np.zeros((16, 256), np.float32)
+    run_case(z, P(tile=64, tokens_per_sample=4, bit_budget=3.5, candidates=(3, 4), tau=2.0), "all zero")
+    # the same tile everywhere: equal entropies, ties broken by index
+    row = synth.random_tensor(1, 64, synth.F32, 3)
+    x = np.tile(row, (32, 8))
+    run_case(x, P(tile=64, tokens_per_sample=8, bit_budget=3.3, candidates=(3, 4), tau=2.0), "repeated tile")
+    # half the tiles tied at the threshold
+    x2 = np.concatenate([x[:16], synth.random_tensor(16, 512, synth.F32, 4, scale=3)], 0)
+    run_case(x2, P(tile=64, tokens_per_sample=32, bit_budget=3.6, candidates=(3, 4), tau=2.0), "half tied")
+
+
+def test_value_extremes():
+    g = np.random.default_rng(5)
+    cases = {
+        "subnormal": (g.standard_normal((8, 256)) * 1e-39).astype(np.float32),
+        "tiny_range": (1e-38 + g.standard_normal((8, 256)) * 1e-45).astype(np.float32),
+        "huge": (g.standard_normal((8, 256)) * 1e35).astype(np.float32),
+        "one_hot": np.where(g.random((8, 256)) < 1 / 64, -7.0, 0.0).astype(np.float32),
+        "neg_zero": np.full((8, 256), -0.0, np.float32),
+        "constant": np.full((8, 256), 3.25, np.float32),
+    }
+    for name, x in cases.items():
+        run_case(x, P(tile=64, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0), name)
+        run_case(x, P(tile=32, tokens_per_sample=0, bit_budget=8.0, candidates=(8,), tau=0.0), name + " 8-bit tau0")
+
+
+def test_empty_tensor():
+    p = P(tile=64, tokens_per_sample=0, bit_budget=3.0, candidates=(3,), tau=2.0)
+    x = torch.empty((0, 128), dtype=torch.bfloat16, device="cuda")
+    say("[edge] empty tensor")
+    Pg = to_host(tah.encode(x, p))
+    R = oracle.encode(np.zeros((0, 128), np.uint16), p)
+    assert np.array_equal(Pg, R)
+    y = tah.decode(to_dev(R), 0, 128, p, torch.float32)
+    assert y.shape == (0, 128)
+
+
+def test_bad_header_sets_status_and_leaves_output():
+    p = P(tile=64, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0)
+    x = synth.random_tensor(32, 256, synth.BF16, 9)
+    xt = to_dev(x)
+    ws = tah.alloc_workspace(32, 256, p)
+    say("[edge] corrupted header")
+    Pg = tah.encode(xt, p, ws=ws)
+    y = tah.decode(Pg, 32, 256, p, torch.float32, ws=ws)
+    assert tah.read_device_status(ws) == 0
+    for off in (0, 8, 16, 45, 64):
+        bad = Pg.clone()
+        bad[off] ^= 1
+        sentinel = torch.full((32, 256), 123.0, device="cuda")
+        tah.decode(bad, 32, 256, p, torch.float32, y=sentinel, ws=ws)
+        assert tah.read_device_status(ws) == 5
+        assert torch.all(sentinel == 123.0)
+    # params that disagree with the header
+    sentinel = torch.full((32, 256), 123.0, device="cuda")
+    tah.decode(Pg, 32, 256, P(tile=64, bit_budget=3.5, candidates=(3, 4), tau=4.0), torch.float32, y=sentinel, ws=ws)
+    assert tah.read_device_status(ws) == 5 and torch.all(sentinel == 123.0)
+    tah.decode(Pg, 32, 256, p, torch.float32, y=sentinel, ws=ws)
+    assert tah.read_device_status(ws) == 0 and torch.equal(sentinel, y)
+
+
+def test_determinism_and_tile_entropy_api():
+    w = synth.workload("c2_4096x2048_bf16_g64")
+    x = synth.generate(w.name, 5)
+    xt = to_dev(x)
+    say("[edge] determinism")
+    a = tah.encode(xt, w.params)
+    b = tah.encode(xt, w.params)
+    assert torch.equal(a, b)
+    h = tah.tile_entropy(xt, w.params).cpu().numpy()
+    st = oracle.tile_stats(x[:256], synth.Params(tile=64, tokens_per_sample=0, bit_budget=3.5, candidates=(2, 3, 4, 8)))
+    assert np.array_equal(h[:st["H"].size].view(np.uint32), st["H"].view(np.uint32))
