@@ -271,3 +271,39 @@ def read_device_status(ws: torch.Tensor, stream=None) -> int:
     out = ctypes.c_int32()
     _check(lib().tah_read_device_status(_ptr(ws), _stream(stream), ctypes.byref(out)), "tah_read_device_status")
     return int(out.value)
+
+
+class Codec:
+    """Cached C arguments for repeated calls on fixed buffers (the benchmark's
+    hot loop): one ctypes call per step, nothing else on the host."""
+
+    def __init__(self, tokens: int, hidden: int, p, x_dtype: torch.dtype, y_dtype: torch.dtype | None = None):
+        self.tokens, self.hidden = int(tokens), int(hidden)
+        self.p = p
+        self._cp = _cparams(p)
+        self._pref = ctypes.byref(self._cp)
+        self.x_code = _dtype_code(x_dtype)
+        self.y_code = _dtype_code(y_dtype or x_dtype)
+        self.payload_bytes = payload_bytes(tokens, hidden, p)
+        self.workspace_bytes = max(workspace_bytes(tokens, hidden, p), 256)
+        L = lib()
+        self._rt, self._enc, self._dec = L.tah_roundtrip, L.tah_encode, L.tah_decode
+
+    def roundtrip(self, x, payload, y, ws, stream_handle: int) -> None:
+        rc = self._rt(x.data_ptr(), self.x_code, self.tokens, self.hidden, self._pref,
+                      payload.data_ptr() if payload is not None else None, self.payload_bytes if payload is not None else 0,
+                      y.data_ptr(), self.y_code, ws.data_ptr(), self.workspace_bytes, stream_handle)
+        if rc:
+            raise TahError(rc, "tah_roundtrip")
+
+    def encode(self, x, payload, ws, stream_handle: int) -> None:
+        rc = self._enc(x.data_ptr(), self.x_code, self.tokens, self.hidden, self._pref, payload.data_ptr(),
+                       self.payload_bytes, ws.data_ptr(), self.workspace_bytes, stream_handle)
+        if rc:
+            raise TahError(rc, "tah_encode")
+
+    def decode(self, payload, y, ws, stream_handle: int) -> None:
+        rc = self._dec(payload.data_ptr(), self.payload_bytes, self.tokens, self.hidden, self._pref, y.data_ptr(),
+                       self.y_code, ws.data_ptr(), self.workspace_bytes, stream_handle)
+        if rc:
+            raise TahError(rc, "tah_decode")

@@ -35,8 +35,12 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return u >> 16;
 }
 
+// Two fp32 -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const f32x2_t v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
 // log2 for the entropy (TAH-Quant §3.2, Eq. 2 writes "log"; the base does not
@@ -203,6 +207,37 @@ template <typename T>
 __device__ __forceinline__ uint32_t f32_to_elem_bits(float f) {
   if constexpr (Elem<T>::kBytes == 4) return __float_as_uint(f);
   else return f32_to_bf16_rne(f);
+}
+
+// A group of NT consecutive tiles held in registers on its way to LDS: thread
+// i owns the 16-byte chunks i, i + NT, i + 2 NT, ... of the group, so every
+// load instruction of the workgroup reads one contiguous, coalesced block.
+template <int G, typename T>
+struct GroupRegs {
+  uint4 c[TileRow<G, T>::kChunks];
+};
+
+template <int G, typename T, int NT>
+__device__ __forceinline__ void group_load(const uint8_t* __restrict__ src, int n_tiles, GroupRegs<G, T>& r) {
+  using R = TileRow<G, T>;
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  const int nchunks = n_tiles * R::kChunks;
+#pragma unroll
+  for (int i = 0; i < R::kChunks; ++i) {
+    const int c = threadIdx.x + i * NT;
+    r.c[i] = c < nchunks ? s[c] : make_uint4(0u, 0u, 0u, 0u);
+  }
+}
+
+template <int G, typename T, int NT>
+__device__ __forceinline__ void group_to_lds(const GroupRegs<G, T>& r, uint8_t* lds, int n_tiles) {
+  using R = TileRow<G, T>;
+  const int nchunks = n_tiles * R::kChunks;
+#pragma unroll
+  for (int i = 0; i < R::kChunks; ++i) {
+    const int c = threadIdx.x + i * NT;
+    if (c < nchunks) *reinterpret_cast<uint4*>(lds + (c / R::kChunks) * R::kStride + (c % R::kChunks) * 16) = r.c[i];
+  }
 }
 
 // Copy n_tiles contiguous tiles (global, 16-byte aligned) into padded LDS rows.

@@ -1,0 +1,231 @@
+"""Benchmark of the TAH-Quant codec on one MI355X.
+
+One step = one fused encode + decode (tah_roundtrip: entropy, allocation,
+outlier test, pivot swap + Hadamard, quantization, packing of the payload,
+and the rebuilt bf16 tensor) of the 8192 x 8192 bf16 stage-boundary tensor
+(GeLU(N(0, 2)) activations with 0.1% outlier channels x200; tile 64; budget
+3 bits over {3, 4, 8}). Inputs are resident in HBM before the timed region;
+three buffer sets rotate so no step reads what the previous step left in the
+256 MB Infinity Cache.
+
+value = algorithmic bytes per step (activations read + payload written +
+activations written) / time per step, in GB/s.
+
+Prints one JSON line. Extra legs: encode-only and decode-only rates, the same
+shape with a mixed 80% INT4 / 20% INT3 allocation (the paper's default,
+general two-pass path), a 512 MB device copy for the achievable bandwidth, and
+the CPU oracle on the host (single thread).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published figure
+WORKLOAD = "c5_8192x8192_bf16_g64"
+MIXED = "x2_c5_budget3p8"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_encode_c5_roundtrip_traffic.json")
+CSRC = os.path.join(ROOT, "activation_quantization_pipeline_amd", "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".hpp")):
+            h.update(f.encode())
+            h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(bytes_alg):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (scaled by the same counters on a plain copy), or None when the kernel
+    sources changed since the counters were taken."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return t.get("traffic_bytes_per_launch")
+
+
+def to_dev(x, torch):
+    import numpy as np
+
+    if x.dtype == np.uint16:
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(x).cuda()
+
+
+def time_launches(torch, launch, n_sets, steps, warmup):
+    """Per-launch GPU durations from events on the launch stream, plus the
+    wall time of `steps` back-to-back launches bracketed by synchronize."""
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        launch(i % n_sets)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record(stream)
+        launch(i % n_sets)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [a.elapsed_time(b) for a, b in ev]
+    return wall / steps * 1e3, statistics.mean(per), statistics.median(per), min(per)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
+    ap.add_argument("--no-extras", action="store_true", help="time only the headline round trip")
+    ap.add_argument("--copy-only", action="store_true", help="only a 512 MB device copy (counter calibration)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: the TAH-Quant codec is a per-stage, single-GPU kernel; this build measures one GPU only "
+              "and does not run with --gpus > 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import activation_quantization_pipeline_amd as tah
+    import synth
+
+    dev = torch.device("cuda:0")
+    stream_h = torch.cuda.current_stream().cuda_stream
+
+    if args.copy_only:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        ms, mean, med, mn = time_launches(torch, lambda i: dst.copy_(src), 1, args.steps, args.warmup)
+        print(json.dumps({"copy_bytes": 512 << 20, "copy_ms": med, "copy_gbps": 2 * (512 << 20) / (med * 1e-3) / 1e9}))
+        return
+
+    w = synth.workload(WORKLOAD)
+    p = w.params
+    T, C = w.tokens, w.hidden
+    x_host = synth.generate(WORKLOAD, 0)
+    codec = tah.Codec(T, C, p, torch.bfloat16, torch.bfloat16)
+    n_sets = 3
+    xs = [to_dev(x_host, torch) for _ in range(n_sets)]
+    ys = [torch.empty((T, C), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
+    ps = [torch.empty(codec.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+    ws = torch.empty(codec.workspace_bytes, dtype=torch.uint8, device=dev)
+    x_bytes = T * C * 2
+    bytes_step = x_bytes + codec.payload_bytes + x_bytes  # X read, payload written, Y written
+
+    ms, k_mean, k_med, k_min = time_launches(
+        torch, lambda i: codec.roundtrip(xs[i], ps[i], ys[i], ws, stream_h), n_sets, args.steps, args.warmup)
+    value = bytes_step / (ms * 1e-3) / 1e9
+    achieved = bytes_step / (k_mean * 1e-3) / 1e9
+
+    out = {
+        "metric": "encode+decode GB/s of activations on 1 MI355X; % of HBM peak",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "io_dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "8192x8192 bf16 stage-boundary activations, GeLU(N(0,2)) + 0.1% outlier channels x200; "
+                        "tile 64, budget 3 bits over {3,4,8}, tau 2; fused encode+decode (tah_roundtrip)",
+            "tokens": T,
+            "hidden": C,
+            "tile": p.tile,
+            "bit_budget": p.bit_budget,
+            "candidates": list(p.candidates),
+            "tau": p.tau,
+            "payload_bytes": codec.payload_bytes,
+            "bytes_per_step": bytes_step,
+            "hbm_fraction": round(value / HBM_PEAK_GBPS, 4),
+        },
+        "roofline": {
+            "bound": "hbm",
+            "kernel": "k_encode<64, bf16, bf16 out, uniform allocation>",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": measured_traffic(bytes_step),
+            "kernel_ms_mean": round(k_mean, 5),
+            "kernel_ms_median": round(k_med, 5),
+            "kernel_ms_min": round(k_min, 5),
+            "algorithmic_bytes_per_launch": bytes_step,
+        },
+    }
+
+    if not args.no_extras:
+        extras = {}
+        # encode only and decode only on the same tensor
+        _, e_mean, _, _ = time_launches(torch, lambda i: codec.encode(xs[i], ps[i], ws, stream_h), n_sets,
+                                        args.steps, args.warmup)
+        extras["encode_gbps"] = round((x_bytes + codec.payload_bytes) / (e_mean * 1e-3) / 1e9, 1)
+        _, d_mean, _, _ = time_launches(torch, lambda i: codec.decode(ps[i], ys[i], ws, stream_h), n_sets,
+                                        args.steps, args.warmup)
+        extras["decode_gbps"] = round((x_bytes + codec.payload_bytes) / (d_mean * 1e-3) / 1e9, 1)
+        extras["activation_gbps_roundtrip"] = round(x_bytes / (ms * 1e-3) / 1e9, 1)
+        # general path with a mixed allocation (80% INT4 / 20% INT3) at the same shape
+        wm = synth.workload(MIXED)
+        cm = tah.Codec(T, C, wm.params, torch.bfloat16, torch.bfloat16)
+        pm = [torch.empty(cm.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+        wsm = torch.empty(cm.workspace_bytes, dtype=torch.uint8, device=dev)
+        m_ms, _, _, _ = time_launches(torch, lambda i: cm.roundtrip(xs[i], pm[i], ys[i], wsm, stream_h), n_sets,
+                                      args.steps, args.warmup)
+        extras["mixed_80_20_roundtrip_gbps"] = round((2 * x_bytes + cm.payload_bytes) / (m_ms * 1e-3) / 1e9, 1)
+        extras["mixed_80_20_ms_per_step"] = round(m_ms, 5)
+        del pm, wsm
+        # achievable bandwidth of a plain 512 MB device copy
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        _, c_mean, _, _ = time_launches(torch, lambda i: dst.copy_(src), 1, 50, 5)
+        extras["copy_512MB_gbps"] = round(2 * (512 << 20) / (c_mean * 1e-3) / 1e9, 1)
+        del src, dst
+        out["extras"] = extras
+
+    if not args.no_cpu_baseline:
+        import oracle
+
+        runs = []
+        for _ in range(3):
+            t0 = time.perf_counter()
+            R = oracle.encode(x_host, p)
+            oracle.decode(R, T, C, p, oracle.BF16)
+            runs.append(time.perf_counter() - t0)
+            if runs[-1] > 10.0:
+                break
+        t_cpu = statistics.median(runs)
+        out["cpu_baseline"] = {
+            "value": round(bytes_step / t_cpu / 1e9, 4),
+            "unit": "GB/s",
+            "cores": 1,
+            "kind": "oracle",
+            "sample": f"the full 8192x8192 tensor of this workload, oracle encode then decode to bf16, "
+                      f"single thread, median of {len(runs)} runs ({t_cpu:.2f} s each)",
+        }
+
+    print(json.dumps(out))
+
+
+if __name__ == "__main__":
+    main()
