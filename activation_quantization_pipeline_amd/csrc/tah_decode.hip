@@ -136,7 +136,9 @@ __global__ __launch_bounds__((dec_tiles_per_wg<G, TOut>())) void k_decode(DecArg
   meta_side[tid] = (uint8_t)side;
   meta_hi[tid] = (uint8_t)hi;
 
-  const int cls = act ? (flag | (hi << 1)) : 4;
+  // plain tiles first, transformed tiles as one run rotated to wave (block mod NW)
+  // so that the Hadamard work spreads over the CU's SIMDs
+  const int cls = act ? ((flag << 1) | hi) : 4;
   const uint64_t b0 = ballot(cls == 0), b1 = ballot(cls == 1), b2 = ballot(cls == 2), b3 = ballot(cls == 3);
   if (lane == 0) {
     cnt[wave][0] = __popcll(b0);
@@ -153,6 +155,11 @@ __global__ __launch_bounds__((dec_tiles_per_wg<G, TOut>())) void k_decode(DecArg
       for (int w = 0; w < NW; ++w) dst += (c < cls || (c == cls && w < wave)) ? cnt[w][c] : 0;
     const uint64_t mine = cls == 0 ? b0 : cls == 1 ? b1 : cls == 2 ? b2 : b3;
     dst += (int)lanes_below(mine);
+    int plain = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) plain += cnt[w][0] + cnt[w][1];
+    const int start = (int)(blockIdx.x % NW) * 64;
+    dst = (dst + n + start - plain) % n;
     perm[dst] = (uint16_t)tid;
   }
   __syncthreads();

@@ -81,6 +81,55 @@ __device__ __forceinline__ void fwht(float (&v)[G]) {
   }
 }
 
+// Value of v in lane (lane xor M), M in {1, 2, 4, 8}: DPP quad permutes for
+// 1 and 2, a bit-mode swizzle for 4 and 8. The partner lane must be active.
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+  const int i = __float_as_int(v);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true));  // [1,0,3,2]
+  else if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true));  // [2,3,0,1]
+  else return __int_as_float(__builtin_amdgcn_ds_swizzle(i, 0x1F | (M << 10)));  // and 0x1f, xor M
+}
+
+// The same transform as fwht<G> spread over the 16 lanes of an aligned group:
+// lane r holds elements [r V, r V + V) of the tile (V = G / 16). Stages
+// h < V are butterflies inside the lane; stage h = V M pairs lane r with
+// r xor M. Every butterfly is the same single-rounded a + b / a - b as in
+// fwht<G>, in the same stage order, so the results are identical.
+template <int V>
+__device__ __forceinline__ void fwht16(float (&y)[V], int r) {
+#pragma unroll
+  for (int h = 1; h < V; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      if ((j & h) == 0) {
+        const float a = y[j], b = y[j + h];
+        y[j] = a + b;
+        y[j + h] = a - b;
+      }
+  // lower lane: own + partner; upper lane: partner - own (fma with -1 rounds once)
+  {
+    const float sg = (r & 1) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) y[i] = __builtin_fmaf(y[i], sg, xor_lane<1>(y[i]));
+  }
+  {
+    const float sg = (r & 2) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) y[i] = __builtin_fmaf(y[i], sg, xor_lane<2>(y[i]));
+  }
+  {
+    const float sg = (r & 4) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) y[i] = __builtin_fmaf(y[i], sg, xor_lane<4>(y[i]));
+  }
+  {
+    const float sg = (r & 8) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) y[i] = __builtin_fmaf(y[i], sg, xor_lane<8>(y[i]));
+  }
+}
+
 // Number of lanes below this one whose bit is set in mask.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
@@ -209,6 +258,38 @@ __device__ __forceinline__ uint32_t f32_to_elem_bits(float f) {
   else return f32_to_bf16_rne(f);
 }
 
+// Elements [r V, r V + V) of an LDS tile row, as fp32 (bf16 widens exactly).
+template <int V, typename T>
+__device__ __forceinline__ void lds_read_part(const uint8_t* row, int r, float (&y)[V]) {
+  if constexpr (Elem<T>::kBytes == 4) {
+    const float* p = reinterpret_cast<const float*>(row) + r * V;
+#pragma unroll
+    for (int i = 0; i < V; ++i) y[i] = p[i];
+  } else {
+    const uint32_t* p = reinterpret_cast<const uint32_t*>(row) + r * (V / 2);
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) {
+      const uint32_t u = p[i];
+      y[2 * i] = __uint_as_float(u << 16);
+      y[2 * i + 1] = __uint_as_float(u & 0xffff0000u);
+    }
+  }
+}
+
+// Elements [r V, r V + V) of an LDS tile row from fp32 (bf16: round to nearest even).
+template <int V, typename T>
+__device__ __forceinline__ void lds_write_part(uint8_t* row, int r, const float (&y)[V]) {
+  if constexpr (Elem<T>::kBytes == 4) {
+    float* p = reinterpret_cast<float*>(row) + r * V;
+#pragma unroll
+    for (int i = 0; i < V; ++i) p[i] = y[i];
+  } else {
+    uint32_t* p = reinterpret_cast<uint32_t*>(row) + r * (V / 2);
+#pragma unroll
+    for (int i = 0; i < V / 2; ++i) p[i] = pack_bf16x2(y[2 * i], y[2 * i + 1]);
+  }
+}
+
 // A group of NT consecutive tiles held in registers on its way to LDS: thread
 // i owns the 16-byte chunks i, i + NT, i + 2 NT, ... of the group, so every
 // load instruction of the workgroup reads one contiguous, coalesced block.
@@ -222,21 +303,37 @@ __device__ __forceinline__ void group_load(const uint8_t* __restrict__ src, int 
   using R = TileRow<G, T>;
   const uint4* s = reinterpret_cast<const uint4*>(src);
   const int nchunks = n_tiles * R::kChunks;
+  if (n_tiles == NT) {
 #pragma unroll
-  for (int i = 0; i < R::kChunks; ++i) {
-    const int c = threadIdx.x + i * NT;
-    r.c[i] = c < nchunks ? s[c] : make_uint4(0u, 0u, 0u, 0u);
+    for (int i = 0; i < R::kChunks; ++i) r.c[i] = s[threadIdx.x + i * NT];
+  } else {
+#pragma unroll
+    for (int i = 0; i < R::kChunks; ++i) {
+      const int c = threadIdx.x + i * NT;
+      r.c[i] = c < nchunks ? s[c] : make_uint4(0u, 0u, 0u, 0u);
+    }
   }
+}
+
+// Makes the compiler wait for the loads of r here (an empty asm that reads them).
+template <int G, typename T>
+__device__ __forceinline__ void group_wait(const GroupRegs<G, T>& r) {
+#pragma unroll
+  for (int i = 0; i < TileRow<G, T>::kChunks; ++i)
+    asm volatile("" ::"v"(r.c[i].x), "v"(r.c[i].y), "v"(r.c[i].z), "v"(r.c[i].w));
 }
 
 template <int G, typename T, int NT>
 __device__ __forceinline__ void group_to_lds(const GroupRegs<G, T>& r, uint8_t* lds, int n_tiles) {
   using R = TileRow<G, T>;
+  static_assert(NT % R::kChunks == 0, "a pass of NT chunks covers whole tiles");
   const int nchunks = n_tiles * R::kChunks;
+  // chunk threadIdx.x + i NT lands in row threadIdx.x / kChunks + i NT / kChunks
+  uint8_t* base = lds + (threadIdx.x / R::kChunks) * R::kStride + (threadIdx.x % R::kChunks) * 16;
 #pragma unroll
   for (int i = 0; i < R::kChunks; ++i) {
-    const int c = threadIdx.x + i * NT;
-    if (c < nchunks) *reinterpret_cast<uint4*>(lds + (c / R::kChunks) * R::kStride + (c % R::kChunks) * 16) = r.c[i];
+    if (n_tiles == NT || (int)threadIdx.x + i * NT < nchunks)
+      *reinterpret_cast<uint4*>(base + i * (NT / R::kChunks) * R::kStride) = r.c[i];
   }
 }
 
@@ -266,11 +363,14 @@ __device__ __forceinline__ void stage_in(const uint8_t* __restrict__ src, uint8_
 template <int G, typename T, int NT>
 __device__ __forceinline__ void stage_out(const uint8_t* lds, uint8_t* __restrict__ dst, int n_tiles) {
   using R = TileRow<G, T>;
+  static_assert(NT % R::kChunks == 0, "a pass of NT chunks covers whole tiles");
   const int nchunks = n_tiles * R::kChunks;
-  uint4* d = reinterpret_cast<uint4*>(dst);
-  for (int c = threadIdx.x; c < nchunks; c += NT) {
-    uint4 v = *reinterpret_cast<const uint4*>(lds + (c / R::kChunks) * R::kStride + (c % R::kChunks) * 16);
-    d[c] = v;
+  const uint8_t* base = lds + (threadIdx.x / R::kChunks) * R::kStride + (threadIdx.x % R::kChunks) * 16;
+  uint4* d = reinterpret_cast<uint4*>(dst) + threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < R::kChunks; ++i) {
+    if (n_tiles == NT || (int)threadIdx.x + i * NT < nchunks)
+      d[i * NT] = *reinterpret_cast<const uint4*>(base + i * (NT / R::kChunks) * R::kStride);
   }
 }
 

@@ -1,23 +1,22 @@
 // Encode and fused encode+decode kernels of the TAH-Quant codec for gfx950.
 //
-// One workgroup takes NT consecutive tiles (NT lanes, one tile per lane):
-//  1. stage:   the NT tiles (contiguous in HBM) are copied into padded LDS
-//              rows with 16-byte coalesced loads;
+// A workgroup is one wavefront; it takes groups of 64 consecutive tiles, one
+// tile per lane:
+//  1. stage:   the 64 tiles (contiguous in HBM) arrive with 16-byte coalesced
+//              loads (prefetched one group ahead) and go into padded LDS rows;
 //  2. phase A: lane i reads tile i from LDS and computes the outlier ratio of
-//              Eq. (3) (top-2 magnitudes, pivot d, flag), and, for a uniform
+//              Eq. (3) (top-2 magnitudes, pivot d, flag) and, for a uniform
 //              allocation, the tile entropy of Eq. (1)-(2); with a mixed
 //              allocation the width bit comes from the selection pass instead.
 //              It fixes the tile's code-block offset (§3.4 packing order);
-//  3. compact: tiles are regrouped by class (transformed or not x width) so
-//              that whole wavefronts take the same branch: the Hadamard path
-//              of §3.3 then runs only in the waves that hold flagged tiles;
-//  4. phase B: each lane re-reads its assigned tile, applies the pivot swap
-//              (P_d, done in LDS) and the register FWHT (Eq. 4) if flagged,
-//              quantizes asymmetrically, packs the codes and stores code block,
+//  3. forward: the flagged tiles get the pivot swap P_d and the Hadamard
+//              transform of Eq. (4), computed by 16-lane groups through LDS;
+//  4. quantize: every lane quantizes its (transformed or not) tile
+//              asymmetrically (§3.3), packs the codes and stores code block,
 //              scale and zero-point; the fused variant dequantizes from the
-//              codes in registers, inverts the transform (H^T / G, undo swap)
-//              and writes the tile back to LDS;
-//  5. out:     the rebuilt tiles leave LDS with 16-byte coalesced stores.
+//              codes in registers into the tile's LDS row;
+//  5. inverse: flagged tiles get H^T / G and the swap undone (16-lane groups);
+//  6. out:     the rebuilt tiles leave LDS with 16-byte coalesced stores.
 #include "tah_device.hpp"
 #include "tah_internal.hpp"
 
@@ -43,21 +42,10 @@ constexpr int tiles_per_wg() {
   return TileRow<G, T>::kBytes <= 128 ? 256 : (TileRow<G, T>::kBytes <= 256 ? 128 : 64);
 }
 
-// Rebuilt tile into its LDS row (T), then the pivot swap is undone in place.
-template <int G, typename T>
-__device__ __forceinline__ void write_y_row(uint8_t* row, const float (&v)[G], int flag, int piv) {
-  lds_write_tile<G, T>(row, v);
-  if (flag) {
-    const uint32_t yd = lds_elem_bits<T>(row, piv);
-    lds_elem_set<T>(row, piv, f32_to_elem_bits<T>(v[0]));
-    lds_elem_set<T>(row, 0, yd);
-  }
-}
-
 // Minimum waves per SIMD the register allocator must leave room for.
-template <int G, typename T>
+template <int G, typename T, int OUT>
 constexpr int kMinWaves() {
-  return G <= 64 ? 3 : 1;
+  return (G <= 64 && OUT != 0 && Elem<T>::kBytes == 2) ? 3 : (G <= 64 ? 2 : 1);
 }
 
 template <int G, int B>
@@ -154,68 +142,136 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
   }
 }
 
+// Step s rounded up to bf16 and its reciprocal (§3.3 asymmetric quantizer).
+__device__ __forceinline__ void step_of(float lo, float hv, int b, float& s, float& inv) {
+  const float L = (float)((1 << b) - 1);
+  uint32_t sb = __float_as_uint((hv - lo) / L);
+  if (sb & 0xffffu) sb = (sb & 0xffff0000u) + 0x10000u;
+  s = __uint_as_float(sb);
+  if (!(s >= 0x1p-126f)) s = 0.0f;
+  inv = s > 0.0f ? 1.0f / s : 0.0f;
+}
+
+// Quantize one tile held in registers (§3.3): zero-point lo = min, step from
+// the range, codes q_k = round-half-even of the exact (y_k - lo) * inv (one
+// fused rounding against 2^23); store code block, scale and zero-point. With
+// OUT the tile is replaced by its dequantized values (the receiver's step of
+// Algorithm 1, from the codes in registers).
+template <int G, int OUT>
+__device__ __forceinline__ void quantize_tile(const EncArgs& a, float (&v)[G], int64_t t, int b, int64_t code_off) {
+  float lo = v[0], hv = v[0];
+#pragma unroll
+  for (int k = 1; k < G; ++k) {
+    lo = fminf(lo, v[k]);
+    hv = fmaxf(hv, v[k]);
+  }
+  lo = lo + 0.0f;
+  hv = hv + 0.0f;
+  float s, inv;
+  step_of(lo, hv, b, s, inv);
+  uint32_t mq[G];
+#pragma unroll
+  for (int k = 0; k < G; ++k) mq[k] = __float_as_uint(__builtin_fmaf(v[k] - lo, inv, 0x1p23f));
+  if (a.payload) {
+    store_codes_b<G>(b, mq, a.payload + code_off);
+    reinterpret_cast<uint16_t*>(a.payload + a.off_scale)[t] = (uint16_t)(__float_as_uint(s) >> 16);
+    reinterpret_cast<float*>(a.payload + a.off_zero)[t] = lo;
+  }
+  if constexpr (OUT != 0) {
+#pragma unroll
+    for (int k = 0; k < G; ++k) v[k] = __builtin_fmaf(__uint_as_float(mq[k]) - 0x1p23f, s, lo);
+  }
+}
+
 // OUT: 0 = no reconstruction, 1 = fp32, 2 = bf16.
-// Persistent workgroups: group g of NT tiles is processed by workgroup
-// g mod gridDim.x; while a group is being processed, the next group's tiles
-// are already on their way from HBM into registers.
+// A workgroup is one wavefront with LDS rows of its own, and it is persistent:
+// group g of 64 tiles goes to workgroup g mod gridDim.x. Groups of small tiles
+// are prefetched into registers while the current group is processed.
+//
+// Transformed tiles (flag set by Eq. 3) are few and scattered, so their
+// Hadamard transforms are not run in the lane that owns the tile (that would
+// make the whole wavefront execute both paths): 16-lane groups transform them,
+// four tiles at a time, into LDS slots of fp32; the owning lane takes the
+// transformed tile from its slot, runs the same quantizer as every other lane
+// and puts the dequantized values back; the 16-lane groups then invert the
+// transform into the output row. The first kCoop transformed tiles of a group
+// are quantized together with the plain tiles; groups with more (tau near 1)
+// take further rounds of kCoop.
 template <int G, typename TIn, int OUT, bool MIXED>
-__global__ __launch_bounds__((tiles_per_wg<G, TIn>()), (kMinWaves<G, TIn>())) void k_encode(EncArgs a) {
-  constexpr int NT = tiles_per_wg<G, TIn>();
-  constexpr int NW = NT / 64;
+__global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncArgs a) {
+  constexpr int NT = 64;
+  constexpr int V = G / 16;     // elements per lane in a 16-lane transform group
+  constexpr int kCoop = 8;      // transformed tiles per group handled by 16-lane groups
+  constexpr int kSlot = G + 4;  // fp32 slot stride: 16 bytes of padding
   using RI = TileRow<G, TIn>;
   using TOut = typename std::conditional<OUT == 1, float, bf16_t>::type;
   using RO = TileRow<G, TOut>;
-  constexpr int kRowMax = (OUT != 0 && RO::kStride > RI::kStride) ? RO::kStride : RI::kStride;
-  // After compaction every LDS row is read and rewritten by the one lane that
-  // owns it, so a rebuilt tile can go straight back into its own row when the
-  // output row is not wider than the input row.
-  constexpr bool kSameRow = RO::kStride == RI::kStride;
+  constexpr bool kPrefetch = RI::kChunks <= 8;
+  // Each LDS row is read and rewritten only by its own lane, so a rebuilt tile
+  // goes back into its own row when rows have the same width; otherwise
+  // rebuilt tiles get rows of their own.
+  constexpr bool kSameRow = OUT == 0 || RO::kStride == RI::kStride;
 
-  __shared__ __attribute__((aligned(16))) uint8_t xs[NT * kRowMax];
-  __shared__ uint32_t meta_off[NT];
-  __shared__ uint8_t meta_side[NT];
-  __shared__ uint8_t meta_hi[NT];
-  __shared__ uint16_t perm[NT];
-  __shared__ int cnt[NW][4];
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NT * RI::kStride];
+  __shared__ __attribute__((aligned(16))) uint8_t ys_own[kSameRow ? 16 : NT * RO::kStride];
+  __shared__ __attribute__((aligned(16))) float ts[kCoop * kSlot];
+  __shared__ uint32_t flist[NT];
+  uint8_t* ys = kSameRow ? xs : ys_own;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x;
+  const int q4 = lane >> 4, r16 = lane & 15;  // 16-lane group and lane within it
 
   if (blockIdx.x == 0 && a.payload) {
-    if (tid < 32) reinterpret_cast<uint32_t*>(a.payload)[tid] = a.hdr.w[tid];
+    if (lane < 32) reinterpret_cast<uint32_t*>(a.payload)[lane] = a.hdr.w[lane];
     for (int r = 0; r < a.pads.n; ++r)
-      for (int i = tid; i < a.pads.len[r]; i += NT) a.payload[a.pads.off[r] + i] = 0;
+      for (int i = lane; i < a.pads.len[r]; i += NT) a.payload[a.pads.off[r] + i] = 0;
   }
 
   const int64_t ngroups = (a.tiles + NT - 1) / NT;
   int64_t g = blockIdx.x;
   GroupRegs<G, TIn> pre;
-  if (g < ngroups) {
+  if (kPrefetch && g < ngroups) {
     const int64_t t0 = g * NT;
     group_load<G, TIn, NT>(a.x + t0 * RI::kBytes, (int)min<int64_t>(NT, a.tiles - t0), pre);
   }
 
+  // The rebuilt tiles of a group leave LDS at the top of the next iteration,
+  // after the prefetched tiles have arrived: loads and stores share one
+  // completion counter on this target, so waiting for the prefetch only ever
+  // drains stores issued a whole group earlier.
+  int64_t prev_t0 = -1;
+  int prev_n = 0;
   for (; g < ngroups; g += gridDim.x) {
     const int64_t t0 = g * NT;
     const int n = (int)min<int64_t>(NT, a.tiles - t0);
+    if constexpr (!kPrefetch) group_load<G, TIn, NT>(a.x + t0 * RI::kBytes, n, pre);
+    group_wait(pre);
+    if constexpr (OUT != 0) {
+      if (prev_t0 >= 0) stage_out<G, TOut, NT>(ys, a.y + prev_t0 * RO::kBytes, prev_n);
+    }
     group_to_lds<G, TIn, NT>(pre, xs, n);
     __syncthreads();
-    {  // prefetch the next group of this workgroup
+    if constexpr (kPrefetch) {  // the next group of this workgroup
       const int64_t gn = g + gridDim.x;
       if (gn < ngroups) {
         const int64_t tn = gn * NT;
         group_load<G, TIn, NT>(a.x + tn * RI::kBytes, (int)min<int64_t>(NT, a.tiles - tn), pre);
+      } else {
+        // last group: the old contents are dead (without this the compiler keeps
+        // them alive through the iteration for the wait at the loop top)
+        pre = GroupRegs<G, TIn>{};
       }
     }
 
-    // ---------------- phase A: lane tid owns tile t0 + tid ----------------
-    const bool act = tid < n;
-    const int64_t t = t0 + tid;
+    // ---------------- phase A: lane owns tile t0 + lane ----------------
+    const bool act = lane < n;
+    const int64_t t = t0 + lane;
     int flag = 0, piv = 0, hi = 0;
+    float v[G];
     if (act) {
-      float v[G];
       float m1, m2, l1;
       int d;
-      tile_stats<G, TIn>(xs + tid * RI::kStride, v, m1, m2, d, l1);
+      tile_stats<G, TIn>(xs + lane * RI::kStride, v, m1, m2, d, l1);
       flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
       piv = d;
       if constexpr (!MIXED) {
@@ -234,122 +290,116 @@ __global__ __launch_bounds__((tiles_per_wg<G, TIn>()), (kMinWaves<G, TIn>())) vo
       if (a.payload) a.payload[a.off_side + t] = (uint8_t)((flag << 7) | piv);
     }
 
-    // Code-block offsets: tile t starts at t*sz_lo + (b_hi tiles before t)*(sz_hi - sz_lo).
+    // Code-block offsets: tile t starts at t*sz_lo + (b_hi tiles before t)*(sz_hi - sz_lo);
+    // the 64 tiles of a group are one run of the block table.
     const uint64_t hmask = ballot(act && hi);
-    uint32_t rel_off = (uint32_t)tid * (uint32_t)a.sz_lo;
-    int64_t wg_off = t0 * a.sz_lo;
+    int64_t code_off = a.off_codes + t * a.sz_lo;
     if constexpr (MIXED) {
-      const uint32_t hb_wg = a.table[t0 >> 6];
-      const uint32_t hb = (t0 + 64 * wave < a.tiles ? a.table[(t0 >> 6) + wave] : hb_wg) + lanes_below(hmask);
-      rel_off += (hb - hb_wg) * (uint32_t)(a.sz_hi - a.sz_lo);
-      wg_off += (int64_t)hb_wg * (a.sz_hi - a.sz_lo);
+      const uint32_t hb = a.table[t0 >> 6] + lanes_below(hmask);
+      code_off += (int64_t)hb * (a.sz_hi - a.sz_lo);
     } else {
       // uniform allocation: no tile has b_hi
-      if (lane == 0 && a.bitmap && t0 + 64 * wave < a.tiles) {
-        const int64_t blk = (t0 >> 6) + wave;
+      if (lane == 0 && a.bitmap) {
+        const int64_t blk = t0 >> 6;
         a.bitmap[2 * blk] = 0u;
         a.bitmap[2 * blk + 1] = 0u;
         a.table[blk] = 0u;
       }
     }
 
-    // ---------------- compaction by class ----------------
-    const int cls = act ? (flag | (hi << 1)) : 4;
-    const uint64_t b0 = ballot(cls == 0), b1 = ballot(cls == 1), b2 = ballot(cls == 2), b3 = ballot(cls == 3);
-    if (lane == 0) {
-      cnt[wave][0] = __popcll(b0);
-      cnt[wave][1] = __popcll(b1);
-      cnt[wave][2] = __popcll(b2);
-      cnt[wave][3] = __popcll(b3);
-    }
-    meta_off[tid] = rel_off;
-    meta_side[tid] = (uint8_t)((flag << 7) | piv);
-    meta_hi[tid] = (uint8_t)hi;
-    __syncthreads();
-    if (act) {
-      int dst = 0;
+    // ---------------- transformed tiles (§3.3) ----------------
+    // flist[j] names the j-th flagged tile of the group (lane | pivot << 8);
+    // rounds of up to kCoop of them use the LDS slots, tile j in slot j - j_lo.
+    const uint64_t fmask = ballot(act && flag);
+    const int nf = (int)__popcll(fmask);
+    const int slot = (int)lanes_below(fmask);
+    const int b = hi ? a.b_hi : a.b_lo;
+    // P_d (the first and the d-th element exchange places) and H of Eq. (4)
+    // without the 1/sqrt(G), by 16-lane groups, four tiles at a time.
+    auto forward = [&](int j_lo, int j_hi) {
+      for (int j0 = j_lo; j0 < j_hi; j0 += 4) {
+        const int j = j0 + q4;
+        uint32_t e = 0;
+        if (j < j_hi) {
+          e = flist[j];
+          if (r16 == 0) {
+            uint8_t* row = xs + (e & 255u) * RI::kStride;
+            const int d = (int)(e >> 8);
+            const uint32_t x0 = lds_elem_bits<TIn>(row, 0), xd = lds_elem_bits<TIn>(row, d);
+            lds_elem_set<TIn>(row, 0, xd);
+            lds_elem_set<TIn>(row, d, x0);
+          }
+        }
+        __syncthreads();
+        if (j < j_hi) {
+          float y[V];
+          lds_read_part<V, TIn>(xs + (e & 255u) * RI::kStride, r16, y);
+          fwht16<V>(y, r16);
+          lds_write_part<V, float>(reinterpret_cast<uint8_t*>(ts + (j - j_lo) * kSlot), r16, y);
+        }
+      }
+      __syncthreads();
+    };
+    // H^T = H, the 1/G, and the swap undone, into the tile's output row.
+    auto inverse = [&](int j_lo, int j_hi) {
+      __syncthreads();
+      for (int j0 = j_lo; j0 < j_hi; j0 += 4) {
+        const int j = j0 + q4;
+        if (j < j_hi) {
+          const uint32_t e = flist[j];
+          uint8_t* row = ys + (e & 255u) * RO::kStride;
+          float y[V];
+          lds_read_part<V, float>(reinterpret_cast<const uint8_t*>(ts + (j - j_lo) * kSlot), r16, y);
+          fwht16<V>(y, r16);
 #pragma unroll
-      for (int c = 0; c < 4; ++c)
-#pragma unroll
-        for (int w = 0; w < NW; ++w) dst += (c < cls || (c == cls && w < wave)) ? cnt[w][c] : 0;
-      const uint64_t mine = cls == 0 ? b0 : cls == 1 ? b1 : cls == 2 ? b2 : b3;
-      dst += (int)lanes_below(mine);
-      perm[dst] = (uint16_t)tid;
-    }
-    __syncthreads();
+          for (int i = 0; i < V; ++i) y[i] = y[i] * (1.0f / G);
+          lds_write_part<V, TOut>(row, r16, y);
+          if (r16 == 0) {  // element d takes y_0, element 0 takes y_d
+            const int d = (int)(e >> 8);
+            const uint32_t yd = lds_elem_bits<TOut>(row, d);
+            lds_elem_set<TOut>(row, d, f32_to_elem_bits<TOut>(y[0]));
+            lds_elem_set<TOut>(row, 0, yd);
+          }
+        }
+      }
+    };
 
-    // ---------------- phase B: lane tid takes tile j = perm[tid] ----------------
-    float v[G];
-    int j = 0;
-    flag = 0;
-    piv = 0;
-    if (act) {
-      j = perm[tid];
-      const uint32_t side = meta_side[j];
-      flag = side >> 7;
-      piv = side & 127;
-      hi = meta_hi[j];
-      uint8_t* row = xs + j * RI::kStride;
-      uint32_t xd = 0;
-      if (flag) {  // pivot swap P_d (§3.3): slot d <- x_0 here, x_d goes to register 0
-        const uint32_t x0 = lds_elem_bits<TIn>(row, 0);
-        xd = lds_elem_bits<TIn>(row, piv);
-        lds_elem_set<TIn>(row, piv, x0);
+    if (nf != 0) {
+      if (act && flag) flist[slot] = (uint32_t)lane | ((uint32_t)piv << 8);
+      __syncthreads();
+    }
+    // Round 0 quantizes the plain tiles and the first kCoop transformed tiles;
+    // further rounds (groups with many transformed tiles) take kCoop more each.
+    for (int j_lo = 0;; j_lo += kCoop) {
+      const int j_hi = nf < j_lo + kCoop ? nf : j_lo + kCoop;
+      const bool mine = act && (flag ? (slot >= j_lo && slot < j_hi) : j_lo == 0);
+      uint8_t* sl = reinterpret_cast<uint8_t*>(ts + (slot - j_lo) * kSlot);
+      if (j_hi > j_lo) {
+        forward(j_lo, j_hi);
+        if (mine && flag) lds_read_tile<G, float>(sl, v);
       }
-      lds_read_tile<G, TIn>(row, v);
-      if (flag) {
-        v[0] = elem_bits_to_f32<TIn>(xd);
-        fwht<G>(v);  // Eq. (4) without the 1/sqrt(G)
-      }
-      // asymmetric quantizer: zero-point lo, step s rounded up to bf16
-      float lo = v[0], hv = v[0];
-#pragma unroll
-      for (int k = 1; k < G; ++k) {
-        lo = fminf(lo, v[k]);
-        hv = fmaxf(hv, v[k]);
-      }
-      lo = lo + 0.0f;
-      hv = hv + 0.0f;
-      const int b = hi ? a.b_hi : a.b_lo;
-      const float L = (float)((1 << b) - 1);
-      uint32_t sb = __float_as_uint((hv - lo) / L);
-      if (sb & 0xffffu) sb = (sb & 0xffff0000u) + 0x10000u;
-      float s = __uint_as_float(sb);
-      if (!(s >= 0x1p-126f)) s = 0.0f;
-      const float inv = s > 0.0f ? 1.0f / s : 0.0f;
-      // q_k = round-half-even of the exact (y_k - lo) * inv: one fused rounding against 2^23
-      uint32_t mq[G];
-#pragma unroll
-      for (int k = 0; k < G; ++k) mq[k] = __float_as_uint(__builtin_fmaf(v[k] - lo, inv, 0x1p23f));
-      if (a.payload) {
-        const int64_t tj = t0 + j;
-        store_codes_b<G>(b, mq, a.payload + a.off_codes + wg_off + meta_off[j]);
-        reinterpret_cast<uint16_t*>(a.payload + a.off_scale)[tj] = (uint16_t)(__float_as_uint(s) >> 16);
-        reinterpret_cast<float*>(a.payload + a.off_zero)[tj] = lo;
+      if (mine) {
+        quantize_tile<G, OUT>(a, v, t, b, code_off);
+        if constexpr (OUT != 0) {
+          if (!flag) lds_write_tile<G, TOut>(ys + lane * RO::kStride, v);
+          else lds_write_tile<G, float>(sl, v);
+        }
       }
       if constexpr (OUT != 0) {
-        // receiver side (Algorithm 1 line 5) from the codes held in registers
-#pragma unroll
-        for (int k = 0; k < G; ++k) v[k] = __builtin_fmaf(__uint_as_float(mq[k]) - 0x1p23f, s, lo);
-        if (flag) {
-          fwht<G>(v);
-#pragma unroll
-          for (int k = 0; k < G; ++k) v[k] = v[k] * (1.0f / G);
-        }
-        if constexpr (kSameRow) write_y_row<G, TOut>(xs + j * RO::kStride, v, flag, piv);
+        if (j_hi > j_lo) inverse(j_lo, j_hi);
       }
+      if (j_hi >= nf) break;
+      __syncthreads();
     }
 
     if constexpr (OUT != 0) {
-      if constexpr (!kSameRow) {
-        // wider output rows overlap other lanes' input rows: wait for every read
-        __syncthreads();
-        if (act) write_y_row<G, TOut>(xs + j * RO::kStride, v, flag, piv);
-      }
-      __syncthreads();
-      stage_out<G, TOut, NT>(xs, a.y + t0 * RO::kBytes, n);
+      prev_t0 = t0;
+      prev_n = n;
     }
-    __syncthreads();  // LDS is rewritten by the next group
+    __syncthreads();  // LDS rows are read by other lanes next
+  }
+  if constexpr (OUT != 0) {
+    if (prev_t0 >= 0) stage_out<G, TOut, NT>(ys, a.y + prev_t0 * RO::kBytes, prev_n);
   }
 }
 
@@ -365,7 +415,7 @@ static int cu_count() {
   static int cus = 0;
   if (!cus) {
     int dev = 0;
-    hipGetDevice(&dev);
+    (void)hipGetDevice(&dev);
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
   }
   return cus;
@@ -373,7 +423,7 @@ static int cu_count() {
 
 template <int G, typename TIn, int OUT, bool MIXED>
 static hipError_t launch_one(const EncArgs& a, hipStream_t st) {
-  constexpr int NT = tiles_per_wg<G, TIn>();
+  constexpr int NT = 64;
   static const int per_cu = wgs_per_cu(k_encode<G, TIn, OUT, MIXED>, NT);
   const int64_t ngroups = a.tiles > 0 ? (a.tiles + NT - 1) / NT : 1;
   const int64_t resident = (int64_t)per_cu * cu_count();
