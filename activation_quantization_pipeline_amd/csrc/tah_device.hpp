@@ -19,9 +19,9 @@
 
 namespace tah {
 
-// ε (Eq. 1), ς (Eq. 2), ϱ (Eq. 3) of TAH-Quant §3.2-3.3: small positive constants, 2^-40 each.
-constexpr float kEps = 0x1p-40f;
-constexpr float kSigma = 0x1p-40f;
+// ϱ of Eq. (3) (TAH-Quant §3.3): a small positive constant, 2^-40. The ε of
+// Eq. (1) and ς of Eq. (2) only keep zeros finite; the entropy below handles
+// zeros explicitly instead.
 constexpr float kRho = 0x1p-40f;
 
 typedef uint16_t bf16_t;
@@ -43,24 +43,118 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 
-// log2 for the entropy (TAH-Quant §3.2, Eq. 2 writes "log"; the base does not
-// change the ranking). u = m 2^e, m in [0.5, 1): f = 2m - 1 in [0, 1) exactly,
-// log2 u = (e - 1) + log2(1 + f), with log2(1 + f) replaced by the degree-5
-// minimax polynomial f (c1 + f (c2 + f (c3 + f (c4 + f c5)))) (|error| < 1.5e-5
-// on [0, 1]); the -1 is folded into the last Horner step. Valid for normal u > 0.
-__device__ __forceinline__ float log2s(float u) {
-  const float c1 = 0x1.7124acp+0f, c2 = -0x1.6b5948p-1f, c3 = 0x1.aba0f0p-2f, c4 = -0x1.91fd90p-3f,
-              c5 = 0x1.7c0becp-5f;
-  float m = __builtin_amdgcn_frexp_mantf(u);
-  int e = __builtin_amdgcn_frexp_expf(u);
-  float f = __builtin_fmaf(m, 2.0f, -1.0f);
-  float t = c5;
-  t = __builtin_fmaf(t, f, c4);
-  t = __builtin_fmaf(t, f, c3);
-  t = __builtin_fmaf(t, f, c2);
-  t = __builtin_fmaf(t, f, c1);
-  t = __builtin_fmaf(t, f, -1.0f);
-  return (float)e + t;
+// Tables of the entropy's log2, j = 0..127 (the top 7 stored mantissa bits):
+//   kLog2Tab[j]       = fp32(log2(1 + j/128) - 1)
+//   kLog2Tab[128 + j] = fp32((log2(1 + (j+1)/128) - log2(1 + j/128)) / 2^16)
+// each computed in double precision and rounded once to fp32.
+__device__ const float kLog2Tab[256] = {
+    -0x1p+0f, -0x1.fa406cp-1f, -0x1.f48c34p-1f, -0x1.eee32ep-1f,
+    -0x1.e9452cp-1f, -0x1.e3b206p-1f, -0x1.de298ep-1f, -0x1.d8abap-1f,
+    -0x1.d33812p-1f, -0x1.cdcebep-1f, -0x1.c86f7cp-1f, -0x1.c31a28p-1f,
+    -0x1.bdce9ep-1f, -0x1.b88cbap-1f, -0x1.b35458p-1f, -0x1.ae2558p-1f,
+    -0x1.a8ff98p-1f, -0x1.a3e2f4p-1f, -0x1.9ecf5p-1f, -0x1.99c48cp-1f,
+    -0x1.94c288p-1f, -0x1.8fc924p-1f, -0x1.8ad846p-1f, -0x1.85efdp-1f,
+    -0x1.810fa6p-1f, -0x1.7c37aap-1f, -0x1.7767c2p-1f, -0x1.729fd2p-1f,
+    -0x1.6ddfc2p-1f, -0x1.692778p-1f, -0x1.6476dap-1f, -0x1.5fcdcep-1f,
+    -0x1.5b2c3ep-1f, -0x1.56921p-1f, -0x1.51ff2ep-1f, -0x1.4d738p-1f,
+    -0x1.48eef2p-1f, -0x1.44716ap-1f, -0x1.3ffad4p-1f, -0x1.3b8b1cp-1f,
+    -0x1.37222cp-1f, -0x1.32bfeep-1f, -0x1.2e645p-1f, -0x1.2a0f3cp-1f,
+    -0x1.25c0ap-1f, -0x1.217868p-1f, -0x1.1d3682p-1f, -0x1.18fadcp-1f,
+    -0x1.14c56p-1f, -0x1.109602p-1f, -0x1.0c6caap-1f, -0x1.08494cp-1f,
+    -0x1.042bd4p-1f, -0x1.001434p-1f, -0x1.f804aep-2f, -0x1.efec62p-2f,
+    -0x1.e7df6p-2f, -0x1.dfdd8ap-2f, -0x1.d7e6cp-2f, -0x1.cffae6p-2f,
+    -0x1.c819dcp-2f, -0x1.c04386p-2f, -0x1.b877c6p-2f, -0x1.b0b68p-2f,
+    -0x1.a8ff98p-2f, -0x1.a152f2p-2f, -0x1.99b072p-2f, -0x1.9218p-2f,
+    -0x1.8a898p-2f, -0x1.8304dap-2f, -0x1.7b89fp-2f, -0x1.7418acp-2f,
+    -0x1.6cb0f6p-2f, -0x1.6552b4p-2f, -0x1.5dfddp-2f, -0x1.56b22ep-2f,
+    -0x1.4f6fbcp-2f, -0x1.48365ep-2f, -0x1.410602p-2f, -0x1.39de8ep-2f,
+    -0x1.32bfeep-2f, -0x1.2baa0cp-2f, -0x1.249cd2p-2f, -0x1.1d982cp-2f,
+    -0x1.169c06p-2f, -0x1.0fa848p-2f, -0x1.08bcep-2f, -0x1.01d9bcp-2f,
+    -0x1.f5fd8ap-3f, -0x1.e857d4p-3f, -0x1.dac22ep-3f, -0x1.cd3c72p-3f,
+    -0x1.bfc67ap-3f, -0x1.b26024p-3f, -0x1.a5094cp-3f, -0x1.97c1ccp-3f,
+    -0x1.8a898p-3f, -0x1.7d604ap-3f, -0x1.704604p-3f, -0x1.633a8cp-3f,
+    -0x1.563dc2p-3f, -0x1.494f86p-3f, -0x1.3c6fb6p-3f, -0x1.2f9e32p-3f,
+    -0x1.22dadcp-3f, -0x1.162594p-3f, -0x1.097e38p-3f, -0x1.f9c95ep-4f,
+    -0x1.e0b1aep-4f, -0x1.c7b528p-4f, -0x1.aed392p-4f, -0x1.960cbp-4f,
+    -0x1.7d604ap-4f, -0x1.64ce26p-4f, -0x1.4c561p-4f, -0x1.33f7cep-4f,
+    -0x1.1bb32ap-4f, -0x1.0387fp-4f, -0x1.d6ebd2p-5f, -0x1.a6f9c4p-5f,
+    -0x1.77394cp-5f, -0x1.47aa08p-5f, -0x1.184b8ep-5f, -0x1.d23afcp-6f,
+    -0x1.743ee8p-6f, -0x1.16a21ep-6f, -0x1.72c7bap-7f, -0x1.720d9cp-8f,
+    0x1.6fe50cp-23f, 0x1.6d0dc6p-23f, 0x1.6a41a4p-23f, 0x1.678068p-23f,
+    0x1.64c9dp-23f, 0x1.621da2p-23f, 0x1.5f7b9ep-23f, 0x1.5ce38ep-23f,
+    0x1.5a553ap-23f, 0x1.57d06ap-23f, 0x1.5554e8p-23f, 0x1.52e284p-23f,
+    0x1.50790ap-23f, 0x1.4e184cp-23f, 0x1.4bc018p-23f, 0x1.49704p-23f,
+    0x1.47289ap-23f, 0x1.44e8fcp-23f, 0x1.42b138p-23f, 0x1.408126p-23f,
+    0x1.3e58ap-23f, 0x1.3c377ep-23f, 0x1.3a1d9cp-23f, 0x1.380ad2p-23f,
+    0x1.35fefep-23f, 0x1.33f9fep-23f, 0x1.31fbbp-23f, 0x1.3003fp-23f,
+    0x1.2e12a2p-23f, 0x1.2c27a4p-23f, 0x1.2a42d8p-23f, 0x1.286422p-23f,
+    0x1.268b6p-23f, 0x1.24b87cp-23f, 0x1.22eb54p-23f, 0x1.2123d2p-23f,
+    0x1.1f61dap-23f, 0x1.1da552p-23f, 0x1.1bee2p-23f, 0x1.1a3c2cp-23f,
+    0x1.188f6p-23f, 0x1.16e7a2p-23f, 0x1.1544dep-23f, 0x1.13a6fcp-23f,
+    0x1.120de6p-23f, 0x1.107986p-23f, 0x1.0ee9cap-23f, 0x1.0d5e9cp-23f,
+    0x1.0bd7e8p-23f, 0x1.0a559cp-23f, 0x1.08d7a2p-23f, 0x1.075decp-23f,
+    0x1.05e864p-23f, 0x1.0476fap-23f, 0x1.03099cp-23f, 0x1.01a03ap-23f,
+    0x1.003ac2p-23f, 0x1.fdb24ap-24f, 0x1.faf6a6p-24f, 0x1.f8427ap-24f,
+    0x1.f595a4p-24f, 0x1.f2f008p-24f, 0x1.f0518ap-24f, 0x1.edba0ep-24f,
+    0x1.eb2976p-24f, 0x1.e89fa6p-24f, 0x1.e61c86p-24f, 0x1.e39ffap-24f,
+    0x1.e129e8p-24f, 0x1.deba38p-24f, 0x1.dc50dp-24f, 0x1.d9ed9ap-24f,
+    0x1.d7907cp-24f, 0x1.d5395ep-24f, 0x1.d2e82cp-24f, 0x1.d09cdp-24f,
+    0x1.ce573p-24f, 0x1.cc173cp-24f, 0x1.c9dcdap-24f, 0x1.c7a7f8p-24f,
+    0x1.c5788p-24f, 0x1.c34e6p-24f, 0x1.c12984p-24f, 0x1.bf09dap-24f,
+    0x1.bcef4cp-24f, 0x1.bad9cap-24f, 0x1.b8c942p-24f, 0x1.b6bda2p-24f,
+    0x1.b4b6d8p-24f, 0x1.b2b4d2p-24f, 0x1.b0b782p-24f, 0x1.aebed6p-24f,
+    0x1.accabep-24f, 0x1.aadb28p-24f, 0x1.a8f008p-24f, 0x1.a7094cp-24f,
+    0x1.a526e8p-24f, 0x1.a348cap-24f, 0x1.a16ee6p-24f, 0x1.9f992ap-24f,
+    0x1.9dc78cp-24f, 0x1.9bf9fep-24f, 0x1.9a307p-24f, 0x1.986ad6p-24f,
+    0x1.96a922p-24f, 0x1.94eb4ap-24f, 0x1.93313ep-24f, 0x1.917af4p-24f,
+    0x1.8fc85ep-24f, 0x1.8e197p-24f, 0x1.8c6e22p-24f, 0x1.8ac662p-24f,
+    0x1.89222ap-24f, 0x1.87816ep-24f, 0x1.85e42p-24f, 0x1.844a38p-24f,
+    0x1.82b3aap-24f, 0x1.81206cp-24f, 0x1.7f9074p-24f, 0x1.7e03b6p-24f,
+    0x1.7c7a2cp-24f, 0x1.7af3c8p-24f, 0x1.797082p-24f, 0x1.77f05p-24f,
+    0x1.76732ap-24f, 0x1.74f904p-24f, 0x1.7381d8p-24f, 0x1.720d9cp-24f,
+};
+
+// Copy kLog2Tab into LDS (every lane of a 64-lane workgroup takes 4 entries).
+__device__ __forceinline__ void load_log2_tab(float* lt) {
+  const float4 v = reinterpret_cast<const float4*>(kLog2Tab)[threadIdx.x & 63];
+  if (threadIdx.x < 64) reinterpret_cast<float4*>(lt)[threadIdx.x] = v;
+}
+
+// log2 of the entropy (TAH-Quant §3.2, Eq. 2 writes "log"; the base does not
+// change the ranking). x = m 2^E with m in [0.5, 1) (frexp; E = 0 for x = 0),
+// j = bits 16..22 of x, w = bits 0..15:
+//   log2(x) = fmaf((float)w, D[j], (float)E + T[j]),   lt = {T, D} in LDS.
+// log2_node is the same for x with w = 0 (every widened bf16 value, which
+// sits on a node of the table): the fma would add an exact zero to a sum that
+// is never -0, so it is left out, and the table offset j * 4 is one bit-field
+// extract of bits 14..22 (bits 14 and 15 are zero).
+__device__ __forceinline__ float log2_node(float x, const float* lt) {
+  const uint32_t off = __builtin_amdgcn_ubfe(__float_as_uint(x), 14u, 9u);
+  const float t = *reinterpret_cast<const float*>(reinterpret_cast<const uint8_t*>(lt) + off);
+  return (float)__builtin_amdgcn_frexp_expf(x) + t;
+}
+__device__ __forceinline__ float log2_full(float x, const float* lt) {
+  const uint32_t b = __float_as_uint(x);
+  const uint32_t j = (b >> 16) & 127u;
+  const float base = (float)__builtin_amdgcn_frexp_expf(x) + lt[j];
+  return __builtin_fmaf((float)(b & 0xffffu), lt[128 + j], base);
+}
+
+// Tile entropy of Eq. (1)-(2) with the minus sign, written as
+//   H = log2 L - (1/L) sum_k |a_k| log2 |a_k|,   L = sum_k |a_k|
+// (equal to -sum p_k log2 p_k with p_k = |a_k| / L). fp32 order: S summed
+// left to right with fmaf from 0, then log2(L) - S / L; L = 0 gives 0.
+// NODE: the tile's values are widened bf16 (log2_node applies).
+template <int G, bool NODE>
+__device__ __forceinline__ float tile_entropy(const float (&v)[G], float l1, const float* lt) {
+  float S = 0.0f;
+#pragma unroll
+  for (int k = 0; k < G; ++k) {
+    const float lg = NODE ? log2_node(v[k], lt) : log2_full(fabsf(v[k]), lt);
+    S = __builtin_fmaf(fabsf(v[k]), lg, S);
+  }
+  asm volatile("" : "+v"(S));  // the sum is complete here, ahead of the L = 0 test
+  return l1 > 0.0f ? log2_full(l1, lt) - S / l1 : 0.0f;
 }
 
 // Unnormalized Sylvester Walsh-Hadamard transform in registers, v <- H_G v

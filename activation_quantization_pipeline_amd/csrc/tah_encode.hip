@@ -105,7 +105,12 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = 8 * c + 2 * i;
-        const uint32_t xl = u[i] << 16, xh = u[i] & 0xffff0000u;
+        // the widened values, made opaque to the compiler so that the entropy's
+        // table offset stays one bit-field extract of them (folded into u's
+        // bits it takes two instructions)
+        uint32_t xl, xh;
+        asm("v_lshlrev_b32 %0, 16, %1" : "=v"(xl) : "v"(u[i]));
+        asm("v_and_b32 %0, 0xffff0000, %1" : "=v"(xh) : "v"(u[i]));
         const uint32_t kl = (xl & 0x7fff0000u) | (uint32_t)(G - 1 - k);
         const uint32_t kh = (u[i] & 0x7fff0000u) | (uint32_t)(G - 2 - k);
         v[k] = __uint_as_float(xl);
@@ -216,6 +221,7 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
   __shared__ __attribute__((aligned(16))) uint8_t ys_own[kSameRow ? 16 : NT * RO::kStride];
   __shared__ __attribute__((aligned(16))) float ts[kCoop * kSlot];
   __shared__ uint32_t flist[NT];
+  __shared__ __attribute__((aligned(16))) float lt[256];  // log2 tables of the entropy
   uint8_t* ys = kSameRow ? xs : ys_own;
 
   const int lane = threadIdx.x;
@@ -226,6 +232,8 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
     for (int r = 0; r < a.pads.n; ++r)
       for (int i = lane; i < a.pads.len[r]; i += NT) a.payload[a.pads.off[r] + i] = 0;
   }
+
+  if constexpr (!MIXED) load_log2_tab(lt);  // read after the first barrier of the loop
 
   const int64_t ngroups = (a.tiles + NT - 1) / NT;
   int64_t g = blockIdx.x;
@@ -275,15 +283,7 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
       flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
       piv = d;
       if constexpr (!MIXED) {
-        // Eq. (1)-(2): p_k = |a_k| / (L1 + eps), H = -sum p_k log2(p_k + sigma)
-        const float r = 1.0f / (l1 + kEps);
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < G; ++k) {
-          const float p = fabsf(v[k]) * r;
-          acc = __builtin_fmaf(p, log2s(p + kSigma), acc);
-        }
-        a.H[t] = 0.0f - acc;
+        a.H[t] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);  // Eq. (1)-(2)
       } else {
         hi = (a.bitmap[t >> 5] >> (t & 31)) & 1u;
       }

@@ -50,6 +50,7 @@ __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsA
   constexpr int NT = stats_tiles_per_wg<G, TIn>();
   using RI = TileRow<G, TIn>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[NT * RI::kStride];
+  __shared__ __attribute__((aligned(16))) float lt[256];  // log2 tables of the entropy
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * NT;
   if (a.init) {
@@ -68,6 +69,7 @@ __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsA
   }
   const int n = (int)((a.tiles - t0) < NT ? (a.tiles - t0) : NT);
   if (n <= 0) return;
+  load_log2_tab(lt);
   stage_in<G, TIn, NT>(a.x + t0 * RI::kBytes, xs, n);
   __syncthreads();
   if (tid < n) {
@@ -76,14 +78,7 @@ __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsA
     float l1 = 0.0f;
 #pragma unroll
     for (int k = 0; k < G; ++k) l1 = l1 + fabsf(v[k]);
-    const float r = 1.0f / (l1 + kEps);
-    float acc = 0.0f;
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-      const float p = fabsf(v[k]) * r;
-      acc = __builtin_fmaf(p, log2s(p + kSigma), acc);
-    }
-    a.h[t0 + tid] = 0.0f - acc;
+    a.h[t0 + tid] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);  // Eq. (1)-(2)
   }
 }
 

@@ -28,9 +28,8 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* ε (Eq. 1), ς (Eq. 2) and ϱ (Eq. 3): "small positive constants". Reading: 2^-40 each. */
-static const float kEps = 0x1p-40f;
-static const float kSigma = 0x1p-40f;
+/* ϱ (Eq. 3): a "small positive constant". Reading: 2^-40. (The ε of Eq. 1 and
+ * the ς of Eq. 2 only guard zeros; see tahref_entropy.) */
 static const float kRho = 0x1p-40f;
 
 /* ------------------------------------------------------------------ */
@@ -186,27 +185,41 @@ static void write_header(uint8_t* P, const tahref_plan* pl, const tahref_params*
 
 /*
  * log2 used by the entropy of Eq. (2) (the page writes "log"; any base ranks
- * tiles the same way, and base 2 is cheap from the float exponent).
- * u = m * 2^e with m in [0.5, 1) (frexp); f = 2m - 1 in [0, 1) (exact);
- * log2(u) = (e - 1) + log2(1 + f), and log2(1 + f) is replaced by the
- * degree-5 polynomial f*(c1 + f*(c2 + f*(c3 + f*(c4 + f*c5)))), a minimax
- * fit on [0, 1] with absolute error below 1.5e-5. The "-1" is folded into the
- * last Horner step. Every step is one fp32 rounding (fmaf), so the result is
- * reproducible bit for bit. Domain: normal positive u (here u >= ς).
+ * tiles the same way). For finite u >= 0 with fp32 bits b:
+ *   E = the frexp exponent (u = m * 2^E, m in [0.5, 1); E = 0 for u = 0),
+ *   j = bits 16..22 of b (the top 7 stored mantissa bits), w = bits 0..15,
+ *   T[j] = fp32(log2(1 + j/128) - 1),
+ *   D[j] = fp32((log2(1 + (j+1)/128) - log2(1 + j/128)) / 2^16),
+ *   log2s(u) = fmaf((float)w, D[j], (float)E + T[j]).
+ * For u of the form (1 + j/128) * 2^e (every bf16 value) w = 0 and the result
+ * is log2(u) rounded twice (T, then the sum); otherwise the mantissa is
+ * interpolated linearly between the two neighbouring 7-bit points, with an
+ * error below 1.15e-5. T and D are computed here in double precision from
+ * the C library's log2 and rounded once to fp32. log2s(0) = -1 (it is only
+ * ever multiplied by 0).
  */
+static float g_T[128], g_D[128];
+static int g_tab_ready = 0;
+
+static void log2_tables(void) {
+  if (g_tab_ready) return;
+  for (int j = 0; j < 128; ++j) {
+    const double a = log2(1.0 + j / 128.0), b = log2(1.0 + (j + 1) / 128.0);
+    g_T[j] = (float)(a - 1.0);
+    g_D[j] = (float)((b - a) / 65536.0);
+  }
+  g_tab_ready = 1;
+}
+
 float tahref_log2s(float u) {
-  static const float c1 = 0x1.7124acp+0f, c2 = -0x1.6b5948p-1f, c3 = 0x1.aba0f0p-2f,
-                     c4 = -0x1.91fd90p-3f, c5 = 0x1.7c0becp-5f;
+  log2_tables();
+  uint32_t b;
+  memcpy(&b, &u, 4);
   int e;
-  float m = frexpf(u, &e);
-  float f = fmaf(m, 2.0f, -1.0f);
-  float t = c5;
-  t = fmaf(t, f, c4);
-  t = fmaf(t, f, c3);
-  t = fmaf(t, f, c2);
-  t = fmaf(t, f, c1);
-  t = fmaf(t, f, -1.0f);
-  return (float)e + t;
+  (void)frexpf(u, &e);
+  const int j = (int)((b >> 16) & 127u);
+  const float w = (float)(b & 0xffffu);
+  return fmaf(w, g_D[j], (float)e + g_T[j]);
 }
 
 /*
@@ -229,24 +242,28 @@ void tahref_fwht(float* v, int G) {
 
 /*
  * Entropy of one allocation tile, Eq. (1)-(2):
- *   p_k = |a_k| / (||a||_1 + ε),   H = -sum_k p_k log2(p_k + ς).
+ *   p_k = |a_k| / ||a||_1,   H = -sum_k p_k log2 p_k.
  * Reading: Eq. (2) as printed has no minus sign, but the text says H is high
  * for evenly spread energy and low for a sharp outlier, which is Shannon's
- * entropy; the minus sign is restored.
- * fp32 order: L1 summed left to right; r = 1/(L1 + ε) once; p_k = |a_k| * r;
- * the sum of p_k * log2s(p_k + ς) accumulated left to right with fmaf;
- * H = 0 - acc (so an exact zero is +0).
+ * entropy; the minus sign is restored. The ε of Eq. (1) and the ς inside the
+ * log only keep zeros finite; here they are taken as 0, a zero |a_k| adds
+ * nothing (0 log 0 = 0) and an all-zero tile has H = 0.
+ * Since sum_k p_k = 1, H = log2 L - (1/L) sum_k |a_k| log2 |a_k| with
+ * L = ||a||_1, and that is the form evaluated (one log per element, of the
+ * input value itself):
+ *   L = sum |a_k| left to right; S = sum fmaf(|a_k|, log2s(|a_k|), S) left to
+ *   right from 0; H = log2s(L) - S / L (L > 0), H = 0 (L = 0).
  */
 float tahref_entropy(const float* alpha, int G) {
   float l1 = 0.0f;
   for (int k = 0; k < G; ++k) l1 = l1 + fabsf(alpha[k]);
-  float r = 1.0f / (l1 + kEps);
-  float acc = 0.0f;
+  float S = 0.0f;
   for (int k = 0; k < G; ++k) {
-    float p = fabsf(alpha[k]) * r;
-    acc = fmaf(p, tahref_log2s(p + kSigma), acc);
+    const float a = fabsf(alpha[k]);
+    S = fmaf(a, tahref_log2s(a), S);
   }
-  return 0.0f - acc;
+  if (!(l1 > 0.0f)) return 0.0f;
+  return tahref_log2s(l1) - S / l1;
 }
 
 /*

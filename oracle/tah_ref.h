@@ -9,8 +9,8 @@
  * It exists so that tests, the smoke check and the benchmark's CPU baseline can
  * check the GPU library against it. Nothing in the product path may include,
  * link or call this code, and it shares no code, header or table with the GPU
- * library: the payload format, the fp32 operation order and the log2
- * polynomial are restated here independently from the written specification.
+ * library: the payload format, the fp32 operation order and the log2 tables
+ * are restated here independently from the written specification.
  *
  * Precision: every quantity that decides an integer (entropy ranking, outlier
  * flag, pivot, codes) is computed in IEEE fp32 in a fixed, documented

@@ -12,7 +12,8 @@ import pytest
 import activation_quantization_pipeline_amd as tah
 import synth
 
-HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "tah.h")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tah.h")
 
 
 def declared_functions():
@@ -97,3 +98,21 @@ def test_payload_size_is_shape_only(ref):
     assert n1 == tah.payload_bytes(4096, 2048, p)
     # no tokens: every section is empty, only the 256-byte header section is left
     assert tah.payload_bytes(0, 2048, p) == ref.plan(0, 2048, p)["total"] == 256
+
+
+def test_device_log2_tables_match_their_definition():
+    """The GPU library's log2 tables of the entropy (literal constants in its
+    device header) against their definition, recomputed here in double
+    precision: T[j] = fp32(log2(1 + j/128) - 1), D[j] = fp32((log2(1 + (j+1)/128)
+    - log2(1 + j/128)) / 2^16)."""
+    import numpy as np
+
+    src = open(os.path.join(ROOT, "activation_quantization_pipeline_amd", "csrc", "tah_device.hpp")).read()
+    body = src[src.index("kLog2Tab[256] = {"):]
+    body = body[body.index("{") + 1:body.index("};")]
+    vals = [float.fromhex(x[:-1]) for x in re.findall(r"-?0x1[0-9a-f.]*p[+-]\d+f", body)]
+    assert len(vals) == 256
+    for j in range(128):
+        a, b = math.log2(1 + j / 128), math.log2(1 + (j + 1) / 128)
+        assert np.float32(vals[j]) == np.float32(a - 1.0), j
+        assert np.float32(vals[128 + j]) == np.float32((b - a) / 65536.0), j
