@@ -89,12 +89,10 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   int64_t w = 0;
   o->ws_status = w;
   w += 256;
-  o->ws_counter = w;
-  w += 256;
-  o->ws_state = w;
-  w = align256(w + (int64_t)sizeof(SampleState) * (mixed ? o->nsamples : 0));
-  o->ws_hist = w;
-  w = align256(w + 4 * kBins * (mixed ? o->nsamples : 0));
+  o->ws_state = w;  // two selection states per sample (ping-pong across passes)
+  w = align256(w + 2 * (int64_t)sizeof(SampleState) * (mixed ? o->nsamples : 0));
+  o->ws_hist = w;  // three rotating histograms per sample
+  w = align256(w + 3 * 4 * kBins * (mixed ? o->nsamples : 0));
   o->ws_H = w;
   w = align256(w + 4 * o->tiles);
   o->ws_blockcnt = w;

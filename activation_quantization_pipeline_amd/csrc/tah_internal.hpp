@@ -33,7 +33,7 @@ struct Plan {
   // payload layout
   int64_t off_table, off_bitmap, off_side, off_scale, off_zero, off_codes, code_bytes, total;
   // workspace layout
-  int64_t ws_status, ws_state, ws_counter, ws_hist, ws_H, ws_blockcnt, ws_table, ws_bitmap, ws_total;
+  int64_t ws_status, ws_state, ws_hist, ws_H, ws_blockcnt, ws_table, ws_bitmap, ws_total;
   int32_t npasses;
   SelectPass passes[kMaxPasses];
 };

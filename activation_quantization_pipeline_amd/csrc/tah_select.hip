@@ -6,12 +6,21 @@
 //   k_stats  - one lane per tile computes the entropy of Eq. (1)-(2) from the
 //              LDS-staged tile and writes it to the workspace; it also resets
 //              the selection state and histograms;
-//   k_hist   - one pass per digit: a 2048-bin LDS histogram of the current
-//              digit over the keys that still match the prefix, merged into
-//              the sample's global histogram; the last workgroup to finish
-//              (atomic ticket) picks the digit that holds rank r. Three passes
-//              cover the 32-bit order-preserving entropy key; then passes over
-//              the tile index resolve ties (lower index first);
+//   k_hist   - one launch per digit pass. Each workgroup first applies the
+//              previous pass (one wavefront scans that pass's histogram of the
+//              sample in order and finds the digit that holds rank r), then
+//              builds a 2048-bin LDS histogram of the current digit over the
+//              keys that still match the prefix (lanes of a wavefront that
+//              share a digit add once: entropy keys cluster) and adds it into
+//              the sample's global histogram. Three passes cover the 32-bit
+//              order-preserving entropy key; then passes over the tile index
+//              resolve ties (lower index first). Histograms rotate over three
+//              buffers (read the previous, add to the current, clear the next)
+//              and states over two, so kernel boundaries are the only
+//              synchronisation: a last-workgroup ticket would need a
+//              device-scope release per workgroup, which on this multi-die part
+//              writes back the L2;
+//   k_pick   - applies the last pass: the final threshold state per sample;
 //   k_mark   - one bit per tile: key above the threshold, or equal to it with
 //              an index up to the last selected tie; per-64-tile counts;
 //   k_table  - exclusive scan of those counts: b_hi tiles before each run of
@@ -33,10 +42,8 @@ __device__ __forceinline__ uint32_t orderable(float f) {
 struct StatsArgs {
   const uint8_t* x;
   float* h;
-  SampleState* st;
   uint32_t* hist;
-  uint32_t* counter;
-  int64_t tiles, nsamples, k, hist_words;
+  int64_t tiles, hist_words;
   int32_t init;
 };
 
@@ -53,19 +60,9 @@ __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsA
   __shared__ __attribute__((aligned(16))) float lt[256];  // log2 tables of the entropy
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * NT;
-  if (a.init) {
+  if (a.init) {  // the first selection pass's histograms start at zero
     const int64_t gid = (int64_t)blockIdx.x * NT + tid, gsz = (int64_t)gridDim.x * NT;
     for (int64_t i = gid; i < a.hist_words; i += gsz) a.hist[i] = 0u;
-    for (int64_t s = gid; s < a.nsamples; s += gsz) {
-      SampleState z;
-      z.key = 0u;
-      z.upos = 0u;
-      z.r = a.k;
-      z.tie_all = 0;
-      z.pad = 0;
-      a.st[s] = z;
-    }
-    if (gid == 0) *a.counter = 0u;
   }
   const int n = (int)((a.tiles - t0) < NT ? (a.tiles - t0) : NT);
   if (n <= 0) return;
@@ -95,12 +92,8 @@ hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, b
   StatsArgs a;
   a.x = static_cast<const uint8_t*>(x);
   a.h = h_out;
-  a.st = reinterpret_cast<SampleState*>(w + pl.ws_state);
   a.hist = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
-  a.counter = reinterpret_cast<uint32_t*>(w + pl.ws_counter);
   a.tiles = pl.tiles;
-  a.nsamples = pl.nsamples;
-  a.k = pl.k;
   a.hist_words = pl.k > 0 ? pl.nsamples * kBins : 0;
   a.init = init_select ? 1 : 0;
   const bool bf = pl.x_dtype == TAH_DTYPE_BF16;
@@ -115,34 +108,35 @@ hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, b
 // ------------------------------------------------------------------ hist ----
 struct HistArgs {
   const float* H;
-  SampleState* st;
-  uint32_t* hist;
-  uint32_t* counter;
-  int64_t N, nsamples, chunks_per_sample;
-  uint32_t total_wg;
-  SelectPass pass;
+  const SampleState* st_prev;  // state before the previous pass (unused on pass 0)
+  SampleState* st_cur;         // state before this pass, written by each sample's first block
+  const uint32_t* hist_prev;   // previous pass's histograms
+  uint32_t* hist_cur;          // this pass's histograms (zero on entry)
+  uint32_t* hist_clear;        // the next pass's histograms, cleared here
+  int64_t N, nsamples, chunks_per_sample, k;
+  SelectPass pass, prev;
+  int32_t has_prev;
 };
 
-constexpr int kHistThreads = 256;
-constexpr int kHistPerThread = 4;
+// Large workgroups: fewer of them add into the same global bins.
+constexpr int kHistThreads = 1024;
+constexpr int kHistPerThread = 16;
 constexpr int kHistChunk = kHistThreads * kHistPerThread;
 
-// The wave scans one sample's histogram in order (descending digits for the
-// entropy key, ascending for the tile index) and keeps the digit where the
-// running count reaches r; the histogram is cleared for the next pass.
-__device__ void finalize_sample(const HistArgs& a, int64_t s) {
+// Apply one pass to a sample's state: one wavefront scans the pass's histogram
+// in order (descending digits for the entropy key, ascending for the tile
+// index) and finds the digit where the running count reaches r.
+__device__ __forceinline__ SampleState apply_pass(SampleState S, const uint32_t* h, const SelectPass& ps) {
   const int lane = threadIdx.x & 63;
-  uint32_t* h = a.hist + s * kBins;
-  SampleState S = a.st[s];
-  const bool skip = a.pass.kind == 1 && S.tie_all;
+  if (ps.kind == 1 && S.tie_all) return S;
   constexpr int PER = kBins / 64;
   uint32_t c[PER];
   uint32_t sum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int ord = lane * PER + i;
-    const int bin = a.pass.kind == 0 ? (kBins - 1 - ord) : ord;
-    c[i] = __hip_atomic_load(&h[bin], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int bin = ps.kind == 0 ? (kBins - 1 - ord) : ord;
+    c[i] = h[bin];
     sum += c[i];
   }
   // inclusive prefix of the per-lane sums over the wave
@@ -153,11 +147,15 @@ __device__ void finalize_sample(const HistArgs& a, int64_t s) {
     if (lane >= off) incl += o;
   }
   const uint64_t excl = incl - sum;
-  const bool here = !skip && (int64_t)excl < S.r && S.r <= (int64_t)incl;
+  const bool here = (int64_t)excl < S.r && S.r <= (int64_t)incl;
+  const uint64_t hm = ballot(here);
+  if (hm == 0) return S;  // rank beyond the histogram: cannot happen for 1 <= r <= count
+  const int src = __ffsll((unsigned long long)hm) - 1;
+  uint32_t digit = 0, cnt = 0;
+  int64_t before = 0;
   if (here) {
-    int64_t before = (int64_t)excl;
+    before = (int64_t)excl;
     int ord = lane * PER;
-    uint32_t cnt = 0;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
       if (before + (int64_t)c[i] >= S.r) {
@@ -167,64 +165,106 @@ __device__ void finalize_sample(const HistArgs& a, int64_t s) {
       }
       before += c[i];
     }
-    const uint32_t digit = (uint32_t)(a.pass.kind == 0 ? (kBins - 1 - ord) : ord);
-    S.r -= before;
-    if (a.pass.kind == 0) {
-      S.key |= digit << a.pass.shift;
-      if (a.pass.last_h) {
-        S.tie_all = (S.r == (int64_t)cnt) ? 1 : 0;
-        S.upos = S.tie_all ? 0xffffffffu : 0u;
-      }
-    } else {
-      S.upos |= digit << a.pass.shift;
-    }
-    a.st[s] = S;
+    digit = (uint32_t)(ps.kind == 0 ? (kBins - 1 - ord) : ord);
   }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) h[lane * PER + i] = 0u;
+  digit = (uint32_t)__shfl((int)digit, src, 64);
+  cnt = (uint32_t)__shfl((int)cnt, src, 64);
+  before = (int64_t)__shfl((long long)before, src, 64);
+  S.r -= before;
+  if (ps.kind == 0) {
+    S.key |= digit << ps.shift;
+    if (ps.last_h) {
+      S.tie_all = (S.r == (int64_t)cnt) ? 1 : 0;
+      S.upos = S.tie_all ? 0xffffffffu : 0u;
+    }
+  } else {
+    S.upos |= digit << ps.shift;
+  }
+  return S;
 }
 
 __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
   __shared__ uint32_t lh[kBins];
-  __shared__ int last;
-  const int tid = threadIdx.x;
-  for (int i = tid; i < kBins; i += kHistThreads) lh[i] = 0u;
-  __syncthreads();
+  __shared__ SampleState ss;
+  const int tid = threadIdx.x, lane = tid & 63;
   const int64_t s = blockIdx.x / a.chunks_per_sample;
-  const int64_t u0 = (blockIdx.x % a.chunks_per_sample) * kHistChunk;
-  const SampleState S = a.st[s];
-  const int hs = a.pass.shift + a.pass.width;  // bits above the current digit
-  const uint32_t dmask = (1u << a.pass.width) - 1u;
-#pragma unroll
-  for (int i = 0; i < kHistPerThread; ++i) {
-    const int64_t u = u0 + i * kHistThreads + tid;
-    if (u < a.N) {
-      const uint32_t key = orderable(a.H[s * a.N + u]);
-      bool match;
-      uint32_t digit;
-      if (a.pass.kind == 0) {
-        match = hs >= 32 || (key >> hs) == (S.key >> hs);
-        digit = (key >> a.pass.shift) & dmask;
-      } else {
-        const uint32_t uu = (uint32_t)u;
-        match = !S.tie_all && key == S.key && (hs >= 32 || (uu >> hs) == (S.upos >> hs));
-        digit = (uu >> a.pass.shift) & dmask;
-      }
-      if (match) atomicAdd(&lh[digit], 1u);
+  const int64_t c = blockIdx.x % a.chunks_per_sample;
+  const int64_t u0 = c * kHistChunk;
+  // the next pass's histogram of this sample, cleared in slices by the sample's blocks
+  {
+    const int64_t per = (kBins + a.chunks_per_sample - 1) / a.chunks_per_sample;
+    const int64_t b0 = c * per, b1 = b0 + per < kBins ? b0 + per : kBins;
+    for (int64_t i = b0 + tid; i < b1; i += kHistThreads) a.hist_clear[s * kBins + i] = 0u;
+  }
+  for (int i = tid; i < kBins; i += kHistThreads) lh[i] = 0u;
+  if (tid < 64) {
+    SampleState S;
+    if (a.has_prev) {
+      S = apply_pass(a.st_prev[s], a.hist_prev + s * kBins, a.prev);
+    } else {
+      S.key = 0u;
+      S.upos = 0u;
+      S.r = a.k;
+      S.tie_all = 0;
+      S.pad = 0;
+    }
+    if (tid == 0) {
+      ss = S;
+      if (c == 0) a.st_cur[s] = S;
     }
   }
   __syncthreads();
+  const SampleState S = ss;
+  if (a.pass.kind == 1 && S.tie_all) return;  // no tie to resolve in this sample
+  const int hs = a.pass.shift + a.pass.width;  // bits above the current digit
+  const uint32_t dmask = (1u << a.pass.width) - 1u;
+  float hv[kHistPerThread];  // all loads in flight before the first use
+#pragma unroll
+  for (int i = 0; i < kHistPerThread; ++i) {
+    const int64_t u = u0 + i * kHistThreads + tid;
+    hv[i] = u < a.N ? a.H[s * a.N + u] : 0.0f;
+  }
+#pragma unroll
+  for (int i = 0; i < kHistPerThread; ++i) {
+    const int64_t u = u0 + i * kHistThreads + tid;
+    bool want = false;
+    uint32_t digit = 0;
+    if (u < a.N) {
+      const uint32_t key = orderable(hv[i]);
+      if (a.pass.kind == 0) {
+        want = hs >= 32 || (key >> hs) == (S.key >> hs);
+        digit = (key >> a.pass.shift) & dmask;
+      } else {
+        const uint32_t uu = (uint32_t)u;
+        want = key == S.key && (hs >= 32 || (uu >> hs) == (S.upos >> hs));
+        digit = (uu >> a.pass.shift) & dmask;
+      }
+    }
+    // lanes with the same digit as the first remaining lane add together (twice),
+    // the rest one by one
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+      const uint64_t wm = ballot(want);
+      if (wm == 0) break;
+      const int leader = __ffsll((unsigned long long)wm) - 1;
+      const uint32_t d0 = (uint32_t)__shfl((int)digit, leader, 64);
+      const bool same = want && digit == d0;
+      const uint64_t sm = ballot(same);
+      if (lane == leader) atomicAdd(&lh[d0], (uint32_t)__popcll(sm));
+      want = want && !same;
+    }
+    if (want) atomicAdd(&lh[digit], 1u);
+  }
+  __syncthreads();
   for (int i = tid; i < kBins; i += kHistThreads)
-    if (lh[i]) atomicAdd(&a.hist[s * kBins + i], lh[i]);
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) last = (atomicAdd(a.counter, 1u) == a.total_wg - 1u) ? 1 : 0;
-  __syncthreads();
-  if (!last) return;
-  __threadfence();
-  for (int64_t s2 = tid >> 6; s2 < a.nsamples; s2 += kHistThreads / 64) finalize_sample(a, s2);
-  __syncthreads();
-  if (tid == 0) *a.counter = 0u;
+    if (lh[i]) atomicAdd(&a.hist_cur[s * kBins + i], lh[i]);
+}
+
+// One wavefront per sample: the state after the last pass.
+__global__ __launch_bounds__(64) void k_pick(HistArgs a) {
+  const int64_t s = blockIdx.x;
+  const SampleState S = apply_pass(a.st_prev[s], a.hist_prev + s * kBins, a.prev);
+  if (threadIdx.x == 0) a.st_cur[s] = S;
 }
 
 // ------------------------------------------------------------------ mark ----
@@ -258,17 +298,36 @@ __global__ __launch_bounds__(256) void k_mark(MarkArgs a) {
 
 // ------------------------------------------------------------------ table ----
 constexpr int kScanThreads = 1024;
+constexpr int kScanPer = 8;  // counts per thread and step
+constexpr int kScanStep = kScanThreads * kScanPer;
 
+// Exclusive scan of the per-64-tile counts. Global memory is read and written
+// coalesced (through an LDS copy of the step); each thread scans kScanPer
+// consecutive counts, then the threads' totals are scanned across the block.
 __global__ __launch_bounds__(kScanThreads) void k_table(const uint32_t* cnt, uint32_t* table, int64_t nblocks) {
+  __shared__ uint32_t buf[kScanStep];
   __shared__ uint32_t wsum[kScanThreads / 64];
   __shared__ uint32_t carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) carry_s = 0u;
-  __syncthreads();
-  for (int64_t base = 0; base < nblocks; base += kScanThreads) {
-    const int64_t i = base + tid;
-    const uint32_t v = i < nblocks ? cnt[i] : 0u;
-    uint32_t incl = v;
+  for (int64_t base = 0; base < nblocks; base += kScanStep) {
+    uint32_t ld[kScanPer];
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int64_t i = base + j * kScanThreads + tid;
+      ld[j] = i < nblocks ? cnt[i] : 0u;
+    }
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) buf[j * kScanThreads + tid] = ld[j];
+    __syncthreads();
+    uint32_t v[kScanPer];
+    uint32_t tot = 0;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      v[j] = buf[tid * kScanPer + j];
+      tot += v[j];
+    }
+    uint32_t incl = tot;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const uint32_t o = __shfl_up(incl, off, 64);
@@ -278,9 +337,19 @@ __global__ __launch_bounds__(kScanThreads) void k_table(const uint32_t* cnt, uin
     __syncthreads();
     uint32_t before = carry_s;
     for (int w = 0; w < wave; ++w) before += wsum[w];
-    if (i < nblocks) table[i] = before + incl - v;
+    uint32_t run = before + incl - tot;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      buf[tid * kScanPer + j] = run;
+      run += v[j];
+    }
     __syncthreads();
-    if (tid == kScanThreads - 1) carry_s = before + incl;
+    if (tid == kScanThreads - 1) carry_s = run;
+#pragma unroll
+    for (int j = 0; j < kScanPer; ++j) {
+      const int64_t i = base + j * kScanThreads + tid;
+      if (i < nblocks) table[i] = buf[j * kScanThreads + tid];
+    }
     __syncthreads();
   }
 }
@@ -288,32 +357,49 @@ __global__ __launch_bounds__(kScanThreads) void k_table(const uint32_t* cnt, uin
 hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st) {
   uint8_t* w = static_cast<uint8_t*>(ws);
   uint8_t* P = static_cast<uint8_t*>(payload);
+  SampleState* states = reinterpret_cast<SampleState*>(w + pl.ws_state);
+  uint32_t* hists = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
+  const int64_t hsz = pl.nsamples * kBins;
   HistArgs h;
   h.H = reinterpret_cast<const float*>(w + pl.ws_H);
-  h.st = reinterpret_cast<SampleState*>(w + pl.ws_state);
-  h.hist = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
-  h.counter = reinterpret_cast<uint32_t*>(w + pl.ws_counter);
   h.N = pl.N;
   h.nsamples = pl.nsamples;
+  h.k = pl.k;
   h.chunks_per_sample = (pl.N + kHistChunk - 1) / kHistChunk;
   const int64_t nwg = h.chunks_per_sample * pl.nsamples;
-  h.total_wg = (uint32_t)nwg;
+  // pass p: state p in states[p % 2], histogram p in hists[p % 3] (zeroed by k_stats for p = 0)
   for (int p = 0; p < pl.npasses; ++p) {
     h.pass = pl.passes[p];
+    h.has_prev = p > 0;
+    h.prev = p > 0 ? pl.passes[p - 1] : pl.passes[p];
+    h.st_prev = states + ((p + 1) % 2) * pl.nsamples;
+    h.st_cur = states + (p % 2) * pl.nsamples;
+    h.hist_prev = hists + ((p + 2) % 3) * hsz;
+    h.hist_cur = hists + (p % 3) * hsz;
+    h.hist_clear = hists + ((p + 1) % 3) * hsz;
     hipLaunchKernelGGL(k_hist, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // the final state (after the last pass) goes to states[npasses % 2]
+  const int p = pl.npasses;
+  h.prev = pl.passes[p - 1];
+  h.st_prev = states + ((p + 1) % 2) * pl.nsamples;
+  h.st_cur = states + (p % 2) * pl.nsamples;
+  h.hist_prev = hists + ((p + 2) % 3) * hsz;
+  hipLaunchKernelGGL(k_pick, dim3((unsigned)pl.nsamples), dim3(64), 0, st, h);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   MarkArgs m;
   m.H = h.H;
-  m.st = h.st;
+  m.st = h.st_cur;
   m.bitmap = reinterpret_cast<uint32_t*>(P ? P + pl.off_bitmap : w + pl.ws_bitmap);
   m.blockcnt = reinterpret_cast<uint32_t*>(w + pl.ws_blockcnt);
   m.tiles = pl.tiles;
   m.N = pl.N;
   m.nblocks = pl.nblocks;
   hipLaunchKernelGGL(k_mark, dim3((unsigned)((pl.tiles + 255) / 256)), dim3(256), 0, st, m);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
   uint32_t* table = reinterpret_cast<uint32_t*>(P ? P + pl.off_table : w + pl.ws_table);
   hipLaunchKernelGGL(k_table, dim3(1), dim3(kScanThreads), 0, st, (const uint32_t*)m.blockcnt, table, pl.nblocks);
