@@ -1,15 +1,20 @@
 // Decode kernel of the TAH-Quant codec for gfx950 (Algorithm 1, line 5: the
-// receiving stage dequantizes). One workgroup rebuilds NT consecutive tiles:
-//  - the payload header is checked against the expected one (shape, params,
-//    section offsets); on a mismatch the status word is set and nothing is written;
-//  - phase A, lane i: side byte (flag, pivot), width bit, scale, zero-point and
-//    the code-block offset of tile i (block table + popcount of the width map);
-//  - tiles are regrouped by (flag, width) so that whole wavefronts take the
-//    same branch;
-//  - phase B: each lane loads its code block, unpacks, dequantizes
-//    (fmaf(q, s, lo)), applies H^T / G and undoes the pivot swap on flagged
-//    tiles (§3.3), and writes the tile to LDS;
-//  - the tiles leave LDS with 16-byte coalesced stores.
+// receiving stage dequantizes). A workgroup is one wavefront and is
+// persistent: group g of 64 consecutive tiles (one per lane) goes to
+// workgroup g mod gridDim.x.
+//  - the payload header is checked once against the expected one (shape,
+//    params, section offsets); on a mismatch the status word is set and
+//    nothing is written;
+//  - a software pipeline hides the dependent loads: a group's metadata (side
+//    byte, scale, zero-point, width-map words, block-table entry) is loaded
+//    two groups ahead; its code region (contiguous in the payload, located by
+//    the block table and the width map) one group ahead, with 16-byte
+//    coalesced loads into registers;
+//  - processing: the region goes to LDS, each lane reads its code block,
+//    unpacks and dequantizes (fmaf(q, s, lo)); flagged tiles get H^T / G and
+//    the swap undone (§3.3) by 16-lane groups through fp32 LDS slots, as in
+//    the encoder; rows are written to LDS and leave it with 16-byte coalesced
+//    stores at the top of the next iteration.
 #include <type_traits>
 
 #include "tah_device.hpp"
@@ -27,25 +32,13 @@ struct DecArgs {
   Header expect;
 };
 
-template <int G, typename TOut>
-constexpr int dec_tiles_per_wg() {
-  return TileRow<G, TOut>::kBytes <= 128 ? 256 : (TileRow<G, TOut>::kBytes <= 256 ? 128 : 64);
-}
-
+// The G codes of width B at src (LDS, 4-byte aligned; 8-byte aligned for
+// G >= 64), dequantized: v_k = fmaf(q_k, s, lo).
 template <int G, int B>
 __device__ __forceinline__ void load_dequant(const uint8_t* src, float s, float lo, float (&v)[G]) {
   constexpr int W = G * B / 32;
   uint32_t w[W];
-  if constexpr (G >= 128) {
-#pragma unroll
-    for (int i = 0; i < W / 4; ++i) {
-      const uint4 q = reinterpret_cast<const uint4*>(src)[i];
-      w[4 * i] = q.x;
-      w[4 * i + 1] = q.y;
-      w[4 * i + 2] = q.z;
-      w[4 * i + 3] = q.w;
-    }
-  } else if constexpr (G >= 64) {
+  if constexpr (G >= 64) {
 #pragma unroll
     for (int i = 0; i < W / 2; ++i) {
       const uint2 q = reinterpret_cast<const uint2*>(src)[i];
@@ -74,132 +67,217 @@ __device__ __forceinline__ void load_dequant_b(int b, const uint8_t* src, float 
   }
 }
 
-template <int G, typename TOut>
-__global__ __launch_bounds__((dec_tiles_per_wg<G, TOut>())) void k_decode(DecArgs a) {
-  constexpr int NT = dec_tiles_per_wg<G, TOut>();
-  constexpr int NW = NT / 64;
-  using RO = TileRow<G, TOut>;
-  __shared__ __attribute__((aligned(16))) uint8_t ys[NT * RO::kStride];
-  __shared__ uint32_t meta_off[NT];
-  __shared__ uint32_t meta_scale[NT];
-  __shared__ float meta_lo[NT];
-  __shared__ uint8_t meta_side[NT];
-  __shared__ uint8_t meta_hi[NT];
-  __shared__ uint16_t perm[NT];
-  __shared__ int cnt[NW][4];
-  __shared__ int bad;
+// A group's metadata: per lane (side byte, bf16 scale, zero-point) and per
+// group (block-table entry, width-map words).
+struct DecMeta {
+  uint32_t side, scale, tab, bm0, bm1;
+  float zero;
+};
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (tid < 64) {
+template <int NT>
+__device__ __forceinline__ void load_meta(const DecArgs& a, int64_t g, DecMeta& m) {
+  const int64_t t0 = g * NT;
+  const int64_t t = t0 + threadIdx.x;
+  const int64_t tc = t < a.tiles ? t : a.tiles - 1;  // inactive lanes read a valid tile
+  m.side = a.payload[a.off_side + tc];
+  m.scale = reinterpret_cast<const uint16_t*>(a.payload + a.off_scale)[tc];
+  m.zero = reinterpret_cast<const float*>(a.payload + a.off_zero)[tc];
+  const int64_t blk = t0 >> 6;
+  m.tab = reinterpret_cast<const uint32_t*>(a.payload + a.off_table)[blk];
+  m.bm0 = reinterpret_cast<const uint32_t*>(a.payload + a.off_bitmap)[2 * blk];
+  m.bm1 = reinterpret_cast<const uint32_t*>(a.payload + a.off_bitmap)[2 * blk + 1];
+}
+
+// The code region of a group: first byte and length (the group's blocks are
+// contiguous: b_lo blocks and b_hi blocks in tile order).
+template <int NT>
+__device__ __forceinline__ void region_of(const DecArgs& a, int64_t g, const DecMeta& m, int64_t& rs, int& rlen) {
+  const int64_t t0 = g * NT;
+  const int n = (int)((a.tiles - t0) < NT ? (a.tiles - t0) : NT);
+  const uint64_t bm = ((uint64_t)m.bm1 << 32) | m.bm0;
+  const uint64_t valid = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+  rs = a.off_codes + t0 * a.sz_lo + (int64_t)m.tab * (a.sz_hi - a.sz_lo);
+  rlen = n * a.sz_lo + __popcll(bm & valid) * (a.sz_hi - a.sz_lo);
+}
+
+// Region bytes of a group go through registers in 16-byte chunks: the region
+// holds at most NT * G bytes (8-bit codes), plus one chunk of misalignment.
+// (A native 4 x u32 vector, not the uint4 struct: struct copies become
+// memcpy and keep the array in scratch memory.)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int G, int NT>
+struct RegionRegs {
+  static constexpr int kChunks = (NT * G + 16 + 16 * NT - 1) / (16 * NT);
+  u32x4 c[kChunks];
+};
+
+template <int G, int NT>
+__device__ __forceinline__ void load_region(const DecArgs& a, int64_t rs, int rlen, RegionRegs<G, NT>& r) {
+  const int64_t base = rs & ~(int64_t)15;
+  const int nchunks = (int)((rs - base + rlen + 15) >> 4);
+  const int64_t last = (a.len >> 4) - 1;  // the payload's last whole chunk (bounds on a corrupt table)
+#pragma unroll
+  for (int i = 0; i < RegionRegs<G, NT>::kChunks; ++i) {
+    const int c = (int)threadIdx.x + i * NT;
+    int64_t q = (base >> 4) + (c < nchunks ? c : 0);
+    q = q < last ? q : last;
+    q = q > 0 ? q : 0;
+    r.c[i] = reinterpret_cast<const u32x4*>(a.payload)[q];
+  }
+}
+
+template <int G, typename TOut>
+__global__ __launch_bounds__(64) void k_decode(DecArgs a) {
+  constexpr int NT = 64;
+  constexpr int V = G / 16;     // elements per lane in a 16-lane transform group
+  constexpr int kCoop = 8;      // flagged tiles per round
+  constexpr int kSlot = G + 4;  // fp32 slot stride
+  using RO = TileRow<G, TOut>;
+  using RR = RegionRegs<G, NT>;
+  __shared__ __attribute__((aligned(16))) uint8_t ys[NT * RO::kStride];
+  __shared__ __attribute__((aligned(16))) u32x4 region[NT * RR::kChunks];
+  __shared__ __attribute__((aligned(16))) float ts[kCoop * kSlot];
+  __shared__ uint32_t flist[NT];
+
+  const int lane = threadIdx.x;
+  const int q4 = lane >> 4, r16 = lane & 15;
+
+  {  // header
     bool mism = false;
-    if (tid < 32) {
-      uint32_t got = reinterpret_cast<const uint32_t*>(a.payload)[tid];
-      uint32_t want = a.expect.w[tid];
-      if (tid == 1) {  // byte 6 records the encoder's input dtype: 0 or 1
+    if (lane < 32) {
+      uint32_t got = reinterpret_cast<const uint32_t*>(a.payload)[lane];
+      uint32_t want = a.expect.w[lane];
+      if (lane == 1) {  // byte 6 records the encoder's input dtype: 0 or 1
         mism = ((got >> 16) & 0xffu) > 1u;
         got &= 0xff00ffffu;
         want &= 0xff00ffffu;
       }
       mism = mism || got != want;
     }
-    const uint64_t m = ballot(mism);
-    if (tid == 0) bad = m != 0;
+    const bool bad = ballot(mism) != 0;
+    if (blockIdx.x == 0 && lane == 0) *a.status = bad ? (int32_t)TAH_ERR_BAD_PAYLOAD : (int32_t)TAH_OK;
+    if (bad) return;
   }
-  __syncthreads();
-  if (blockIdx.x == 0 && tid == 0) *a.status = bad ? (int32_t)TAH_ERR_BAD_PAYLOAD : (int32_t)TAH_OK;
-  if (bad) return;
 
-  const int64_t t0 = (int64_t)blockIdx.x * NT;
-  const int n = (int)((a.tiles - t0) < NT ? (a.tiles - t0) : NT);
-  if (n <= 0) return;
-  const bool act = tid < n;
-  const int64_t t = t0 + tid;
-  const uint32_t* table = reinterpret_cast<const uint32_t*>(a.payload + a.off_table);
-  const uint32_t* bitmap = reinterpret_cast<const uint32_t*>(a.payload + a.off_bitmap);
+  const int64_t ngroups = (a.tiles + NT - 1) / NT;
+  const int64_t step = gridDim.x;
+  int64_t g = blockIdx.x;
+  if (g >= ngroups) return;
 
-  // ---------------- phase A ----------------
-  int flag = 0, hi = 0;
-  uint32_t side = 0;
-  if (act) {
-    side = a.payload[a.off_side + t];
-    flag = side >> 7;
-    hi = (bitmap[t >> 5] >> (t & 31)) & 1u;
-    meta_scale[tid] = reinterpret_cast<const uint16_t*>(a.payload + a.off_scale)[t];
-    meta_lo[tid] = reinterpret_cast<const float*>(a.payload + a.off_zero)[t];
-  }
-  const uint64_t hmask = ballot(act && hi);
-  const int64_t blk_wave = (t0 >> 6) + wave;
-  const uint32_t hb_wg = table[t0 >> 6];
-  const uint32_t hb = (act ? table[blk_wave] : hb_wg) + lanes_below(hmask);
-  const int64_t wg_off = t0 * a.sz_lo + (int64_t)hb_wg * (a.sz_hi - a.sz_lo);
-  meta_off[tid] = (uint32_t)tid * (uint32_t)a.sz_lo + (hb - hb_wg) * (uint32_t)(a.sz_hi - a.sz_lo);
-  meta_side[tid] = (uint8_t)side;
-  meta_hi[tid] = (uint8_t)hi;
+  DecMeta mc, mn;  // metadata of the next group (its region is loading) and of the one after
+  RR rr;
+  int64_t rs_c;
+  int rlen_c;
+  load_meta<NT>(a, g, mc);
+  region_of<NT>(a, g, mc, rs_c, rlen_c);
+  load_region<G, NT>(a, rs_c, rlen_c, rr);
+  if (g + step < ngroups) load_meta<NT>(a, g + step, mn);
 
-  // plain tiles first, transformed tiles as one run rotated to wave (block mod NW)
-  // so that the Hadamard work spreads over the CU's SIMDs
-  const int cls = act ? ((flag << 1) | hi) : 4;
-  const uint64_t b0 = ballot(cls == 0), b1 = ballot(cls == 1), b2 = ballot(cls == 2), b3 = ballot(cls == 3);
-  if (lane == 0) {
-    cnt[wave][0] = __popcll(b0);
-    cnt[wave][1] = __popcll(b1);
-    cnt[wave][2] = __popcll(b2);
-    cnt[wave][3] = __popcll(b3);
-  }
-  __syncthreads();
-  if (act) {
-    int dst = 0;
+  int64_t prev_t0 = -1;
+  int prev_n = 0;
+  for (; g < ngroups; g += step) {
+    const int64_t t0 = g * NT;
+    const int n = (int)((a.tiles - t0) < NT ? (a.tiles - t0) : NT);
+    if (prev_t0 >= 0) stage_out<G, TOut, NT>(ys, a.y + prev_t0 * RO::kBytes, prev_n);
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int i = 0; i < RR::kChunks; ++i) region[lane + i * NT] = rr.c[i];
+    const DecMeta m = mc;
+    const int64_t rs = rs_c;
+    // the next group's region, and the metadata two groups ahead
+    if (g + step < ngroups) {
+      mc = mn;
+      region_of<NT>(a, g + step, mc, rs_c, rlen_c);
+      load_region<G, NT>(a, rs_c, rlen_c, rr);
+      if (g + 2 * step < ngroups) load_meta<NT>(a, g + 2 * step, mn);
+    } else {
 #pragma unroll
-      for (int w = 0; w < NW; ++w) dst += (c < cls || (c == cls && w < wave)) ? cnt[w][c] : 0;
-    const uint64_t mine = cls == 0 ? b0 : cls == 1 ? b1 : cls == 2 ? b2 : b3;
-    dst += (int)lanes_below(mine);
-    int plain = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) plain += cnt[w][0] + cnt[w][1];
-    const int start = (int)(blockIdx.x % NW) * 64;
-    dst = (dst + n + start - plain) % n;
-    perm[dst] = (uint16_t)tid;
-  }
-  __syncthreads();
+      for (int i = 0; i < RR::kChunks; ++i) rr.c[i] = u32x4{0u, 0u, 0u, 0u};  // last group: the old contents are dead
+    }
+    __syncthreads();
 
-  // ---------------- phase B ----------------
-  if (act) {
-    const int j = perm[tid];
-    const uint32_t sj = meta_side[j];
-    const int fj = sj >> 7;
-    const int d = sj & (G - 1);  // a corrupt pivot must not index outside the tile
-    const int b = meta_hi[j] ? a.b_hi : a.b_lo;
-    const int sz = meta_hi[j] ? a.sz_hi : a.sz_lo;
-    int64_t off = a.off_codes + wg_off + meta_off[j];
-    if (off + sz > a.len) off = a.off_codes;  // stays in bounds on a corrupt table
-    const float s = __uint_as_float(meta_scale[j] << 16);
-    const float lo = meta_lo[j];
+    // ---------------- dequantize: lane owns tile t0 + lane ----------------
+    const bool act = lane < n;
+    const uint64_t bm = ((uint64_t)m.bm1 << 32) | m.bm0;
+    const int hi = act ? (int)((bm >> lane) & 1u) : 0;
+    const int flag = act ? (int)(m.side >> 7) : 0;
+    const int piv = (int)(m.side & (G - 1));  // a corrupt pivot must not index outside the tile
+    const int b = hi ? a.b_hi : a.b_lo;
+    const int sz = hi ? a.sz_hi : a.sz_lo;
     float v[G];
-    load_dequant_b<G>(b, a.payload + off, s, lo, v);
-    if (fj) {
-      fwht<G>(v);
+    if (act) {
+      int off = (int)(rs & 15) + lane * a.sz_lo + (int)lanes_below(bm) * (a.sz_hi - a.sz_lo);
+      const int cap = RR::kChunks * NT * 16 - sz;
+      off = off < cap ? off : 0;  // stays inside the region buffer on a corrupt table
+      const float s = __uint_as_float(m.scale << 16);
+      load_dequant_b<G>(b, reinterpret_cast<const uint8_t*>(region) + off, s, m.zero, v);
+    }
+    const uint64_t fmask = ballot(act && flag);
+    const int nf = (int)__popcll(fmask);
+    const int slot = (int)lanes_below(fmask);
+    if (act && !flag) lds_write_tile<G, TOut>(ys + lane * RO::kStride, v);
+    if (nf != 0) {
+      if (act && flag) flist[slot] = (uint32_t)lane | ((uint32_t)piv << 8);
+      // rounds of kCoop flagged tiles: owners fill the slots, 16-lane groups
+      // apply H^T / G and undo the swap into the tile's row
+      for (int j_lo = 0; j_lo < nf; j_lo += kCoop) {
+        const int j_hi = nf < j_lo + kCoop ? nf : j_lo + kCoop;
+        if (act && flag && slot >= j_lo && slot < j_hi)
+          lds_write_tile<G, float>(reinterpret_cast<uint8_t*>(ts + (slot - j_lo) * kSlot), v);
+        __syncthreads();
+        for (int j0 = j_lo; j0 < j_hi; j0 += 4) {
+          const int j = j0 + q4;
+          if (j < j_hi) {
+            const uint32_t e = flist[j];
+            uint8_t* row = ys + (e & 255u) * RO::kStride;
+            float y[V];
+            lds_read_part<V, float>(reinterpret_cast<const uint8_t*>(ts + (j - j_lo) * kSlot), r16, y);
+            fwht16<V>(y, r16);
 #pragma unroll
-      for (int k = 0; k < G; ++k) v[k] = v[k] * (1.0f / G);
+            for (int i = 0; i < V; ++i) y[i] = y[i] * (1.0f / G);
+            lds_write_part<V, TOut>(row, r16, y);
+            if (r16 == 0) {  // element d takes y_0, element 0 takes y_d
+              const int d = (int)(e >> 8);
+              const uint32_t yd = lds_elem_bits<TOut>(row, d);
+              lds_elem_set<TOut>(row, d, f32_to_elem_bits<TOut>(y[0]));
+              lds_elem_set<TOut>(row, 0, yd);
+            }
+          }
+        }
+        __syncthreads();
+      }
     }
-    uint8_t* row = ys + j * RO::kStride;
-    lds_write_tile<G, TOut>(row, v);
-    if (fj) {
-      const uint32_t yd = lds_elem_bits<TOut>(row, d);
-      lds_elem_set<TOut>(row, d, f32_to_elem_bits<TOut>(v[0]));
-      lds_elem_set<TOut>(row, 0, yd);
-    }
+    prev_t0 = t0;
+    prev_n = n;
+    __syncthreads();  // rows and region are read by other lanes next
   }
-  __syncthreads();
-  stage_out<G, TOut, NT>(ys, a.y + t0 * RO::kBytes, n);
+  if (prev_t0 >= 0) stage_out<G, TOut, NT>(ys, a.y + prev_t0 * RO::kBytes, prev_n);
+}
+
+template <typename K>
+static int dec_wgs_per_cu(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 64, 0) != hipSuccess || n < 1) n = 1;
+  return n;
+}
+
+static int dec_cu_count() {
+  static int cus = 0;
+  if (!cus) {
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
+  }
+  return cus;
 }
 
 template <int G, typename TOut>
 static hipError_t launch_dec_t(const DecArgs& a, hipStream_t st) {
-  constexpr int NT = dec_tiles_per_wg<G, TOut>();
-  const int64_t nwg = a.tiles > 0 ? (a.tiles + NT - 1) / NT : 1;
-  hipLaunchKernelGGL((k_decode<G, TOut>), dim3((unsigned)nwg), dim3(NT), 0, st, a);
+  static const int per_cu = dec_wgs_per_cu(k_decode<G, TOut>);
+  const int64_t ngroups = a.tiles > 0 ? (a.tiles + 63) / 64 : 1;
+  const int64_t resident = (int64_t)per_cu * dec_cu_count();
+  const int64_t nwg = ngroups < resident ? ngroups : resident;
+  hipLaunchKernelGGL((k_decode<G, TOut>), dim3((unsigned)nwg), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
