@@ -157,6 +157,12 @@ __device__ __forceinline__ float tile_entropy(const float (&v)[G], float l1, con
   return l1 > 0.0f ? log2_full(l1, lt) - S / l1 : 0.0f;
 }
 
+// The same entropy from the two sums L = sum |a_k| and S = sum |a_k| log2 |a_k|.
+__device__ __forceinline__ float entropy_from_sums(float l1, float S, const float* lt) {
+  asm volatile("" : "+v"(S));
+  return l1 > 0.0f ? log2_full(l1, lt) - S / l1 : 0.0f;
+}
+
 // Unnormalized Sylvester Walsh-Hadamard transform in registers, v <- H_G v
 // (H_G[i][j] = (-1)^popcount(i & j)); stages h = 1, 2, ..., G/2, butterfly
 // (a, b) -> (a + b, a - b). Fully unrolled: G log2 G adds, no data movement.
