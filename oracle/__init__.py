@@ -82,6 +82,12 @@ def lib():
         L.tahref_encode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, P(_Params), ctypes.c_void_p, ctypes.c_size_t]
         L.tahref_decode.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int64, P(_Params), ctypes.c_void_p, ctypes.c_int]
         L.tahref_tile_stats.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, P(_Params)] + [ctypes.c_void_p] * 6
+        L.tahref_naive_payload_bytes.argtypes = [ctypes.c_int64, ctypes.c_int, P(ctypes.c_size_t)]
+        L.tahref_naive_quantize.argtypes = [ctypes.c_float, ctypes.c_int, ctypes.c_float, P(ctypes.c_int32)]
+        L.tahref_naive_dequantize.argtypes = [ctypes.c_int32, ctypes.c_int, ctypes.c_float]
+        L.tahref_naive_dequantize.restype = ctypes.c_float
+        L.tahref_naive_encode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t]
+        L.tahref_naive_decode.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int, ctypes.c_float, ctypes.c_void_p, ctypes.c_int]
         _lib = L
     return _lib
 
@@ -209,3 +215,49 @@ def tile_stats(x: np.ndarray, p) -> dict:
     if rc:
         raise OracleError(rc, "tile_stats")
     return dict(H=H, flag=flag, pivot=piv, hi=hi, lo=lo, scale=sc)
+
+
+# ---------------------------------------------------------------- backward compressor (Q_Naive) ----
+def naive_payload_bytes(n: int, bits: int) -> int:
+    out = ctypes.c_size_t()
+    rc = lib().tahref_naive_payload_bytes(int(n), int(bits), ctypes.byref(out))
+    if rc:
+        raise OracleError(rc, "naive_payload_bytes")
+    return out.value
+
+
+def naive_quantize(g, bits: int, c: float) -> np.ndarray:
+    g = np.asarray(g, dtype=np.float32).ravel()
+    q = ctypes.c_int32()
+    out = np.zeros(g.size, dtype=np.int32)
+    f = lib().tahref_naive_quantize
+    for i, v in enumerate(g):
+        rc = f(float(v), int(bits), float(np.float32(c)), ctypes.byref(q))
+        if rc:
+            raise OracleError(rc, "naive_quantize")
+        out[i] = q.value
+    return out
+
+
+def naive_dequantize(q, bits: int, c: float) -> np.ndarray:
+    q = np.asarray(q, dtype=np.int32).ravel()
+    f = lib().tahref_naive_dequantize
+    return np.array([f(int(v), int(bits), float(np.float32(c))) for v in q], dtype=np.float32)
+
+
+def naive_encode(g: np.ndarray, bits: int, c: float) -> np.ndarray:
+    g = np.ascontiguousarray(g)
+    out = np.zeros(naive_payload_bytes(g.size, bits), dtype=np.uint8)
+    rc = lib().tahref_naive_encode(_ptr(g), _dtype_of(g), g.size, int(bits), float(np.float32(c)), _ptr(out), out.size)
+    if rc:
+        raise OracleError(rc, "naive_encode")
+    return out
+
+
+def naive_decode(payload: np.ndarray, n: int, bits: int, c: float, y_dtype: int = F32) -> np.ndarray:
+    payload = np.ascontiguousarray(payload, dtype=np.uint8)
+    y = np.zeros(n, dtype=np.float32 if y_dtype == F32 else np.uint16)
+    rc = lib().tahref_naive_decode(_ptr(payload), payload.size, int(n), int(bits), float(np.float32(c)), _ptr(y), int(y_dtype))
+    if rc:
+        raise OracleError(rc, "naive_decode")
+    return y

@@ -568,3 +568,99 @@ int tahref_decode(const uint8_t* P, size_t len, int64_t tokens, int64_t hidden, 
   if (hi_count != pl.k * pl.nsamples) return TAHREF_ERR_BAD_PAYLOAD;
   return TAHREF_OK;
 }
+
+/* ------------------------------------------------------------------ */
+/* backward compressor Q_Naive (Algorithm 1 lines 6-7, App. H Eq. 24)  */
+/* ------------------------------------------------------------------ */
+
+static int naive_args_ok(int64_t n, int bits, float c) {
+  return n >= 0 && bits >= 2 && bits <= 16 && c > 0.0f && isfinite(c) && isfinite(ldexpf(c, bits - 1));
+}
+
+int tahref_naive_payload_bytes(int64_t n, int bits, size_t* out) {
+  if (n < 0 || bits < 2 || bits > 16 || !out) return TAHREF_ERR_INVALID_ARG;
+  const int64_t groups = (n + 31) / 32; /* 32 codes of b bits fill b whole 32-bit words */
+  *out = (size_t)align256(256 + groups * 4 * bits);
+  return TAHREF_OK;
+}
+
+/*
+ * q = clamp(round_half_even(g * c * 2^(b-1)), -2^(b-1), 2^(b-1) - 1).
+ * c * 2^(b-1) is exact (a power-of-two scaling), so the product g * c_q is the
+ * one fp32 rounding before the integer rounding, the same as rounding c * g
+ * and scaling it by 2^(b-1).
+ */
+int tahref_naive_quantize(float g, int bits, float c, int32_t* q) {
+  if (!naive_args_ok(1, bits, c) || !q) return TAHREF_ERR_INVALID_ARG;
+  const float cq = ldexpf(c, bits - 1);
+  const float y = g * cq;
+  const float lo = -ldexpf(1.0f, bits - 1), hi = ldexpf(1.0f, bits - 1) - 1.0f;
+  float r = nearbyintf(y); /* the default rounding mode: half to even */
+  if (!(r >= lo)) r = lo;  /* also catches NaN */
+  if (r > hi) r = hi;
+  *q = (int32_t)r;
+  return TAHREF_OK;
+}
+
+/* g_hat = Q(c g) / c = (q 2^-(b-1)) / c = q / (c 2^(b-1)): one fp32 division of exact operands. */
+float tahref_naive_dequantize(int32_t q, int bits, float c) {
+  const float cq = ldexpf(c, bits - 1);
+  return (float)q / cq;
+}
+
+static void naive_header(uint8_t* P, int64_t n, int bits, float c, int dtype, int64_t total) {
+  memset(P, 0, 256);
+  put_u32(P, 0, 0x4E484154u); /* "TAHN" */
+  put_u16(P, 4, 1);
+  put_u8(P, 6, (uint32_t)dtype);
+  put_u8(P, 7, (uint32_t)bits);
+  put_u64(P, 8, (uint64_t)n);
+  put_u32(P, 16, f2u(c));
+  put_u64(P, 24, (uint64_t)total);
+}
+
+int tahref_naive_encode(const void* g, int g_dtype, int64_t n, int bits, float c, uint8_t* P, size_t cap) {
+  if (!naive_args_ok(n, bits, c) || (g_dtype != TAHREF_F32 && g_dtype != TAHREF_BF16) || !P || (n > 0 && !g))
+    return TAHREF_ERR_INVALID_ARG;
+  size_t total;
+  tahref_naive_payload_bytes(n, bits, &total);
+  if (cap < total) return TAHREF_ERR_BUFFER_TOO_SMALL;
+  memset(P, 0, total);
+  naive_header(P, n, bits, c, g_dtype, (int64_t)total);
+  const uint32_t mask = (bits == 32) ? 0xffffffffu : ((1u << bits) - 1u);
+  for (int64_t i = 0; i < n; ++i) {
+    const float gi = g_dtype == TAHREF_F32 ? ((const float*)g)[i] : bf16_to_f32(((const uint16_t*)g)[i]);
+    int32_t q;
+    tahref_naive_quantize(gi, bits, c, &q);
+    const uint32_t code = (uint32_t)q & mask;
+    for (int k = 0; k < bits; ++k) { /* bit by bit, least significant first */
+      const int64_t bit = i * bits + k;
+      if ((code >> k) & 1u) P[256 + bit / 8] |= (uint8_t)(1u << (bit % 8));
+    }
+  }
+  return TAHREF_OK;
+}
+
+int tahref_naive_decode(const uint8_t* P, size_t len, int64_t n, int bits, float c, void* y, int y_dtype) {
+  if (!naive_args_ok(n, bits, c) || (y_dtype != TAHREF_F32 && y_dtype != TAHREF_BF16) || !P || (n > 0 && !y))
+    return TAHREF_ERR_INVALID_ARG;
+  size_t total;
+  tahref_naive_payload_bytes(n, bits, &total);
+  if (len < total) return TAHREF_ERR_BUFFER_TOO_SMALL;
+  if (get_u32(P, 0) != 0x4E484154u || get_u16(P, 4) != 1 || P[7] != (uint8_t)bits ||
+      (uint64_t)get_u32(P, 8) + ((uint64_t)get_u32(P, 12) << 32) != (uint64_t)n || get_u32(P, 16) != f2u(c) ||
+      (uint64_t)get_u32(P, 24) + ((uint64_t)get_u32(P, 28) << 32) != (uint64_t)total)
+    return TAHREF_ERR_BAD_PAYLOAD;
+  for (int64_t i = 0; i < n; ++i) {
+    uint32_t code = 0;
+    for (int k = 0; k < bits; ++k) {
+      const int64_t bit = i * bits + k;
+      code |= (uint32_t)((P[256 + bit / 8] >> (bit % 8)) & 1u) << k;
+    }
+    const int32_t q = (code >> (bits - 1)) & 1u ? (int32_t)code - (int32_t)(1u << bits) : (int32_t)code;
+    const float v = tahref_naive_dequantize(q, bits, c);
+    if (y_dtype == TAHREF_F32) ((float*)y)[i] = v;
+    else ((uint16_t*)y)[i] = f32_to_bf16_rne(v);
+  }
+  return TAHREF_OK;
+}

@@ -75,6 +75,26 @@ int tahref_decode(const uint8_t* payload, size_t payload_len, int64_t tokens, in
 int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden, const tahref_params* p,
                       float* H, uint8_t* flag, uint8_t* pivot, uint8_t* hi, float* lo, float* scale);
 
+/*
+ * Backward compressor Q_Naive for the activation gradients that travel back
+ * across the stage boundary (Algorithm 1 lines 6-7; §3.5 calls it a simple
+ * fixed-point compressor of 6-8 bits) with the scaling of Appendix H,
+ * Eq. (24): g_hat = Q(c g) / c. Reading: Q is b-bit signed fixed point with
+ * b-1 fractional bits (values k 2^-(b-1), k in [-2^(b-1), 2^(b-1)-1]),
+ * round half to even, saturating; c is a positive constant.
+ * Payload: 256-byte header region (magic "TAHN", version, input dtype, b, n,
+ * c, total), then the n codes as b-bit two's complement, code i at stream
+ * bits [i b, i b + b), least significant bit first, zero padded to a whole
+ * number of 32-code groups and to 256 bytes.
+ */
+int tahref_naive_payload_bytes(int64_t n, int bits, size_t* out);
+int tahref_naive_quantize(float g, int bits, float c, int32_t* q);
+float tahref_naive_dequantize(int32_t q, int bits, float c);
+int tahref_naive_encode(const void* g, int g_dtype, int64_t n, int bits, float c, uint8_t* payload,
+                        size_t payload_cap);
+int tahref_naive_decode(const uint8_t* payload, size_t payload_len, int64_t n, int bits, float c, void* y,
+                        int y_dtype);
+
 #ifdef __cplusplus
 }
 #endif

@@ -469,3 +469,73 @@ def test_bf16_input_widens_exactly(ref):
     assert Pb[6] == 1 and Pf[6] == 0
     Pb[6] = 0
     assert np.array_equal(Pb, Pf)
+
+
+# ------------------------------------------------ backward compressor (Q_Naive) ----
+# Algorithm 1 lines 6-7 (fixed-point compressor of the activation gradients) and
+# Appendix H Eq. (24) g_hat = Q(c g) / c; Q read as b-bit signed fixed point with
+# b-1 fractional bits, round half to even, saturating.
+
+def test_naive_quantize_worked_values(ref):
+    # b = 8, c = 1: step 2^-7; range [-1, 1 - 2^-7]
+    got = ref.naive_quantize([0.5, -1.0, 0.999, 3.0, -3.0, 2.0**-8, 1.5 * 2.0**-7, -2.5 * 2.0**-7, 0.0, -0.0], 8, 1.0)
+    # 0.5*128 = 64; -128; 127.87 -> 128 saturates to 127; +-3 saturate; 0.5 -> 0 (tie to even);
+    # 1.5 -> 2 (tie to even); -2.5 -> -2 (tie to even); zeros
+    assert got.tolist() == [64, -128, 127, 127, -128, 0, 2, -2, 0, 0]
+
+
+def test_naive_grid_points_round_trip_exactly(ref):
+    # every representable k / (c 2^(b-1)) comes back bit for bit
+    for bits, c in ((4, 1.0), (6, 1e4), (8, 3.5), (10, 2.0**-3)):
+        cq = np.float32(c) * np.float32(2.0 ** (bits - 1))
+        k = np.arange(-(2 ** (bits - 1)), 2 ** (bits - 1), dtype=np.int64)
+        g = (k.astype(np.float64) / np.float64(cq)).astype(np.float32)
+        q = ref.naive_quantize(g, bits, c)
+        assert np.array_equal(q, k)
+        assert np.array_equal(ref.naive_dequantize(q, bits, c), g)
+
+
+def test_naive_error_bound_and_saturation(ref):
+    g = np.random.default_rng(4).standard_normal(4000).astype(np.float32) * 0.3
+    for bits, c in ((4, 1.0), (8, 1.0), (8, 2.0), (10, 0.5)):
+        cq = c * 2.0 ** (bits - 1)
+        lo, hi = -(2 ** (bits - 1)) / cq, (2 ** (bits - 1) - 1) / cq
+        gh = ref.naive_dequantize(ref.naive_quantize(g, bits, c), bits, c).astype(np.float64)
+        inside = (g >= lo) & (g <= hi)
+        # half a step plus the fp32 roundings of the product and of the division
+        tol = 0.5 / cq + 2.0 ** -23 * np.abs(g[inside]) * 2
+        assert np.all(np.abs(gh[inside] - g[inside]) <= tol)
+        assert np.all(gh[g > hi] == np.float32(hi)) and np.all(gh[g < lo] == np.float32(lo))
+
+
+def test_naive_scaling_keeps_small_gradients(ref):
+    # App. H: gradients of order 1e-5 vanish in 8-bit fixed point; Eq. (24) with c = 1e4 keeps them
+    g = np.random.default_rng(6).uniform(-3e-5, 3e-5, 1000).astype(np.float32)
+    assert np.all(ref.naive_quantize(g, 8, 1.0) == 0)
+    gh = ref.naive_dequantize(ref.naive_quantize(g, 8, 1e4), 8, 1e4)
+    assert np.count_nonzero(gh) > 900
+    assert np.abs(gh - g).max() <= 0.5 / (1e4 * 128) * 1.001
+
+
+def test_naive_payload_bytes_worked_by_hand(ref):
+    # b = 4, c = 1 (step 1/8): 0.5 -> 4 = 0100b, -0.25 -> -2 = 1110b, 0.125 -> 1 = 0001b, -1 -> -8 = 1000b.
+    # Stream, LSB first: byte 0 = code1 << 4 | code0 = 0xE4, byte 1 = code3 << 4 | code2 = 0x81.
+    P = ref.naive_encode(np.array([0.5, -0.25, 0.125, -1.0], np.float32), 4, 1.0)
+    assert P.size == 512  # 256-byte header region + one 32-code group of 16 bytes, padded to 256
+    assert bytes(P[0:4]) == b"TAHN" and P[4] == 1 and P[5] == 0 and P[6] == 0 and P[7] == 4
+    assert int.from_bytes(bytes(P[8:16]), "little") == 4
+    assert bytes(P[16:20]) == np.float32(1.0).tobytes()
+    assert int.from_bytes(bytes(P[24:32]), "little") == 512
+    assert P[256] == 0xE4 and P[257] == 0x81 and not P[258:].any()
+    assert ref.naive_decode(P, 4, 4, 1.0).tolist() == [0.5, -0.25, 0.125, -1.0]
+
+
+def test_naive_payload_size_and_padding(ref):
+    for n, bits in ((0, 8), (1, 8), (31, 6), (32, 6), (33, 10), (1000, 16)):
+        groups = (n + 31) // 32
+        want = ((256 + groups * 4 * bits) + 255) // 256 * 256
+        assert ref.naive_payload_bytes(n, bits) == want
+        g = np.linspace(-1, 1, n, dtype=np.float32)
+        P = ref.naive_encode(g, bits, 1.0)
+        used = 256 + (n * bits + 7) // 8
+        assert not P[used:].any()
