@@ -43,6 +43,9 @@ EXPORTS = (
     "tah_roundtrip",
     "tah_tile_entropy",
     "tah_workspace_entropy",
+    "tah_naive_payload_bytes",
+    "tah_naive_encode",
+    "tah_naive_decode",
     "tah_read_device_status",
     "tah_status_string",
     "tah_abi_version",
@@ -118,6 +121,12 @@ def lib() -> ctypes.CDLL:
         L.tah_roundtrip.restype = ctypes.c_int
         L.tah_tile_entropy.argtypes = [vp, ctypes.c_int, i64, i64, P(_CParams), vp, vp, sz, vp]
         L.tah_tile_entropy.restype = ctypes.c_int
+        L.tah_naive_payload_bytes.argtypes = [i64, ctypes.c_int, P(sz)]
+        L.tah_naive_payload_bytes.restype = ctypes.c_int
+        L.tah_naive_encode.argtypes = [vp, ctypes.c_int, i64, ctypes.c_int, ctypes.c_float, vp, sz, vp]
+        L.tah_naive_encode.restype = ctypes.c_int
+        L.tah_naive_decode.argtypes = [vp, sz, i64, ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, sz, vp]
+        L.tah_naive_decode.restype = ctypes.c_int
         L.tah_read_device_status.argtypes = [vp, vp, P(ctypes.c_int32)]
         L.tah_read_device_status.restype = ctypes.c_int
         L.tah_status_string.argtypes = [ctypes.c_int]
@@ -265,6 +274,40 @@ def tile_entropy(x: torch.Tensor, p, h: torch.Tensor | None = None, ws: torch.Te
                                 ws.numel(), _stream(stream))
     _check(rc, "tah_tile_entropy")
     return h
+
+
+# ---------------------------------------------------------------- backward compressor ----
+def naive_payload_bytes(n: int, bits: int) -> int:
+    out = ctypes.c_size_t()
+    _check(lib().tah_naive_payload_bytes(int(n), int(bits), ctypes.byref(out)), "tah_naive_payload_bytes")
+    return int(out.value)
+
+
+def naive_encode(g: torch.Tensor, bits: int, c: float, payload: torch.Tensor | None = None,
+                 stream=None) -> torch.Tensor:
+    """tah_naive_encode: gradient tensor g (any shape, contiguous) -> payload."""
+    if not g.is_contiguous():
+        raise ValueError("g must be contiguous")
+    n = g.numel()
+    if payload is None:
+        payload = torch.zeros(naive_payload_bytes(n, bits), dtype=torch.uint8, device=g.device)
+    rc = lib().tah_naive_encode(_ptr(g), _dtype_code(g.dtype), n, int(bits), float(c), _ptr(payload),
+                                payload.numel(), _stream(stream))
+    _check(rc, "tah_naive_encode")
+    return payload
+
+
+def naive_decode(payload: torch.Tensor, n: int, bits: int, c: float, y_dtype: torch.dtype = torch.float32,
+                 y: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """tah_naive_decode: payload -> n gradient values (y_dtype)."""
+    if y is None:
+        y = torch.empty(int(n), dtype=y_dtype, device=payload.device)
+    if ws is None:
+        ws = torch.empty(256, dtype=torch.uint8, device=payload.device)
+    rc = lib().tah_naive_decode(_ptr(payload), payload.numel(), int(n), int(bits), float(c), _ptr(y),
+                                _dtype_code(y.dtype), _ptr(ws), ws.numel(), _stream(stream))
+    _check(rc, "tah_naive_decode")
+    return y
 
 
 def read_device_status(ws: torch.Tensor, stream=None) -> int:

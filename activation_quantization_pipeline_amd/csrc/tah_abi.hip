@@ -290,6 +290,36 @@ tah_status_t tah_tile_entropy(const void* x, tah_dtype_t x_dtype, int64_t tokens
   return hip_status(launch_stats(pl, x, h, ws, false, static_cast<hipStream_t>(stream)));
 }
 
+static bool naive_ok(int64_t n, int bits, float c) {
+  return n >= 0 && bits >= 2 && bits <= 16 && c > 0.0f && isfinite(c) && isfinite(ldexpf(c, bits - 1));
+}
+
+tah_status_t tah_naive_payload_bytes(int64_t n, int bits, size_t* out) {
+  if (n < 0 || bits < 2 || bits > 16 || !out) return TAH_ERR_INVALID_ARG;
+  *out = (size_t)naive_payload_bytes(n, bits);
+  return TAH_OK;
+}
+
+tah_status_t tah_naive_encode(const void* g, tah_dtype_t g_dtype, int64_t n, int bits, float c, void* payload,
+                              size_t payload_cap, void* stream) {
+  if (!naive_ok(n, bits, c)) return TAH_ERR_INVALID_ARG;
+  if (g_dtype != TAH_DTYPE_F32 && g_dtype != TAH_DTYPE_BF16) return TAH_ERR_INVALID_ARG;
+  if (!payload || !aligned16(payload) || (n > 0 && (!g || !aligned16(g)))) return TAH_ERR_INVALID_ARG;
+  if (payload_cap < (size_t)naive_payload_bytes(n, bits)) return TAH_ERR_BUFFER_TOO_SMALL;
+  return hip_status(launch_naive_encode(g, g_dtype, n, bits, c, payload, static_cast<hipStream_t>(stream)));
+}
+
+tah_status_t tah_naive_decode(const void* payload, size_t payload_len, int64_t n, int bits, float c, void* y,
+                              tah_dtype_t y_dtype, void* ws, size_t ws_cap, void* stream) {
+  if (!naive_ok(n, bits, c)) return TAH_ERR_INVALID_ARG;
+  if (y_dtype != TAH_DTYPE_F32 && y_dtype != TAH_DTYPE_BF16) return TAH_ERR_INVALID_ARG;
+  if (!payload || !aligned16(payload) || !ws || !aligned16(ws) || (n > 0 && (!y || !aligned16(y))))
+    return TAH_ERR_INVALID_ARG;
+  if (payload_len < (size_t)naive_payload_bytes(n, bits)) return TAH_ERR_BUFFER_TOO_SMALL;
+  if (ws_cap < 256) return TAH_ERR_BUFFER_TOO_SMALL;
+  return hip_status(launch_naive_decode(payload, n, bits, c, y, y_dtype, ws, static_cast<hipStream_t>(stream)));
+}
+
 tah_status_t tah_read_device_status(const void* ws, void* stream, int32_t* out) {
   if (!ws || !out) return TAH_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);

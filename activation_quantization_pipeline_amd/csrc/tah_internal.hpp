@@ -64,6 +64,13 @@ hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, b
 hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st);
 hipError_t launch_decode(const Plan& pl, const void* payload, void* y, int y_dtype, void* ws, hipStream_t st);
 
+// Backward compressor (tah_naive.hip).
+int64_t naive_payload_bytes(int64_t n, int bits);
+hipError_t launch_naive_encode(const void* g, int g_dtype, int64_t n, int bits, float c, void* payload,
+                               hipStream_t st);
+hipError_t launch_naive_decode(const void* payload, int64_t n, int bits, float c, void* y, int y_dtype, void* ws,
+                               hipStream_t st);
+
 void make_header(const Plan& pl, Header* h);
 void make_pads(const Plan& pl, PadRanges* pr);
 

@@ -13,8 +13,10 @@ activations written) / time per step, in GB/s.
 
 Prints one JSON line. Extra legs: encode-only and decode-only rates, the same
 shape with a mixed 80% INT4 / 20% INT3 allocation (the paper's default,
-general two-pass path), a 512 MB device copy for the achievable bandwidth, and
-the CPU oracle on the host (single thread).
+general two-pass path), the backward path on activation gradients of the same
+shape (the 8-bit fixed-point compressor with the scaling of Eq. 24, encode and
+decode, and the TAH-Quant codec at 4 bits), a 512 MB device copy for the
+achievable bandwidth, and the CPU oracle on the host (single thread).
 """
 
 import argparse
@@ -195,6 +197,34 @@ def main():
         extras["mixed_80_20_roundtrip_gbps"] = round((2 * x_bytes + cm.payload_bytes) / (m_ms * 1e-3) / 1e9, 1)
         extras["mixed_80_20_ms_per_step"] = round(m_ms, 5)
         del pm, wsm
+        # the backward path (Algorithm 1 lines 6-7): activation gradients of the same shape,
+        # fixed-point compressor at 8 bits with the scaling of Eq. (24), and TAH-Quant at 4 bits
+        gname = "g1_8192x8192_bf16_grad"
+        gw = synth.workload(gname)
+        g_host = synth.generate(gname, 0)
+        gs = [to_dev(g_host, torch) for _ in range(n_sets)]
+        nb, nc = synth.NAIVE[gname]["bits"], synth.NAIVE[gname]["c"]
+        n_el = gw.tokens * gw.hidden
+        npb = tah.naive_payload_bytes(n_el, nb)
+        nps = [torch.empty(npb, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+        wsn = torch.zeros(256, dtype=torch.uint8, device=dev)
+        Lb = tah.lib()
+        ne_args = [(gs[i].data_ptr(), 1, n_el, nb, nc, nps[i].data_ptr(), npb, stream_h) for i in range(n_sets)]
+        nd_args = [(nps[i].data_ptr(), npb, n_el, nb, nc, ys[i].data_ptr(), 1, wsn.data_ptr(), 256, stream_h)
+                   for i in range(n_sets)]
+        _, ne_mean, _, _ = time_launches(torch, lambda i: Lb.tah_naive_encode(*ne_args[i]), n_sets, args.steps,
+                                         args.warmup)
+        _, nd_mean, _, _ = time_launches(torch, lambda i: Lb.tah_naive_decode(*nd_args[i]), n_sets, args.steps,
+                                         args.warmup)
+        extras["bw_naive8_encode_gbps"] = round((2 * n_el + npb) / (ne_mean * 1e-3) / 1e9, 1)
+        extras["bw_naive8_decode_gbps"] = round((npb + 2 * n_el) / (nd_mean * 1e-3) / 1e9, 1)
+        cg = tah.Codec(gw.tokens, gw.hidden, gw.params, torch.bfloat16, torch.bfloat16)
+        pg = [torch.empty(cg.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+        wsg = torch.empty(cg.workspace_bytes, dtype=torch.uint8, device=dev)
+        g_ms, _, _, _ = time_launches(torch, lambda i: cg.roundtrip(gs[i], pg[i], ys[i], wsg, stream_h), n_sets,
+                                      args.steps, args.warmup)
+        extras["bw_tah4_roundtrip_gbps"] = round((2 * 2 * n_el + cg.payload_bytes) / (g_ms * 1e-3) / 1e9, 1)
+        del gs, nps, pg, wsg
         # achievable bandwidth of a plain 512 MB device copy
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)

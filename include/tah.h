@@ -138,8 +138,37 @@ tah_status_t tah_tile_entropy(const void* x, tah_dtype_t x_dtype, int64_t tokens
  * tah_encode and tah_roundtrip. */
 tah_status_t tah_workspace_entropy(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* offset);
 
+/*
+ * Backward compressor for the activation gradients that the next stage sends
+ * back (Algorithm 1, lines 6-7: a simple fixed-point compressor, §3.5), with
+ * the scaling of Appendix H, Eq. (24): g_hat = Q(c g) / c. Q is b-bit signed
+ * fixed point with b-1 fractional bits, round half to even, saturating:
+ *   q = clamp(rne(g * c * 2^(b-1)), -2^(b-1), 2^(b-1) - 1),  g_hat = q / (c * 2^(b-1)).
+ * n elements of a contiguous fp32 or bf16 tensor (any shape, row-major).
+ * bits: 2..16; c: positive and finite, with c * 2^(b-1) finite.
+ * Payload layout (little-endian): bytes 0-3 "TAHN", 4-5 version 1, 6 input
+ * dtype, 7 bits, 8-15 n, 16-19 c (fp32), 24-31 total bytes, zero to byte 255;
+ * then the codes as b-bit two's complement, code i at stream bits
+ * [i b, i b + b), least significant bit first; zero padding to a whole number
+ * of 32-code groups (b 32-bit words each) and to a multiple of 256 bytes.
+ */
+tah_status_t tah_naive_payload_bytes(int64_t n, int bits, size_t* out);
+
+/* Quantize g (n elements, g_dtype) into payload (payload_cap bytes, at least
+ * tah_naive_payload_bytes). */
+tah_status_t tah_naive_encode(const void* g, tah_dtype_t g_dtype, int64_t n, int bits, float c, void* payload,
+                              size_t payload_cap, void* stream);
+
+/* Dequantize payload into y (n elements, y_dtype; bf16 rounded to nearest
+ * even). ws (at least 256 bytes) receives the device status word: the header
+ * is checked against n, bits and c (the input-dtype byte is not), and on a
+ * mismatch the word is TAH_ERR_BAD_PAYLOAD and y is left untouched. */
+tah_status_t tah_naive_decode(const void* payload, size_t payload_len, int64_t n, int bits, float c, void* y,
+                              tah_dtype_t y_dtype, void* ws, size_t ws_cap, void* stream);
+
 /* Waits for `stream`, then copies the device status word of the last
- * tah_decode on this workspace into *out (TAH_OK or TAH_ERR_BAD_PAYLOAD). */
+ * tah_decode or tah_naive_decode on this workspace into *out (TAH_OK or
+ * TAH_ERR_BAD_PAYLOAD). */
 tah_status_t tah_read_device_status(const void* ws, void* stream, int32_t* out);
 
 const char* tah_status_string(tah_status_t s);

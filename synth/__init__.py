@@ -123,6 +123,19 @@ def gen_gelu(tokens, hidden, dtype, seed, wid, n_out, mult, var=2.0):
     return _finish(x, dtype)
 
 
+def gen_gradients(tokens, hidden, dtype, seed, wid, heavy_frac=0.01, heavy_mult=100.0):
+    """Activation gradients at a stage boundary (what Algorithm 1 sends back):
+    N(0,1) per element times a per-token scale 1e-6 * lognormal(sigma = 1.5),
+    and a few tokens (heavy_frac) x heavy_mult: most tokens carry gradients of
+    order 1e-6..1e-5 (App. H speaks of 1e-5), a few carry most of the norm."""
+    g = _philox(seed, wid)
+    row = 1e-6 * np.exp(1.5 * g.standard_normal(tokens))
+    heavy = g.choice(tokens, size=_count(heavy_frac, tokens), replace=False) if tokens else np.zeros(0, int)
+    row[heavy] *= heavy_mult
+    x = g.standard_normal((tokens, hidden)) * row[:, None]
+    return _finish(x, dtype)
+
+
 WORKLOADS = {
     "c1_256x512_f32_g32": Workload(
         "c1_256x512_f32_g32", 256, 512, F32,
@@ -144,6 +157,25 @@ WORKLOADS = {
         "c5_8192x8192_bf16_g64", 8192, 8192, BF16,
         Params(tile=64, tokens_per_sample=0, bit_budget=3.0, candidates=(3, 4, 8), tau=2.0),
         "GeLU(N(0,2)) bf16, 0.1% outlier channels x200", 5),
+    # activation gradients going back across the boundary, coded by TAH-Quant at
+    # 4 bits (App. H, Table 10); the same tensors feed the fixed-point compressor
+    "g1_8192x8192_bf16_grad": Workload(
+        "g1_8192x8192_bf16_grad", 8192, 8192, BF16,
+        Params(tile=64, tokens_per_sample=0, bit_budget=4.0, candidates=(4,), tau=2.0),
+        "activation gradients: N(0,1) x 1e-6 lognormal(1.5) per token, 1% tokens x100", 6),
+    "g2_4096x2048_f32_grad": Workload(
+        "g2_4096x2048_f32_grad", 4096, 2048, F32,
+        Params(tile=64, tokens_per_sample=1024, bit_budget=3.8, candidates=(3, 4), tau=2.0),
+        "activation gradients, fp32, 80/20 INT4/INT3 per 1024-token sample", 7),
+}
+
+# The fixed-point backward compressor's settings for the gradient workloads:
+# bits (6-8 in the paper's runs, 10 after its NaN event, 4 in App. H) and the
+# constant c of Eq. (24), here chosen so that a 1e-5 gradient is about 1/20 of
+# the largest representable value.
+NAIVE = {
+    "g1_8192x8192_bf16_grad": dict(bits=8, c=4096.0),
+    "g2_4096x2048_f32_grad": dict(bits=10, c=4096.0),
 }
 
 # Coverage variants: mixed allocations at other budgets, tau extremes.
@@ -182,6 +214,8 @@ def generate(name: str, seed: int = 0, tokens: int | None = None) -> np.ndarray:
         return gen_sparse_rows(T, H, w.dtype, seed, w.wid, 0.30, 8, 500.0)
     if w.wid == 5:
         return gen_gelu(T, H, w.dtype, seed, w.wid, _count(0.001, H), 200.0)
+    if w.wid in (6, 7):
+        return gen_gradients(T, H, w.dtype, seed, w.wid)
     raise KeyError(name)
 
 

@@ -116,3 +116,25 @@ def test_device_log2_tables_match_their_definition():
         a, b = math.log2(1 + j / 128), math.log2(1 + (j + 1) / 128)
         assert np.float32(vals[j]) == np.float32(a - 1.0), j
         assert np.float32(vals[128 + j]) == np.float32((b - a) / 65536.0), j
+
+
+def test_naive_sizes_match_oracle(ref):
+    for n, bits in ((0, 8), (1, 2), (31, 6), (32, 6), (33, 10), (4096 * 2048, 8), (1000, 16)):
+        assert tah.naive_payload_bytes(n, bits) == ref.naive_payload_bytes(n, bits)
+
+
+def test_naive_argument_errors_without_device():
+    L = tah.lib()
+    v = ctypes.c_void_p
+    need = tah.naive_payload_bytes(1000, 8)
+    enc = lambda g=16, dt=1, n=1000, bits=8, c=1.0, P=16, cap=need: L.tah_naive_encode(v(g), dt, n, bits, c, v(P), cap, v(0))
+    assert enc(bits=1) == 1 and enc(bits=17) == 1 and enc(c=0.0) == 1 and enc(c=-1.0) == 1
+    assert enc(c=math.inf) == 1 and enc(c=math.nan) == 1 and enc(c=3e38, bits=16) == 1  # c 2^15 overflows
+    assert enc(n=-1) == 1 and enc(g=0) == 1 and enc(g=8) == 1 and enc(P=0) == 1 and enc(dt=3) == 1
+    assert enc(cap=need - 1) == 3
+    dec = lambda P=16, ln=need, n=1000, bits=8, c=1.0, y=16, dt=0, ws=16, wcap=256: L.tah_naive_decode(
+        v(P), ln, n, bits, c, v(y), dt, v(ws), wcap, v(0))
+    assert dec(ln=need - 1) == 3 and dec(wcap=255) == 3
+    assert dec(P=0) == 1 and dec(y=0) == 1 and dec(ws=0) == 1 and dec(dt=2) == 1 and dec(bits=0) == 1
+    with pytest.raises(tah.TahError):
+        tah.naive_payload_bytes(10, 20)
