@@ -37,13 +37,15 @@ class _Params(ctypes.Structure):
         ("n_candidates", ctypes.c_int32),
         ("candidates", ctypes.c_uint8 * 4),
         ("tau", ctypes.c_float),
+        ("alloc_tile", ctypes.c_int32),
     ]
 
 
 class _Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("tokens", "hidden", "S", "nsamples", "M", "tiles", "tiles_per_sample", "nblocks")] + [
         (n, ctypes.c_int32) for n in ("G", "log2G", "b_lo", "b_hi")
-    ] + [(n, ctypes.c_int64) for n in ("k", "off_table", "off_bitmap", "off_side", "off_scale", "off_zero", "off_codes", "code_bytes", "total")]
+    ] + [(n, ctypes.c_int64) for n in ("k", "off_table", "off_bitmap", "off_side", "off_scale", "off_zero", "off_codes", "code_bytes", "total",
+                                  "A", "kA", "MA", "atiles", "atiles_per_sample")]
 
 
 def build(force: bool = False) -> str:
@@ -75,6 +77,8 @@ def lib():
         L.tahref_fwht.argtypes = [ctypes.c_void_p, ctypes.c_int]
         L.tahref_entropy.argtypes = [ctypes.c_void_p, ctypes.c_int]
         L.tahref_entropy.restype = ctypes.c_float
+        L.tahref_alloc_entropy.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+        L.tahref_alloc_entropy.restype = ctypes.c_float
         L.tahref_outlier.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_float, P(ctypes.c_int), P(ctypes.c_float), P(ctypes.c_float)]
         L.tahref_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, P(ctypes.c_float), P(ctypes.c_float), ctypes.c_void_p]
         L.tahref_dequantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
@@ -102,6 +106,7 @@ def _params(p) -> _Params:
     for i in range(4):
         c.candidates[i] = int(cands[i]) if i < len(cands) else 0
     c.tau = float(p.tau)
+    c.alloc_tile = int(getattr(p, "alloc_tile", 0))
     return c
 
 
@@ -141,6 +146,13 @@ def fwht(v: np.ndarray) -> np.ndarray:
 def entropy(alpha: np.ndarray) -> float:
     a = np.ascontiguousarray(alpha, dtype=np.float32)
     return float(np.float32(lib().tahref_entropy(_ptr(a), a.size)))
+
+
+def alloc_entropy(alpha: np.ndarray, G: int) -> float:
+    """Entropy of one allocation tile of alpha.size = kA * G channels."""
+    a = np.ascontiguousarray(alpha, dtype=np.float32)
+    assert a.size % G == 0
+    return float(np.float32(lib().tahref_alloc_entropy(_ptr(a), a.size, int(G))))
 
 
 def outlier(alpha: np.ndarray, tau: float):
@@ -204,7 +216,7 @@ def tile_stats(x: np.ndarray, p) -> dict:
     tokens, hidden = x.shape
     pl = plan(tokens, hidden, p)
     n = pl["tiles"]
-    H = np.zeros(n, np.float32)
+    H = np.zeros(pl["atiles"], np.float32)
     flag = np.zeros(n, np.uint8)
     piv = np.zeros(n, np.uint8)
     hi = np.zeros(n, np.uint8)

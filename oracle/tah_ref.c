@@ -88,12 +88,17 @@ static int ilog2(int v) {
 
 /*
  * Width pair and k (§3.2 "Top-p% tile selection"): the paper gives two widths,
- * INT4 for the top p% of a sample's tiles by entropy and INT3 for the rest.
- * Reading for a budget B over a candidate list: b_lo = largest candidate <= B,
- * b_hi = smallest candidate > B (b_lo if none), and p = (B - b_lo)/(b_hi - b_lo),
- * so k = floor(p * N) tiles of the N in a sample get b_hi and the average code
- * width never exceeds B. The budget counts code bits only; the paper quotes its
- * metadata bits separately (§3.4).
+ * INT4 for the top p% of a sample's allocation tiles by entropy and INT3 for
+ * the rest. Reading for a budget B over a candidate list: b_lo = largest
+ * candidate <= B, b_hi = smallest candidate > B (b_lo if none), and
+ * p = (B - b_lo)/(b_hi - b_lo), so k = floor(p * SM) of the SM allocation tiles
+ * of a sample get b_hi and the average code width never exceeds B. The budget
+ * counts code bits only; the paper quotes its metadata bits separately (§3.4).
+ *
+ * Allocation tile (§3.2 "Tile decomposition"): A channels, aligned with the
+ * quantization tiles, so A = kA * G; it must divide hidden. A = G is the
+ * paper's default, A = hidden its token-level special case. Every quantization
+ * tile takes the width of the allocation tile that holds it.
  */
 int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tahref_plan* o) {
   if (!p || !o) return TAHREF_ERR_INVALID_ARG;
@@ -112,6 +117,8 @@ int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tah
   if (p->tokens_per_sample < 0) return TAHREF_ERR_INVALID_ARG;
   int64_t S = p->tokens_per_sample == 0 ? tokens : p->tokens_per_sample;
   if (S > 0 && tokens % S) return TAHREF_ERR_INVALID_ARG;
+  int64_t A = p->alloc_tile == 0 ? G : p->alloc_tile;
+  if (A < G || A % G || hidden % A) return TAHREF_ERR_INVALID_ARG;
   if ((float)p->candidates[0] > p->bit_budget) return TAHREF_ERR_BUDGET_INFEASIBLE;
 
   int b_lo = p->candidates[0], b_hi = -1;
@@ -130,17 +137,22 @@ int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tah
   o->M = hidden / G;
   o->tiles = tokens * o->M;
   o->tiles_per_sample = S * o->M;
+  o->A = A;
+  o->kA = A / G;
+  o->MA = hidden / A;
+  o->atiles = tokens * o->MA;
+  o->atiles_per_sample = S * o->MA;
   o->b_lo = b_lo;
   o->b_hi = b_hi;
-  if (b_hi == b_lo || o->tiles_per_sample == 0) {
+  if (b_hi == b_lo || o->atiles_per_sample == 0) {
     o->k = 0;
   } else {
-    double kk = floor(((double)p->bit_budget - (double)b_lo) * (double)o->tiles_per_sample /
+    double kk = floor(((double)p->bit_budget - (double)b_lo) * (double)o->atiles_per_sample /
                       (double)(b_hi - b_lo));
     o->k = (int64_t)kk;
   }
   o->nblocks = (o->tiles + 63) / 64;
-  int64_t nhi = o->k * o->nsamples;
+  int64_t nhi = o->k * o->kA * o->nsamples; /* quantization tiles at b_hi */
   o->off_table = 256;
   o->off_bitmap = align256(o->off_table + 4 * o->nblocks);
   o->off_side = align256(o->off_bitmap + 8 * o->nblocks);
@@ -156,7 +168,7 @@ int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tah
 static void write_header(uint8_t* P, const tahref_plan* pl, const tahref_params* p, int x_dtype) {
   memset(P, 0, 256);
   put_u32(P, 0, 0x51484154u); /* "TAHQ" */
-  put_u16(P, 4, 1);
+  put_u16(P, 4, 2);
   put_u8(P, 6, (uint32_t)x_dtype);
   put_u8(P, 7, (uint32_t)pl->log2G);
   put_u64(P, 8, (uint64_t)pl->tokens);
@@ -177,6 +189,7 @@ static void write_header(uint8_t* P, const tahref_plan* pl, const tahref_params*
   put_u64(P, 96, (uint64_t)pl->off_zero);
   put_u64(P, 104, (uint64_t)pl->off_codes);
   put_u64(P, 112, (uint64_t)pl->total);
+  put_u32(P, 120, (uint32_t)pl->A);
 }
 
 /* ------------------------------------------------------------------ */
@@ -241,7 +254,7 @@ void tahref_fwht(float* v, int G) {
 }
 
 /*
- * Entropy of one allocation tile, Eq. (1)-(2):
+ * Entropy of a tile of G channels, Eq. (1)-(2):
  *   p_k = |a_k| / ||a||_1,   H = -sum_k p_k log2 p_k.
  * Reading: Eq. (2) as printed has no minus sign, but the text says H is high
  * for evenly spread energy and low for a sharp outlier, which is Shannon's
@@ -254,16 +267,46 @@ void tahref_fwht(float* v, int G) {
  *   L = sum |a_k| left to right; S = sum fmaf(|a_k|, log2s(|a_k|), S) left to
  *   right from 0; H = log2s(L) - S / L (L > 0), H = 0 (L = 0).
  */
-float tahref_entropy(const float* alpha, int G) {
+static void entropy_sums(const float* alpha, int n, float* L, float* S) {
   float l1 = 0.0f;
-  for (int k = 0; k < G; ++k) l1 = l1 + fabsf(alpha[k]);
-  float S = 0.0f;
-  for (int k = 0; k < G; ++k) {
+  for (int k = 0; k < n; ++k) l1 = l1 + fabsf(alpha[k]);
+  float s = 0.0f;
+  for (int k = 0; k < n; ++k) {
     const float a = fabsf(alpha[k]);
-    S = fmaf(a, tahref_log2s(a), S);
+    s = fmaf(a, tahref_log2s(a), s);
   }
-  if (!(l1 > 0.0f)) return 0.0f;
-  return tahref_log2s(l1) - S / l1;
+  *L = l1;
+  *S = s;
+}
+
+static float entropy_from_sums(float L, float S) {
+  if (!(L > 0.0f)) return 0.0f;
+  return tahref_log2s(L) - S / L;
+}
+
+float tahref_entropy(const float* alpha, int G) {
+  float L, S;
+  entropy_sums(alpha, G, &L, &S);
+  return entropy_from_sums(L, S);
+}
+
+/*
+ * Entropy of an allocation tile of A = kA * G channels (§3.2: the distribution
+ * of Eq. (1) is formed over all A channels). Same identity as above; the
+ * summation order is a reading (the pages fix none): L and S are first summed
+ * inside each of the kA quantization tiles as in tahref_entropy, then those
+ * partial sums are added left to right from 0. For A = G this is exactly
+ * tahref_entropy.
+ */
+float tahref_alloc_entropy(const float* alpha, int A, int G) {
+  float L = 0.0f, S = 0.0f;
+  for (int g = 0; g < A / G; ++g) {
+    float l, s;
+    entropy_sums(alpha + (int64_t)g * G, G, &l, &s);
+    L = L + l;
+    S = S + s;
+  }
+  return entropy_from_sums(L, S);
 }
 
 /*
@@ -393,19 +436,30 @@ static void load_tile(const void* x, int dtype, const tahref_plan* pl, int64_t t
   }
 }
 
-/* Entropy of every tile, then the per-sample selection. */
+/* Entropy of every allocation tile (H[atiles]), the per-sample selection over
+ * allocation tiles, and each quantization tile's width flag (hi[tiles]):
+ * allocation tile u of the tensor covers quantization tiles u*kA ... u*kA + kA - 1. */
 static int entropy_and_widths(const void* x, int dtype, const tahref_plan* pl, float* H, uint8_t* hi) {
-  float a[128];
-  for (int64_t t = 0; t < pl->tiles; ++t) {
-    load_tile(x, dtype, pl, t, a);
-    H[t] = tahref_entropy(a, pl->G);
+  float* a = (float*)malloc(sizeof(float) * (size_t)pl->A);
+  uint8_t* hiA = (uint8_t*)malloc((size_t)(pl->atiles + 1));
+  if (!a || !hiA) {
+    free(a);
+    free(hiA);
+    return TAHREF_ERR_INVALID_ARG;
   }
-  for (int64_t s = 0; s < pl->nsamples; ++s) {
-    int64_t first = s * pl->tiles_per_sample;
-    int rc = tahref_allocate(H + first, pl->tiles_per_sample, pl->k, hi + first);
-    if (rc) return rc;
+  for (int64_t u = 0; u < pl->atiles; ++u) {
+    for (int64_t g = 0; g < pl->kA; ++g) load_tile(x, dtype, pl, u * pl->kA + g, a + g * pl->G);
+    H[u] = tahref_alloc_entropy(a, (int)pl->A, pl->G);
   }
-  return TAHREF_OK;
+  int rc = TAHREF_OK;
+  for (int64_t s = 0; s < pl->nsamples && rc == TAHREF_OK; ++s) {
+    int64_t first = s * pl->atiles_per_sample;
+    rc = tahref_allocate(H + first, pl->atiles_per_sample, pl->k, hiA + first);
+  }
+  for (int64_t t = 0; t < pl->tiles; ++t) hi[t] = hiA[t / pl->kA];
+  free(a);
+  free(hiA);
+  return rc;
 }
 
 int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden, const tahref_params* p,
@@ -565,7 +619,7 @@ int tahref_decode(const uint8_t* P, size_t len, int64_t tokens, int64_t hidden, 
       for (int k = 0; k < pl.G; ++k) yh[base + k] = f32_to_bf16_rne(xhat[k]);
     }
   }
-  if (hi_count != pl.k * pl.nsamples) return TAHREF_ERR_BAD_PAYLOAD;
+  if (hi_count != pl.k * pl.kA * pl.nsamples) return TAHREF_ERR_BAD_PAYLOAD;
   return TAHREF_OK;
 }
 

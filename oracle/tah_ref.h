@@ -40,20 +40,24 @@ enum {
 
 /* Codec parameters (paper notation in brackets). */
 typedef struct {
-  int32_t tile;              /* G = A: quantization tile = allocation tile (§3.1, §3.2) */
+  int32_t tile;              /* G: quantization tile (§3.1) */
   int32_t tokens_per_sample; /* S: ranking scope of the top-p% selection; 0 = all tokens (§3.2) */
   float bit_budget;          /* average code bits per element per sample, metadata excluded */
   int32_t n_candidates;      /* number of candidate widths, 1..4 */
   uint8_t candidates[4];     /* strictly increasing, each 1..8 */
   float tau;                 /* outlier threshold tau of Eq. (3); 0 = always, +inf = never (App. F) */
+  int32_t alloc_tile;        /* A: allocation tile (§3.2), a multiple of G dividing hidden; 0 = G */
 } tahref_params;
 
 /* Derived sizes and the payload section layout. */
 typedef struct {
   int64_t tokens, hidden, S, nsamples, M, tiles, tiles_per_sample, nblocks;
   int32_t G, log2G, b_lo, b_hi;
-  int64_t k; /* tiles per sample that get b_hi */
+  int64_t k; /* allocation tiles per sample that get b_hi */
   int64_t off_table, off_bitmap, off_side, off_scale, off_zero, off_codes, code_bytes, total;
+  /* allocation tiles (§3.2): A channels = kA quantization tiles; MA = hidden / A per
+   * token (the paper's M); atiles in all, atiles_per_sample = S * MA per sample */
+  int64_t A, kA, MA, atiles, atiles_per_sample;
 } tahref_plan;
 
 int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tahref_plan* out);
@@ -62,6 +66,7 @@ int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tah
 float tahref_log2s(float u);
 void tahref_fwht(float* v, int G);
 float tahref_entropy(const float* alpha, int G);
+float tahref_alloc_entropy(const float* alpha, int A, int G);
 int tahref_outlier(const float* alpha, int G, float tau, int* d, float* m1, float* m2);
 void tahref_quantize(const float* y, int G, int b, float* lo, float* s, uint32_t* q);
 void tahref_dequantize(const uint32_t* q, int G, float s, float lo, int flag, int d, float* xhat);
@@ -72,6 +77,7 @@ int tahref_encode(const void* x, int x_dtype, int64_t tokens, int64_t hidden, co
                   uint8_t* payload, size_t payload_cap);
 int tahref_decode(const uint8_t* payload, size_t payload_len, int64_t tokens, int64_t hidden,
                   const tahref_params* p, void* y, int y_dtype);
+/* H: one entropy per allocation tile (atiles); the other outputs one per quantization tile. */
 int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden, const tahref_params* p,
                       float* H, uint8_t* flag, uint8_t* pivot, uint8_t* hi, float* lo, float* scale);
 

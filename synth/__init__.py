@@ -27,14 +27,16 @@ BF16 = 1
 
 @dataclasses.dataclass(frozen=True)
 class Params:
-    """Codec parameters: tile G (= allocation tile A), ranking scope S in tokens
-    (0 = all), average code-bit budget, candidate widths and outlier threshold tau."""
+    """Codec parameters: quantization tile G, ranking scope S in tokens (0 = all),
+    average code-bit budget, candidate widths, outlier threshold tau and
+    allocation tile A in channels (0 = G)."""
 
     tile: int = 64
     tokens_per_sample: int = 0
     bit_budget: float = 3.8
     candidates: tuple = (3, 4)
     tau: float = 2.0
+    alloc_tile: int = 0
 
 
 @dataclasses.dataclass(frozen=True)

@@ -539,3 +539,117 @@ def test_naive_payload_size_and_padding(ref):
         P = ref.naive_encode(g, bits, 1.0)
         used = 256 + (n * bits + 7) // 8
         assert not P[used:].any()
+
+
+# ---------------------------------------------------------------- allocation tiles (A = kA * G) ----
+def shannon64(a):
+    p = np.abs(np.asarray(a, np.float64))
+    return float(scipy.stats.entropy(p / p.sum(), base=2)) if p.sum() > 0 else 0.0
+
+
+def test_alloc_entropy_grouping_identity(ref):
+    # Sec. 3.2 forms Eq. (1) over all A channels. Grouping property of Shannon
+    # entropy: kA copies of one tile spread the mass evenly over kA blocks, so
+    # H(A-tile) = H(G-tile) + log2(kA); a zero block adds nothing.
+    g = np.random.default_rng(23)
+    for G in (32, 64):
+        for kA in (2, 3, 4, 5, 16):
+            t = (g.standard_normal(G) * np.exp(g.standard_normal())).astype(np.float32)
+            rep = np.tile(t, kA)
+            want = shannon64(t) + math.log2(kA)
+            assert abs(ref.alloc_entropy(rep, G) - want) <= entropy_tol(rep), (G, kA)
+            z = np.concatenate([t, np.zeros(G * (kA - 1), np.float32)])
+            assert abs(ref.alloc_entropy(z, G) - shannon64(t)) <= entropy_tol(z), (G, kA)
+
+
+def test_alloc_entropy_matches_scipy_and_reduces_to_tile_entropy(ref):
+    g = np.random.default_rng(29)
+    for G in (32, 64, 128):
+        for kA in (1, 2, 3, 8, 64):
+            a = (g.standard_normal(G * kA) * np.exp(g.standard_normal())).astype(np.float32)
+            a[g.integers(0, a.size)] *= 80
+            assert abs(ref.alloc_entropy(a, G) - shannon64(a)) <= entropy_tol(a), (G, kA)
+            # block order does not matter beyond rounding; signs not at all
+            blocks = a.reshape(kA, G)[::-1].ravel()
+            assert abs(ref.alloc_entropy(-blocks, G) - shannon64(a)) <= entropy_tol(a)
+        # A = G is the quantization-tile entropy itself
+        a = g.standard_normal(G).astype(np.float32)
+        assert ref.alloc_entropy(a, G) == ref.entropy(a)
+    # uniform magnitudes over A channels: log2 A; one spike in A channels: 0
+    u = np.full(64 * 48, -0.25, np.float32)
+    assert abs(ref.alloc_entropy(u, 64) - math.log2(u.size)) <= entropy_tol(u)
+    s = np.zeros(64 * 48, np.float32)
+    s[1000] = 3.0
+    assert abs(ref.alloc_entropy(s, 64)) <= 4 * 2.0**-24 * math.log2(3.0)
+    assert ref.alloc_entropy(np.zeros(256, np.float32), 64) == 0.0
+
+
+@pytest.mark.parametrize("A,S", [(128, 0), (256, 4), (512, 0), (1536, 2), (3072, 0)])
+def test_alloc_tile_selection_brute_force(ref, A, S):
+    # widths against an fp64 ranking of the allocation tiles of each sample; A =
+    # hidden is the token-level allocation of Sec. 3.2. The random entropies are
+    # far apart compared with the fp32 error, so the fp64 top-k is the oracle's.
+    G, tokens, hidden = 64, 16, 3072
+    p = synth.Params(tile=G, tokens_per_sample=S, bit_budget=3.3, candidates=(3, 4), tau=2.0, alloc_tile=A)
+    x = synth.random_tensor(tokens, hidden, synth.F32, 31, n_out=40, mult=50)
+    pl = ref.plan(tokens, hidden, p)
+    kA, NA = A // G, pl["atiles_per_sample"]
+    assert (pl["A"], pl["kA"], pl["MA"], pl["atiles"]) == (A, kA, hidden // A, tokens * hidden // A)
+    assert pl["k"] == math.floor(0.3 * NA + 1e-9)
+    st = ref.tile_stats(x, p)
+    assert st["H"].size == pl["atiles"]
+    Hx = np.array([shannon64(r) for r in x.reshape(-1, A)])
+    for u in range(pl["atiles"]):
+        assert abs(st["H"][u] - Hx[u]) <= entropy_tol(x.reshape(-1, A)[u])
+    hi = st["hi"].reshape(-1, kA)
+    assert np.all(hi == hi[:, :1])  # one width per allocation tile
+    for s in range(pl["nsamples"]):
+        Hs = Hx[s * NA:(s + 1) * NA]
+        order = np.argsort(-Hs, kind="stable")
+        k = pl["k"]
+        if 0 < k < NA:
+            assert Hs[order[k - 1]] - Hs[order[k]] > 1e-4  # no near-ties at the cut
+        want = np.zeros(NA, np.uint8)
+        want[order[:k]] = 1
+        assert np.array_equal(hi[s * NA:(s + 1) * NA, 0], want), s
+
+
+def test_token_level_allocation_plan_and_payload(ref):
+    # 8192 x 8192 at G = 64, A = C (token level), the pages' 80/20 split over the
+    # 8192 tokens: 6553 tokens of 128 tiles each get 4 bits.
+    p = synth.Params(tile=64, tokens_per_sample=0, bit_budget=3.8, candidates=(3, 4), alloc_tile=8192)
+    pl = ref.plan(8192, 8192, p)
+    assert (pl["kA"], pl["MA"], pl["atiles_per_sample"], pl["k"]) == (128, 1, 8192, 6553)
+    assert pl["code_bytes"] == 1048576 * 24 + 6553 * 128 * 8
+    # small tensor: header records A; the bitmap holds one run per upgraded token
+    p = synth.Params(tile=32, tokens_per_sample=8, bit_budget=3.5, candidates=(3, 4), alloc_tile=256)
+    x = synth.random_tensor(32, 256, synth.F32, 37, n_out=6, mult=30)
+    P = ref.encode(x, p)
+    pl = ref.plan(32, 256, p)
+    assert P[4] == 2 and P[5] == 0 and int(P[120:124].view(np.uint32)[0]) == 256
+    bm = np.unpackbits(P[pl["off_bitmap"]:pl["off_bitmap"] + 4 * ((pl["tiles"] + 31) // 32)], bitorder="little")
+    rows = bm[:pl["tiles"]].reshape(32, 8)
+    assert np.all(rows == rows[:, :1])
+    assert np.all(rows[:, 0].reshape(4, 8).sum(1) == pl["k"]) and pl["k"] == 4
+    # A = G spelled out is the same codec as the default
+    q = synth.Params(tile=32, tokens_per_sample=8, bit_budget=3.5, candidates=(3, 4))
+    x2 = synth.random_tensor(32, 256, synth.F32, 38, n_out=6, mult=30)
+    assert np.array_equal(ref.encode(x2, q), ref.encode(x2, synth.Params(**{**q.__dict__, "alloc_tile": 32})))
+    y = ref.decode(P, 32, 256, p)
+    assert np.abs(y - x).max() < np.abs(x).max() / 2  # decodes
+
+
+def test_alloc_tile_errors(ref):
+    base = dict(tile=64, bit_budget=3.5, candidates=(3, 4))
+    for A in (32, 96, 200, 640, -64):  # below G, not a multiple of G, not dividing hidden = 512
+        with pytest.raises(ref.OracleError) as e:
+            ref.plan(4, 512, synth.Params(**base, alloc_tile=A))
+        assert e.value.code == 1, A
+    for A in (0, 64, 128, 256, 512):
+        ref.plan(4, 512, synth.Params(**base, alloc_tile=A))
+    # a payload made for one A does not decode as another
+    x = synth.random_tensor(4, 512, synth.F32, 41)
+    P = ref.encode(x, synth.Params(**base, alloc_tile=128))
+    with pytest.raises(ref.OracleError) as e:
+        ref.decode(P, 4, 512, synth.Params(**base, alloc_tile=256))
+    assert e.value.code == 5
