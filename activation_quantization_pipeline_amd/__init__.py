@@ -61,13 +61,15 @@ class TahError(RuntimeError):
 @dataclasses.dataclass(frozen=True)
 class TahParams:
     """Codec parameters (see tah_params_t): tile G, ranking scope S in tokens
-    (0 = all tokens), average code-bit budget, candidate widths, outlier tau."""
+    (0 = all tokens), average code-bit budget, candidate widths, outlier tau,
+    allocation tile A in channels (0 = G)."""
 
     tile: int = 64
     tokens_per_sample: int = 0
     bit_budget: float = 3.8
     candidates: tuple = (3, 4)
     tau: float = 2.0
+    alloc_tile: int = 0
 
 
 class _CParams(ctypes.Structure):
@@ -78,6 +80,7 @@ class _CParams(ctypes.Structure):
         ("n_candidates", ctypes.c_int32),
         ("candidates", ctypes.c_uint8 * 4),
         ("tau", ctypes.c_float),
+        ("alloc_tile", ctypes.c_int32),
     ]
 
 
@@ -93,10 +96,12 @@ def _cparams(p) -> _CParams:
     for i in range(4):
         c.candidates[i] = cands[i] if i < len(cands) else 0
     c.tau = float(p.tau)
+    c.alloc_tile = int(getattr(p, "alloc_tile", 0))
     return c
 
 
 _lib = None
+ABI_VERSION = 2  # TAH_ABI_VERSION of include/tah.h
 
 
 def lib() -> ctypes.CDLL:
@@ -133,6 +138,8 @@ def lib() -> ctypes.CDLL:
         L.tah_status_string.restype = ctypes.c_char_p
         L.tah_abi_version.argtypes = []
         L.tah_abi_version.restype = ctypes.c_int
+        if L.tah_abi_version() != ABI_VERSION:  # a stale build would misread tah_params_t
+            raise ImportError(f"{LIB_PATH} has ABI version {L.tah_abi_version()}, expected {ABI_VERSION}: rebuild it")
         _lib = L
     return _lib
 
@@ -186,7 +193,8 @@ def workspace_entropy_offset(tokens: int, hidden: int, p) -> int:
 def params_default() -> TahParams:
     c = _CParams()
     lib().tah_params_default(ctypes.byref(c))
-    return TahParams(c.tile, c.tokens_per_sample, c.bit_budget, tuple(c.candidates[: c.n_candidates]), c.tau)
+    return TahParams(c.tile, c.tokens_per_sample, c.bit_budget, tuple(c.candidates[: c.n_candidates]), c.tau,
+                     c.alloc_tile)
 
 
 def abi_version() -> int:
@@ -263,10 +271,11 @@ def roundtrip(x: torch.Tensor, p, y_dtype: torch.dtype | None = None, payload: t
 
 def tile_entropy(x: torch.Tensor, p, h: torch.Tensor | None = None, ws: torch.Tensor | None = None,
                  stream=None) -> torch.Tensor:
-    """tah_tile_entropy: fp32 entropy of each of the tokens*hidden/G tiles."""
+    """tah_tile_entropy: fp32 entropy of each of the tokens*hidden/A allocation tiles."""
     tokens, hidden = _shape(x)
     if h is None:
-        h = torch.empty(tokens * (hidden // int(p.tile)), dtype=torch.float32, device=x.device)
+        A = int(getattr(p, "alloc_tile", 0)) or int(p.tile)
+        h = torch.empty(tokens * (hidden // A), dtype=torch.float32, device=x.device)
     if ws is None:
         ws = alloc_workspace(tokens, hidden, p, x.device)
     cp = _cparams(p)

@@ -41,6 +41,8 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
     return TAH_ERR_INVALID_ARG;
   const int64_t S = p->tokens_per_sample == 0 ? tokens : p->tokens_per_sample;
   if (S > 0 && tokens % S) return TAH_ERR_INVALID_ARG;
+  const int64_t A = p->alloc_tile == 0 ? G : p->alloc_tile;
+  if (A < G || A % G || hidden % A) return TAH_ERR_INVALID_ARG;
   if ((float)p->candidates[0] > p->bit_budget) return TAH_ERR_BUDGET_INFEASIBLE;
   // tile indices of a sample and block-table counts are 32-bit on the device
   const int64_t M = hidden / G;
@@ -61,7 +63,10 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   o->nsamples = S > 0 ? tokens / S : 0;
   o->M = M;
   o->tiles = tokens * M;
-  o->N = S * M;
+  o->A = A;
+  o->kA = A / G;
+  o->atiles = tokens * (hidden / A);
+  o->N = S * (hidden / A);
   o->G = G;
   o->log2G = ilog2(G);
   o->b_lo = b_lo;
@@ -75,7 +80,7 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   for (int i = 0; i < 4; ++i) o->candidates[i] = i < p->n_candidates ? p->candidates[i] : 0;
   o->nblocks = (o->tiles + 63) / 64;
 
-  const int64_t nhi = o->k * o->nsamples;
+  const int64_t nhi = o->k * o->kA * o->nsamples;  // quantization tiles at b_hi
   o->off_table = 256;
   o->off_bitmap = align256(o->off_table + 4 * o->nblocks);
   o->off_side = align256(o->off_bitmap + 8 * o->nblocks);
@@ -93,8 +98,10 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   w = align256(w + 2 * (int64_t)sizeof(SampleState) * (mixed ? o->nsamples : 0));
   o->ws_hist = w;  // three rotating histograms per sample
   w = align256(w + 3 * 4 * kBins * (mixed ? o->nsamples : 0));
-  o->ws_H = w;
-  w = align256(w + 4 * o->tiles);
+  o->ws_H = w;  // entropy of each allocation tile
+  w = align256(w + 4 * o->atiles);
+  o->ws_LS = w;  // per-quantization-tile sums (L, S) when an allocation tile spans several
+  w = align256(w + 8 * (o->kA > 1 ? o->tiles : 0));
   o->ws_blockcnt = w;
   w = align256(w + 4 * (mixed ? o->nblocks : 0));
   o->ws_table = w;
@@ -122,7 +129,8 @@ void make_header(const Plan& pl, Header* h) {
   memset(b, 0, sizeof(b));
   auto put = [&](int off, const void* src, int n) { memcpy(b + off, src, n); };
   const uint32_t magic = 0x51484154u;  // "TAHQ"
-  const uint16_t ver = 1;
+  const uint16_t ver = 2;
+  const uint32_t A = (uint32_t)pl.A;
   const uint8_t dt = (uint8_t)pl.x_dtype, lg = (uint8_t)pl.log2G;
   put(0, &magic, 4);
   put(4, &ver, 2);
@@ -147,6 +155,7 @@ void make_header(const Plan& pl, Header* h) {
   put(96, &pl.off_zero, 8);
   put(104, &pl.off_codes, 8);
   put(112, &pl.total, 8);
+  put(120, &A, 4);
   memcpy(h->w, b, 128);
 }
 
@@ -193,11 +202,17 @@ static tah_status_t run_encode(const void* x, tah_dtype_t x_dtype, int64_t token
   pl.x_dtype = x_dtype;
   hipStream_t st = static_cast<hipStream_t>(stream);
   const bool mixed = pl.k > 0;
+  uint8_t* w = static_cast<uint8_t*>(ws);
   if (mixed && pl.tiles > 0) {
-    uint8_t* w = static_cast<uint8_t*>(ws);
     hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, true, st);
     if (e != hipSuccess) return hip_status(e);
     e = launch_select(pl, payload, ws, st);
+    if (e != hipSuccess) return hip_status(e);
+  } else if (pl.kA > 1 && pl.tiles > 0) {
+    // no selection, but the workspace still receives the allocation-tile
+    // entropies; the encoder's own per-quantization-tile entropies then go to
+    // the (by then consumed) partial-sum area
+    hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, false, st);
     if (e != hipSuccess) return hip_status(e);
   }
   return hip_status(launch_encode(pl, x, payload, want_y ? y : nullptr, y_dtype, ws, st, mixed && pl.tiles > 0));

@@ -145,8 +145,9 @@ __device__ __forceinline__ float log2_full(float x, const float* lt) {
 // (equal to -sum p_k log2 p_k with p_k = |a_k| / L). fp32 order: S summed
 // left to right with fmaf from 0, then log2(L) - S / L; L = 0 gives 0.
 // NODE: the tile's values are widened bf16 (log2_node applies).
+// S = sum_k |a_k| log2 |a_k| of one tile, fma-accumulated left to right from 0.
 template <int G, bool NODE>
-__device__ __forceinline__ float tile_entropy(const float (&v)[G], float l1, const float* lt) {
+__device__ __forceinline__ float tile_logsum(const float (&v)[G], const float* lt) {
   float S = 0.0f;
 #pragma unroll
   for (int k = 0; k < G; ++k) {
@@ -154,6 +155,12 @@ __device__ __forceinline__ float tile_entropy(const float (&v)[G], float l1, con
     S = __builtin_fmaf(fabsf(v[k]), lg, S);
   }
   asm volatile("" : "+v"(S));  // the sum is complete here, ahead of the L = 0 test
+  return S;
+}
+
+template <int G, bool NODE>
+__device__ __forceinline__ float tile_entropy(const float (&v)[G], float l1, const float* lt) {
+  const float S = tile_logsum<G, NODE>(v, lt);
   return l1 > 0.0f ? log2_full(l1, lt) - S / l1 : 0.0f;
 }
 

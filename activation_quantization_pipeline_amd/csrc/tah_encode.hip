@@ -489,7 +489,9 @@ hipError_t launch_encode(const Plan& pl, const void* x, void* payload, void* y, 
     a.table = nullptr;
     a.bitmap = nullptr;
   }
-  a.H = reinterpret_cast<float*>(w + pl.ws_H);
+  // the uniform-width kernel writes quantization-tile entropies: the entropy
+  // area when allocation tiles are quantization tiles, else the sum area
+  a.H = reinterpret_cast<float*>(w + (pl.kA > 1 ? pl.ws_LS : pl.ws_H));
   a.tiles = pl.tiles;
   a.off_side = pl.off_side;
   a.off_scale = pl.off_scale;

@@ -23,9 +23,11 @@ struct SelectPass {
 };
 
 struct Plan {
-  int64_t tokens, hidden, S, nsamples, M, tiles, N, nblocks;
+  int64_t tokens, hidden, S, nsamples, M, tiles, nblocks;
   int32_t G, log2G, b_lo, b_hi;
-  int64_t k;  // tiles per sample with b_hi
+  // allocation tiles (§3.2): A = kA * G channels, atiles in all, N per sample
+  int64_t A, kA, atiles, N;
+  int64_t k;  // allocation tiles per sample with b_hi
   int32_t x_dtype;
   float tau, budget;
   int32_t n_candidates;
@@ -33,7 +35,7 @@ struct Plan {
   // payload layout
   int64_t off_table, off_bitmap, off_side, off_scale, off_zero, off_codes, code_bytes, total;
   // workspace layout
-  int64_t ws_status, ws_state, ws_hist, ws_H, ws_blockcnt, ws_table, ws_bitmap, ws_total;
+  int64_t ws_status, ws_state, ws_hist, ws_H, ws_LS, ws_blockcnt, ws_table, ws_bitmap, ws_total;
   int32_t npasses;
   SelectPass passes[kMaxPasses];
 };
@@ -60,6 +62,7 @@ struct PadRanges {
 // Launchers (return hipSuccess or the launch error).
 hipError_t launch_encode(const Plan& pl, const void* x, void* payload, void* y, int y_dtype, void* ws,
                          hipStream_t st, bool mixed);
+// Entropy of every allocation tile into h_out (pl.atiles values).
 hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, bool init_select, hipStream_t st);
 hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st);
 hipError_t launch_decode(const Plan& pl, const void* payload, void* y, int y_dtype, void* ws, hipStream_t st);

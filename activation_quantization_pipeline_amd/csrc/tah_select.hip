@@ -5,7 +5,10 @@
 // O(SM log SM) ranking), the k-th largest key is found by a radix select:
 //   k_stats  - one lane per tile computes the entropy of Eq. (1)-(2) from the
 //              LDS-staged tile and writes it to the workspace; it also resets
-//              the selection state and histograms;
+//              the selection state and histograms. When an allocation tile
+//              spans kA > 1 quantization tiles, the lane writes the tile's two
+//              sums (L, S) instead and k_alloc_entropy adds them up per
+//              allocation tile, left to right, into its entropy;
 //   k_hist   - one launch per digit pass. Each workgroup first applies the
 //              previous pass (one wavefront scans that pass's histogram of the
 //              sample in order and finds the digit that holds rank r), then
@@ -21,8 +24,9 @@
 //              device-scope release per workgroup, which on this multi-die part
 //              writes back the L2;
 //   k_pick   - applies the last pass: the final threshold state per sample;
-//   k_mark   - one bit per tile: key above the threshold, or equal to it with
-//              an index up to the last selected tie; per-64-tile counts;
+//   k_mark   - one bit per quantization tile, from its allocation tile: key
+//              above the threshold, or equal to it with an index up to the last
+//              selected tie; per-64-tile counts;
 //   k_table  - exclusive scan of those counts: b_hi tiles before each run of
 //              64 tiles, which locates every variable-width code block.
 #include <type_traits>
@@ -41,7 +45,8 @@ __device__ __forceinline__ uint32_t orderable(float f) {
 // ------------------------------------------------------------------ stats ----
 struct StatsArgs {
   const uint8_t* x;
-  float* h;
+  float* h;     // entropy per tile (allocation tile = quantization tile)
+  float2* ls;   // (L, S) per tile (allocation tile of several quantization tiles)
   uint32_t* hist;
   int64_t tiles, hist_words;
   int32_t init;
@@ -52,7 +57,7 @@ constexpr int stats_tiles_per_wg() {
   return TileRow<G, TIn>::kBytes <= 128 ? 256 : (TileRow<G, TIn>::kBytes <= 256 ? 128 : 64);
 }
 
-template <int G, typename TIn>
+template <int G, typename TIn, bool SUMS>
 __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsArgs a) {
   constexpr int NT = stats_tiles_per_wg<G, TIn>();
   using RI = TileRow<G, TIn>;
@@ -75,15 +80,40 @@ __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsA
     float l1 = 0.0f;
 #pragma unroll
     for (int k = 0; k < G; ++k) l1 = l1 + fabsf(v[k]);
-    a.h[t0 + tid] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);  // Eq. (1)-(2)
+    if constexpr (SUMS)
+      a.ls[t0 + tid] = make_float2(l1, tile_logsum<G, Elem<TIn>::kBytes == 2>(v, lt));
+    else
+      a.h[t0 + tid] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);  // Eq. (1)-(2)
   }
 }
 
+// Entropy of each allocation tile u of kA quantization tiles (u * kA ...
+// u * kA + kA - 1): their sums added left to right from 0, then the identity
+// H = log2 L - S / L.
+__global__ __launch_bounds__(256) void k_alloc_entropy(const float2* ls, float* h, int64_t atiles, int64_t kA) {
+  __shared__ __attribute__((aligned(16))) float lt[256];
+  load_log2_tab(lt);
+  __syncthreads();
+  const int64_t u = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (u >= atiles) return;
+  const float2* p = ls + u * kA;
+  float L = 0.0f, S = 0.0f;
+  for (int64_t g = 0; g < kA; ++g) {
+    const float2 q = p[g];
+    L = L + q.x;
+    S = S + q.y;
+  }
+  h[u] = entropy_from_sums(L, S, lt);
+}
+
 template <int G, typename TIn>
-static hipError_t launch_stats_t(const StatsArgs& a, hipStream_t st) {
+static hipError_t launch_stats_t(const StatsArgs& a, bool sums, hipStream_t st) {
   constexpr int NT = stats_tiles_per_wg<G, TIn>();
   const int64_t nwg = a.tiles > 0 ? (a.tiles + NT - 1) / NT : 1;
-  hipLaunchKernelGGL((k_stats<G, TIn>), dim3((unsigned)nwg), dim3(NT), 0, st, a);
+  if (sums)
+    hipLaunchKernelGGL((k_stats<G, TIn, true>), dim3((unsigned)nwg), dim3(NT), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_stats<G, TIn, false>), dim3((unsigned)nwg), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
@@ -92,17 +122,23 @@ hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, b
   StatsArgs a;
   a.x = static_cast<const uint8_t*>(x);
   a.h = h_out;
+  a.ls = reinterpret_cast<float2*>(w + pl.ws_LS);
   a.hist = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
   a.tiles = pl.tiles;
   a.hist_words = pl.k > 0 ? pl.nsamples * kBins : 0;
   a.init = init_select ? 1 : 0;
-  const bool bf = pl.x_dtype == TAH_DTYPE_BF16;
+  const bool bf = pl.x_dtype == TAH_DTYPE_BF16, sums = pl.kA > 1;
+  hipError_t e;
   switch (pl.G) {
-    case 32: return bf ? launch_stats_t<32, bf16_t>(a, st) : launch_stats_t<32, float>(a, st);
-    case 64: return bf ? launch_stats_t<64, bf16_t>(a, st) : launch_stats_t<64, float>(a, st);
-    case 128: return bf ? launch_stats_t<128, bf16_t>(a, st) : launch_stats_t<128, float>(a, st);
+    case 32: e = bf ? launch_stats_t<32, bf16_t>(a, sums, st) : launch_stats_t<32, float>(a, sums, st); break;
+    case 64: e = bf ? launch_stats_t<64, bf16_t>(a, sums, st) : launch_stats_t<64, float>(a, sums, st); break;
+    case 128: e = bf ? launch_stats_t<128, bf16_t>(a, sums, st) : launch_stats_t<128, float>(a, sums, st); break;
     default: return hipErrorInvalidValue;
   }
+  if (e != hipSuccess || !sums || pl.atiles == 0) return e;
+  hipLaunchKernelGGL(k_alloc_entropy, dim3((unsigned)((pl.atiles + 255) / 256)), dim3(256), 0, st,
+                     (const float2*)a.ls, h_out, pl.atiles, pl.kA);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------ hist ----
@@ -269,11 +305,11 @@ __global__ __launch_bounds__(64) void k_pick(HistArgs a) {
 
 // ------------------------------------------------------------------ mark ----
 struct MarkArgs {
-  const float* H;
+  const float* H;  // per allocation tile
   const SampleState* st;
   uint32_t* bitmap;
   uint32_t* blockcnt;
-  int64_t tiles, N, nblocks;
+  int64_t tiles, N, nblocks, kA;
 };
 
 __global__ __launch_bounds__(256) void k_mark(MarkArgs a) {
@@ -281,9 +317,10 @@ __global__ __launch_bounds__(256) void k_mark(MarkArgs a) {
   const int64_t t = (int64_t)blockIdx.x * 256 + tid;
   bool sel = false;
   if (t < a.tiles) {
-    const int64_t s = t / a.N;
-    const uint32_t u = (uint32_t)(t - s * a.N);
-    const uint32_t key = orderable(a.H[t]);
+    const int64_t ta = a.kA == 1 ? t : t / a.kA;  // allocation tile
+    const int64_t s = ta / a.N;
+    const uint32_t u = (uint32_t)(ta - s * a.N);
+    const uint32_t key = orderable(a.H[ta]);
     const SampleState S = a.st[s];
     sel = key > S.key || (key == S.key && u <= S.upos);
   }
@@ -398,6 +435,7 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   m.tiles = pl.tiles;
   m.N = pl.N;
   m.nblocks = pl.nblocks;
+  m.kA = pl.kA;
   hipLaunchKernelGGL(k_mark, dim3((unsigned)((pl.tiles + 255) / 256)), dim3(256), 0, st, m);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -20,8 +20,10 @@ achievable bandwidth, and the CPU oracle on the host (single thread).
 """
 
 import argparse
+import dataclasses
 import hashlib
 import json
+import math
 import os
 import statistics
 import sys
@@ -197,6 +199,27 @@ def main():
         extras["mixed_80_20_roundtrip_gbps"] = round((2 * x_bytes + cm.payload_bytes) / (m_ms * 1e-3) / 1e9, 1)
         extras["mixed_80_20_ms_per_step"] = round(m_ms, 5)
         del pm, wsm
+        # allocation tiles of several quantization tiles (Sec. 3.2), up to token-level
+        # allocation (A = hidden), at the same 80/20 split
+        for label, A in (("alloc256", 256), ("alloc_token", C)):
+            ca = tah.Codec(T, C, dataclasses.replace(wm.params, alloc_tile=A), torch.bfloat16, torch.bfloat16)
+            pa = [torch.empty(ca.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+            wsa = torch.empty(ca.workspace_bytes, dtype=torch.uint8, device=dev)
+            a_ms, _, _, _ = time_launches(torch, lambda i: ca.roundtrip(xs[i], pa[i], ys[i], wsa, stream_h), n_sets,
+                                          args.steps, args.warmup)
+            extras[f"mixed_80_20_{label}_roundtrip_gbps"] = round((2 * x_bytes + ca.payload_bytes) / (a_ms * 1e-3) / 1e9,
+                                                                 1)
+            del pa, wsa
+        # the outlier thresholds of App. F on the headline configuration (tau = 2 is the headline)
+        taus = {"2.0": round(value, 1)}
+        for tau in (0.0, 4.0, math.inf):
+            ct = tah.Codec(T, C, dataclasses.replace(p, tau=tau), torch.bfloat16, torch.bfloat16)
+            pt = [torch.empty(ct.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+            t_ms, _, _, _ = time_launches(torch, lambda i: ct.roundtrip(xs[i], pt[i], ys[i], ws, stream_h), n_sets,
+                                          args.steps, args.warmup)
+            taus[str(tau)] = round(bytes_step / (t_ms * 1e-3) / 1e9, 1)
+            del pt
+        extras["tau_sweep_roundtrip_gbps"] = taus
         # the backward path (Algorithm 1 lines 6-7): activation gradients of the same shape,
         # fixed-point compressor at 8 bits with the scaling of Eq. (24), and TAH-Quant at 4 bits
         gname = "g1_8192x8192_bf16_grad"

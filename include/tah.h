@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define TAH_ABI_VERSION 1
+#define TAH_ABI_VERSION 2
 
 typedef enum { TAH_DTYPE_F32 = 0, TAH_DTYPE_BF16 = 1 } tah_dtype_t;
 
@@ -53,20 +53,26 @@ typedef enum {
 
 /*
  * Codec parameters.
- *   tile: G, the quantization tile (§3.1) and allocation tile A = G (§3.2,
- *     the paper's default). A power of two dividing hidden; the GPU kernels are
- *     built for 32, 64 and 128 (the format allows 8..128).
+ *   tile: G, the quantization tile (§3.1). A power of two dividing hidden;
+ *     the GPU kernels are built for 32, 64 and 128 (the format allows 8..128).
  *   tokens_per_sample: S, the ranking scope of the top-p% selection (§3.2:
  *     tiles are ranked within each sample); 0 = all tokens form one sample.
  *     tokens % S must be 0.
  *   bit_budget: average code bits per element of each sample, metadata
  *     excluded. The two candidates around it, b_lo <= budget < b_hi, are used:
- *     the k = floor((budget - b_lo) * N / (b_hi - b_lo)) highest-entropy tiles
- *     of a sample (N tiles) get b_hi, the rest b_lo (§3.2, INT4 for the top p%,
- *     INT3 for the rest).
+ *     the k = floor((budget - b_lo) * N / (b_hi - b_lo)) highest-entropy
+ *     allocation tiles of a sample (N = S * hidden / A of them) get b_hi, the
+ *     rest b_lo (§3.2, INT4 for the top p%, INT3 for the rest). Equal entropies
+ *     rank the lower allocation-tile index first.
  *   n_candidates, candidates: 1..4 widths, strictly increasing, each 1..8.
  *   tau: outlier threshold of Eq. (3) (§3.3, default 2.0); 0 transforms every
  *     non-zero tile, +INFINITY none (Appendix F). Must be >= 0 and not NaN.
+ *   alloc_tile: A, the allocation tile of the bit allocation in channels (§3.2
+ *     "Tile decomposition"): a multiple of G that divides hidden; 0 means A = G
+ *     (the paper's default), A = hidden is token-level allocation. Its entropy
+ *     (Eq. 1-2 over all A channels) adds the per-quantization-tile sums
+ *     L = sum |a| and S = sum |a| log2 |a| left to right; each quantization
+ *     tile takes the width of its allocation tile.
  */
 typedef struct {
   int32_t tile;
@@ -75,6 +81,7 @@ typedef struct {
   int32_t n_candidates;
   uint8_t candidates[4];
   float tau;
+  int32_t alloc_tile;
 } tah_params_t;
 
 /* Fills the paper's defaults (§5.1): G = A = 64, 80% INT4 + 20% INT3
@@ -85,9 +92,10 @@ void tah_params_default(tah_params_t* p);
  * Size in bytes of the payload for this shape and parameters. The payload is a
  * fixed-shape uint8 stream (§3.4): its size depends only on (tokens, hidden,
  * params), never on the values. Layout (little-endian, sections on 256-byte
- * boundaries): 128-byte header (magic "TAHQ", version, shape, params, section
- * offsets) | u32 count of b_hi tiles before each run of 64 tiles | width map,
- * one bit per tile (1 = b_hi) | side byte per tile (bit 7: Hadamard applied,
+ * boundaries): 128-byte header (magic "TAHQ", version 2, shape, params,
+ * section offsets, allocation tile A as u32 at byte 120) | u32 count of b_hi
+ * tiles before each run of 64 tiles | width map, one bit per quantization tile
+ * (1 = b_hi; an allocation tile's bits are equal) | side byte per tile (bit 7: Hadamard applied,
  * bits 0-6: pivot index) | bf16 scale per tile | fp32 zero-point per tile |
  * code blocks of G*b/8 bytes in tile order, codes least-significant-bit first.
  */
@@ -128,14 +136,15 @@ tah_status_t tah_roundtrip(const void* x, tah_dtype_t x_dtype, int64_t tokens, i
                            void* stream);
 
 /*
- * Per-tile entropy only (Eq. 1-2, §3.2): h[t] for each of the tokens*hidden/G
- * tiles, fp32, device pointer. Needs the same workspace as tah_encode.
+ * Allocation-tile entropy only (Eq. 1-2, §3.2): h[u] for each of the
+ * tokens*hidden/A allocation tiles (A = G unless alloc_tile says otherwise),
+ * fp32, device pointer. Needs the same workspace as tah_encode.
  */
 tah_status_t tah_tile_entropy(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden,
                               const tah_params_t* p, float* h, void* ws, size_t ws_cap, void* stream);
 
-/* Byte offset inside the workspace of the fp32 per-tile entropies written by
- * tah_encode and tah_roundtrip. */
+/* Byte offset inside the workspace of the fp32 allocation-tile entropies
+ * (tokens*hidden/A of them) written by tah_encode and tah_roundtrip. */
 tah_status_t tah_workspace_entropy(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* offset);
 
 /*

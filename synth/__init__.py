@@ -180,7 +180,9 @@ NAIVE = {
     "g2_4096x2048_f32_grad": dict(bits=10, c=4096.0),
 }
 
-# Coverage variants: mixed allocations at other budgets, tau extremes.
+# Coverage variants: mixed allocations at other budgets, the tau values of
+# App. F (0, 2, 4, never), allocation tiles of several quantization tiles up to
+# whole tokens (Sec. 3.2: A = C is token-level allocation).
 COVERAGE = {
     "x1a_c2_budget5": ("c2_4096x2048_bf16_g64", dict(bit_budget=5.0, candidates=(3, 4, 8))),
     "x1b_c2_budget2p5": ("c2_4096x2048_bf16_g64", dict(bit_budget=2.5, candidates=(2, 3, 4, 8))),
@@ -189,6 +191,10 @@ COVERAGE = {
     "x3b_c1_tauinf": ("c1_256x512_f32_g32", dict(tau=math.inf)),
     "x3c_c2_tau0": ("c2_4096x2048_bf16_g64", dict(tau=0.0)),
     "x3d_c2_tauinf": ("c2_4096x2048_bf16_g64", dict(tau=math.inf)),
+    "x3e_c2_tau4": ("c2_4096x2048_bf16_g64", dict(tau=4.0)),
+    "x4a_c2_alloc256": ("c2_4096x2048_bf16_g64", dict(alloc_tile=256)),
+    "x4b_c5_token_level": ("c5_8192x8192_bf16_g64", dict(bit_budget=3.8, candidates=(3, 4, 8), alloc_tile=8192)),
+    "x4c_c4_token_level": ("c4_16384x5120_f32_g128", dict(alloc_tile=5120)),
 }
 
 

@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(tah.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert tah.abi_version() == 1
+    assert tah.abi_version() == 2
 
 
 def test_params_default_is_paper_default():
@@ -43,7 +43,10 @@ def test_sizes_match_oracle_layout(ref):
         w = synth.workload(name)
         pl = ref.plan(w.tokens, w.hidden, w.params)
         assert tah.payload_bytes(w.tokens, w.hidden, w.params) == pl["total"], name
-        assert tah.workspace_bytes(w.tokens, w.hidden, w.params) >= 4 * pl["tiles"]
+        assert tah.workspace_bytes(w.tokens, w.hidden, w.params) >= 4 * pl["atiles"]
+    for A in (128, 384, 768, 1536):  # kA = 2, 6, 12, 24 over hidden 1536
+        p = synth.Params(tile=64, tokens_per_sample=10, bit_budget=3.7, candidates=(3, 4, 8), alloc_tile=A)
+        assert tah.payload_bytes(50, 1536, p) == ref.plan(50, 1536, p)["total"], A
 
 
 def test_status_strings():
@@ -64,10 +67,14 @@ def test_argument_errors_without_device():
         (dict(candidates=(3, 9)), 1), (dict(tau=math.nan), 1), (dict(tau=-1.0), 1), (dict(bit_budget=math.nan), 1),
         (dict(bit_budget=math.inf), 1), (dict(tokens_per_sample=3), 1), (dict(bit_budget=2.0), 4),
         (dict(tile=16), 2), (dict(tile=8), 2),
+        (dict(alloc_tile=32), 1), (dict(alloc_tile=96), 1), (dict(alloc_tile=256), 1), (dict(alloc_tile=-64), 1),
     ]
     for over, code in bad:
         fields = {**good.__dict__, **over}
         assert _call_encode(tah.TahParams(**fields)) == code, over
+    for A in (0, 64, 128):  # allocation tiles that fit hidden = 128 pass validation (then fail on the pointers)
+        assert _call_encode(tah.TahParams(**{**good.__dict__, "alloc_tile": A}), x=0) == 1
+        assert _call_encode(tah.TahParams(**{**good.__dict__, "alloc_tile": A}), pcap=10) == 3
     # shape and pointer errors
     assert _call_encode(good, hidden=100) == 1
     assert _call_encode(good, tokens=-1) == 1

@@ -102,14 +102,14 @@ def test_workload_parity(name):
     torch.cuda.synchronize()
     assert_payload_equal(P, R, pl, f"{name} encode")
 
-    say(f"[parity] {name}: entropy in workspace vs oracle")
+    say(f"[parity] {name}: allocation-tile entropy in workspace vs oracle (A = {pl['A']})")
     off = tah.workspace_entropy_offset(w.tokens, w.hidden, p)
-    H = ws[off:off + 4 * pl["tiles"]].cpu().numpy().view(np.float32)
+    H = ws[off:off + 4 * pl["atiles"]].cpu().numpy().view(np.float32)
     rng = np.random.default_rng(1)
-    idx = rng.choice(pl["tiles"], size=min(4000, pl["tiles"]), replace=False)
+    idx = rng.choice(pl["atiles"], size=min(4000, pl["atiles"]), replace=False)
     xf = x.astype(np.float32) if x.dtype == np.float32 else synth.bf16_bits_to_f32(x)
-    tiles = xf.reshape(-1, p.tile)
-    H_ref = np.array([oracle.entropy(tiles[i]) for i in idx], np.float32)
+    atiles = xf.reshape(-1, pl["A"])
+    H_ref = np.array([oracle.alloc_entropy(atiles[i], p.tile) for i in idx], np.float32)
     assert np.array_equal(H[idx].view(np.uint32), H_ref.view(np.uint32))
 
     say(f"[parity] {name}: oracle decode")
@@ -155,7 +155,7 @@ def run_case(x, p, what):
     """encode, decode and round trip of one small tensor against the oracle."""
     tokens, hidden = x.shape
     say(f"[edge] {what}: {tokens}x{hidden} {x.dtype} tile {p.tile} S {p.tokens_per_sample} budget {p.bit_budget} "
-        f"cands {p.candidates} tau {p.tau}")
+        f"cands {p.candidates} tau {p.tau} A {p.alloc_tile}")
     R = oracle.encode(x, p)
     pl = oracle.plan(tokens, hidden, p)
     xt = to_dev(x)
@@ -215,6 +215,46 @@ def test_tau_semantics(tau):
         assert np.all(side >> 7 == 1)
     if tau == math.inf:
         assert not np.any(side >> 7)
+
+
+@pytest.mark.parametrize("tile", [32, 64, 128])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_allocation_tiles(tile, dtype):
+    # allocation tiles of kA quantization tiles (Sec. 3.2), kA a power of two or
+    # not, up to whole tokens; ragged tile counts, one or several samples
+    M = 12
+    for tokens, S in ((37, 0), (40, 8), (130, 13)):
+        x = synth.random_tensor(tokens, tile * M, dtype, tokens + tile, n_out=4, mult=40)
+        for kA in (2, 3, 4, 6, M):
+            run_case(x, P(tile=tile, tokens_per_sample=S, bit_budget=3.6, candidates=(3, 4), tau=2.0, alloc_tile=kA * tile),
+                     f"alloc kA={kA} t{tokens} S{S}")
+    # several widths, and a budget on a candidate (no selection, k = 0)
+    x = synth.random_tensor(64, tile * 8, dtype, 99, n_out=3, mult=30)
+    run_case(x, P(tile=tile, tokens_per_sample=16, bit_budget=5.5, candidates=(2, 4, 8), tau=2.0, alloc_tile=4 * tile),
+             "alloc kA=4 widths 4/8")
+    run_case(x, P(tile=tile, tokens_per_sample=16, bit_budget=4.0, candidates=(2, 4, 8), tau=2.0, alloc_tile=4 * tile),
+             "alloc kA=4 k=0")
+
+
+def test_allocation_tile_ties_and_entropy_api():
+    # equal allocation-tile entropies: the lower index wins
+    z = np.zeros((16, 512), np.float32)
+    run_case(z, P(tile=64, tokens_per_sample=4, bit_budget=3.5, candidates=(3, 4), tau=2.0, alloc_tile=128), "alloc zero")
+    row = synth.random_tensor(1, 128, synth.F32, 3)
+    x = np.tile(row, (32, 4))
+    run_case(x, P(tile=64, tokens_per_sample=8, bit_budget=3.3, candidates=(3, 4), tau=2.0, alloc_tile=128),
+             "alloc repeated")
+    run_case(x, P(tile=64, tokens_per_sample=8, bit_budget=3.3, candidates=(3, 4), tau=2.0, alloc_tile=512),
+             "token level repeated rows")
+    # tah_tile_entropy returns one entropy per allocation tile
+    x = synth.random_tensor(300, 640, synth.BF16, 12, n_out=3, mult=30)
+    for A in (64, 128, 320, 640):
+        p = P(tile=64, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0, alloc_tile=A)
+        say(f"[edge] tile_entropy A={A}")
+        h = tah.tile_entropy(to_dev(x), p).cpu().numpy()
+        st = oracle.tile_stats(x, p)
+        assert h.size == 300 * 640 // A
+        assert np.array_equal(h.view(np.uint32), st["H"].view(np.uint32)), A
 
 
 def test_ties_all_zero_and_repeated_tiles():
