@@ -28,8 +28,12 @@ FLAGS = [
 ]
 
 
+# Per-file flags (none at present).
+FILE_FLAGS: dict = {}
+
+
 def _compile(src: str, out: str, extra: list) -> None:
-    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", out]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(src, []), *extra, "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

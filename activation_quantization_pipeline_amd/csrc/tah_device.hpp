@@ -145,72 +145,14 @@ __device__ __forceinline__ float log2_full(float x, const float* lt) {
 // (equal to -sum p_k log2 p_k with p_k = |a_k| / L). fp32 order: S summed
 // left to right with fmaf from 0, then log2(L) - S / L; L = 0 gives 0.
 // NODE: the tile's values are widened bf16 (log2_node applies).
-// Summation order of the entropy's two sums (Eq. 1-2): leaves of 4 consecutive
-// elements, a leaf summed left to right (L: ((a0 + a1) + a2) + a3; S: the fma
-// chain started from the rounded product a0 log2 a0), then a balanced binary
-// tree of adjacent pairs over the leaves. It is the order a wavefront
-// reduction over lanes of 8 consecutive elements produces.
-template <int N>
-__device__ __forceinline__ float pair_tree(float (&x)[N]) {
-#pragma unroll
-  for (int w = N; w > 1; w /= 2) {
-#pragma unroll
-    for (int i = 0; i < w / 2; ++i) x[i] = x[2 * i] + x[2 * i + 1];
-  }
-  return x[0];
-}
-
-// The same tree built while the leaves arrive: leaf i (in order, i < N)
-// joins its left siblings as soon as they are complete, so only the pending
-// left subtrees (st, one per level) stay live. After leaf N - 1 the whole sum
-// is returned.
-template <int N>
-struct PairTreeAcc {
-  static constexpr int kLevels = N <= 1 ? 1 : (N <= 2 ? 2 : (N <= 4 ? 3 : (N <= 8 ? 4 : (N <= 16 ? 5 : 6))));
-  float st[kLevels];
-  // i is a compile-time constant at every call site (unrolled loops); the
-  // loop has a fixed trip count so that st stays in registers.
-  __device__ __forceinline__ float push(int i, float x) {
-    bool open = true;
-#pragma unroll
-    for (int lv = 0; lv < kLevels; ++lv) {
-      if (open && ((i >> lv) & 1)) {
-        x = st[lv] + x;
-      } else if (open) {
-        st[lv] = x;
-        open = false;
-      }
-    }
-    return x;
-  }
-};
-
-// L = sum_k |a_k| of one tile in the order above.
-template <int G>
-__device__ __forceinline__ float tile_l1(const float (&v)[G]) {
-  PairTreeAcc<G / 4> acc;
-  float sum = 0.0f;
-#pragma unroll
-  for (int i = 0; i < G / 4; ++i)
-    sum = acc.push(i, ((fabsf(v[4 * i]) + fabsf(v[4 * i + 1])) + fabsf(v[4 * i + 2])) + fabsf(v[4 * i + 3]));
-  return sum;
-}
-
-// S = sum_k |a_k| log2 |a_k| of one tile in the order above.
+// S = sum_k |a_k| log2 |a_k| of one tile, fma-accumulated left to right from 0.
 template <int G, bool NODE>
 __device__ __forceinline__ float tile_logsum(const float (&v)[G], const float* lt) {
-  PairTreeAcc<G / 4> tree;
   float S = 0.0f;
 #pragma unroll
-  for (int i = 0; i < G / 4; ++i) {
-    float acc = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int k = 4 * i + j;
-      const float lg = NODE ? log2_node(v[k], lt) : log2_full(fabsf(v[k]), lt);
-      acc = j == 0 ? fabsf(v[k]) * lg : __builtin_fmaf(fabsf(v[k]), lg, acc);
-    }
-    S = tree.push(i, acc);
+  for (int k = 0; k < G; ++k) {
+    const float lg = NODE ? log2_node(v[k], lt) : log2_full(fabsf(v[k]), lt);
+    S = __builtin_fmaf(fabsf(v[k]), lg, S);
   }
   asm volatile("" : "+v"(S));  // the sum is complete here, ahead of the L = 0 test
   return S;

@@ -87,14 +87,13 @@ __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
 
 // Phase-A statistics of one tile read from LDS (Eq. 3 and Eq. 1):
 // m1 = max |a_k|, d = first index holding m1, m2 = max |a_k| over k != d,
-// l1 = sum |a_k| (leaves of 4, then a tree of pairs, as tile_l1); v receives
-// the tile as fp32.
+// l1 = sum |a_k| left to right; v receives the tile as fp32.
 // bf16 tiles: the magnitude bits and (G-1-k) share one 32-bit key (bf16
 // leaves the low 16 bits free), so max/median on unsigned keys give the top
 // two magnitudes, the lowest index among ties, and no float compares.
-// FUSED (bf16 only): the entropy's sum S = sum |a_k| log2 |a_k| (in the order
-// of tile_logsum) is taken in the same pass, its table reads issued with the
-// keys of 8 elements and consumed while the next 8 are in flight. That hides the LDS
+// FUSED (bf16 only): the entropy's sum S = sum |a_k| log2 |a_k| (left to
+// right) is taken in the same pass, its table reads issued with the keys of
+// 8 elements and consumed while the next 8 are in flight. That hides the LDS
 // latency but keeps more registers live, so only the kernels with registers
 // to spare (encode without reconstruction) use it.
 template <int G, typename TIn, bool FUSED>
@@ -103,9 +102,7 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
   if constexpr (Elem<TIn>::kBytes == 2) {
     const uint4* p = reinterpret_cast<const uint4*>(row);
     uint32_t k1 = 0u, k2 = 0u;
-    float sleaf = 0.0f;  // the current leaf of S
-    PairTreeAcc<G / 4> lt_s;
-    float ssum = 0.0f;
+    float s = 0.0f, acc = 0.0f;
     float lgp[8];
 #pragma unroll
     for (int c = 0; c < G / 8; ++c) {
@@ -129,20 +126,17 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
           lgc[2 * i] = log2_node(v[k], lt);
           lgc[2 * i + 1] = log2_node(v[k + 1], lt);
         }
+        s = s + fabsf(v[k]);
         k2 = umed3(k2, kl, k1);
         k1 = max(k1, kl);
+        s = s + fabsf(v[k + 1]);
         k2 = umed3(k2, kh, k1);
         k1 = max(k1, kh);
       }
       if constexpr (FUSED) {
         if (c > 0) {
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const int k = 8 * (c - 1) + i;
-            if ((i & 3) == 0) sleaf = fabsf(v[k]) * lgp[i];
-            else sleaf = __builtin_fmaf(fabsf(v[k]), lgp[i], sleaf);
-            if ((i & 3) == 3) ssum = lt_s.push(k >> 2, sleaf);
-          }
+          for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(fabsf(v[8 * (c - 1) + i]), lgp[i], acc);
         }
 #pragma unroll
         for (int i = 0; i < 8; ++i) lgp[i] = lgc[i];
@@ -150,25 +144,21 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
     }
     if constexpr (FUSED) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int k = G - 8 + i;
-        if ((i & 3) == 0) sleaf = fabsf(v[k]) * lgp[i];
-        else sleaf = __builtin_fmaf(fabsf(v[k]), lgp[i], sleaf);
-        if ((i & 3) == 3) ssum = lt_s.push(k >> 2, sleaf);
-      }
+      for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(fabsf(v[G - 8 + i]), lgp[i], acc);
     }
     m1 = __uint_as_float(k1 & 0xffff0000u);
     m2 = __uint_as_float(k2 & 0xffff0000u);
     d = G - 1 - (int)(k1 & 0xffffu);
-    l1 = tile_l1<G>(v);
-    S = FUSED ? ssum : 0.0f;
+    l1 = s;
+    S = acc;
   } else {
     lds_read_tile<G, TIn>(row, v);
-    float a1 = fabsf(v[0]), a2 = 0.0f;
+    float a1 = fabsf(v[0]), a2 = 0.0f, s = 0.0f + fabsf(v[0]);
     int dd = 0;
 #pragma unroll
     for (int k = 1; k < G; ++k) {
       const float av = fabsf(v[k]);
+      s = s + av;
       const bool c = av > a1;
       a2 = __builtin_amdgcn_fmed3f(a2, av, a1);
       a1 = fmaxf(a1, av);
@@ -177,7 +167,7 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
     m1 = a1;
     m2 = a2;
     d = dd;
-    l1 = tile_l1<G>(v);
+    l1 = s;
     S = 0.0f;
   }
 }
@@ -325,7 +315,8 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
       } else {
         hi = (a.bitmap[t >> 5] >> (t & 31)) & 1u;
       }
-      if (a.payload) a.payload[a.off_side + t] = (uint8_t)((flag << 7) | piv);
+      // side byte: the flag, and the pivot of a transformed tile (0 for the others)
+      if (a.payload) a.payload[a.off_side + t] = (uint8_t)(flag ? (0x80 | piv) : 0);
     }
 
     // Code-block offsets: tile t starts at t*sz_lo + (b_hi tiles before t)*(sz_hi - sz_lo);

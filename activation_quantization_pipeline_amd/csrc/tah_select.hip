@@ -77,7 +77,9 @@ __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsA
   if (tid < n) {
     float v[G];
     lds_read_tile<G, TIn>(xs + tid * RI::kStride, v);
-    const float l1 = tile_l1<G>(v);
+    float l1 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) l1 = l1 + fabsf(v[k]);
     if constexpr (SUMS)
       a.ls[t0 + tid] = make_float2(l1, tile_logsum<G, Elem<TIn>::kBytes == 2>(v, lt));
     else

@@ -96,7 +96,7 @@ void tah_params_default(tah_params_t* p);
  * section offsets, allocation tile A as u32 at byte 120) | u32 count of b_hi
  * tiles before each run of 64 tiles | width map, one bit per quantization tile
  * (1 = b_hi; an allocation tile's bits are equal) | side byte per tile (bit 7: Hadamard applied,
- * bits 0-6: pivot index) | bf16 scale per tile | fp32 zero-point per tile |
+ * bits 0-6: pivot index of a transformed tile, 0 otherwise) | bf16 scale per tile | fp32 zero-point per tile |
  * code blocks of G*b/8 bytes in tile order, codes least-significant-bit first.
  */
 tah_status_t tah_payload_bytes(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* out);

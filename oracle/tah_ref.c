@@ -263,32 +263,20 @@ void tahref_fwht(float* v, int G) {
  * nothing (0 log 0 = 0) and an all-zero tile has H = 0.
  * Since sum_k p_k = 1, H = log2 L - (1/L) sum_k |a_k| log2 |a_k| with
  * L = ||a||_1, and that is the form evaluated (one log per element, of the
- * input value itself), with H = log2s(L) - S / L (L > 0), H = 0 (L = 0).
- * Summation order (a reading: the pages fix none). The tile is cut into
- * leaves of 4 consecutive elements; a leaf's L is ((a0 + a1) + a2) + a3 and its
- * S the fma chain a3 l3 + (a2 l2 + (a1 l1 + a0 l0)) started from the rounded
- * product a0 l0 (a = |alpha_k|, l = log2s(a)); the n/4 leaf sums are then
- * added as a balanced binary tree of adjacent pairs (leaf 2i + leaf 2i+1, then
- * those pairs, ...). n is a power of two >= 8.
+ * input value itself):
+ *   L = sum |a_k| left to right; S = sum fmaf(|a_k|, log2s(|a_k|), S) left to
+ *   right from 0; H = log2s(L) - S / L (L > 0), H = 0 (L = 0).
  */
 static void entropy_sums(const float* alpha, int n, float* L, float* S) {
-  float l[32], s[32];
-  const int nl = n / 4;
-  for (int i = 0; i < nl; ++i) {
-    float a[4];
-    for (int j = 0; j < 4; ++j) a[j] = fabsf(alpha[4 * i + j]);
-    l[i] = ((a[0] + a[1]) + a[2]) + a[3];
-    float acc = a[0] * tahref_log2s(a[0]);
-    for (int j = 1; j < 4; ++j) acc = fmaf(a[j], tahref_log2s(a[j]), acc);
-    s[i] = acc;
+  float l1 = 0.0f;
+  for (int k = 0; k < n; ++k) l1 = l1 + fabsf(alpha[k]);
+  float s = 0.0f;
+  for (int k = 0; k < n; ++k) {
+    const float a = fabsf(alpha[k]);
+    s = fmaf(a, tahref_log2s(a), s);
   }
-  for (int w = nl; w > 1; w /= 2)
-    for (int i = 0; i < w / 2; ++i) {
-      l[i] = l[2 * i] + l[2 * i + 1];
-      s[i] = s[2 * i] + s[2 * i + 1];
-    }
-  *L = l[0];
-  *S = s[0];
+  *L = l1;
+  *S = s;
 }
 
 static float entropy_from_sums(float L, float S) {
@@ -511,7 +499,8 @@ int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden
  *   header (128 B, zero padded to 256) | block table: u32 count of b_hi tiles
  *   before each run of 64 tiles | width map: u32 words, bit t%32 of word t/32
  *   is 1 iff tile t has b_hi (2 words per 64 tiles) | side byte per tile:
- *   bit 7 = transformed, bits 0..6 = pivot d | scale per tile: bf16 bits |
+ *   bit 7 = transformed, bits 0..6 = pivot d of a transformed tile (0 for
+ *   the others) | scale per tile: bf16 bits |
  *   zero-point per tile: fp32 | codes: one block of G*b/8 bytes per tile in
  *   tile order, code k at stream bits [k*b, k*b + b), least significant bit
  *   first (bit i of the block is bit i%8 of byte i/8). Padding bytes are zero.
@@ -564,7 +553,7 @@ int tahref_encode(const void* x, int x_dtype, int64_t tokens, int64_t hidden, co
     int b = hi[t] ? pl.b_hi : pl.b_lo;
     float lo, s;
     tahref_quantize(a, pl.G, b, &lo, &s, q);
-    put_u8(P, pl.off_side + t, (uint32_t)((f ? 0x80 : 0) | d));
+    put_u8(P, pl.off_side + t, (uint32_t)(f ? (0x80 | d) : 0)); /* the pivot only matters to a transformed tile */
     put_u16(P, pl.off_scale + 2 * t, f2u(s) >> 16);
     put_u32(P, pl.off_zero + 4 * t, f2u(lo));
     for (int k = 0; k < pl.G; ++k)
