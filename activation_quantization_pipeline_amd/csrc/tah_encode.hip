@@ -9,13 +9,14 @@
 //              allocation, the tile entropy of Eq. (1)-(2); with a mixed
 //              allocation the width bit comes from the selection pass instead.
 //              It fixes the tile's code-block offset (§3.4 packing order);
-//  3. forward: the flagged tiles get the pivot swap P_d and the Hadamard
-//              transform of Eq. (4), computed by 16-lane groups through LDS;
+//  3. forward: a flagged tile gets the pivot swap P_d in its own LDS row and
+//              the Hadamard transform of Eq. (4) in the lane's registers;
 //  4. quantize: every lane quantizes its (transformed or not) tile
 //              asymmetrically (§3.3), packs the codes and stores code block,
 //              scale and zero-point; the fused variant dequantizes from the
-//              codes in registers into the tile's LDS row;
-//  5. inverse: flagged tiles get H^T / G and the swap undone (16-lane groups);
+//              codes in registers;
+//  5. inverse: a flagged tile gets H^T / G in registers and, once written to
+//              its LDS row, the swap undone there;
 //  6. out:     the rebuilt tiles leave LDS with 16-byte coalesced stores.
 #include "tah_device.hpp"
 #include "tah_internal.hpp"
@@ -218,21 +219,14 @@ __device__ __forceinline__ void quantize_tile(const EncArgs& a, float (&v)[G], i
 // group g of 64 tiles goes to workgroup g mod gridDim.x. Groups of small tiles
 // are prefetched into registers while the current group is processed.
 //
-// Transformed tiles (flag set by Eq. 3) are few and scattered, so their
-// Hadamard transforms are not run in the lane that owns the tile (that would
-// make the whole wavefront execute both paths): 16-lane groups transform them,
-// four tiles at a time, into LDS slots of fp32; the owning lane takes the
-// transformed tile from its slot, runs the same quantizer as every other lane
-// and puts the dequantized values back; the 16-lane groups then invert the
-// transform into the output row. The first kCoop transformed tiles of a group
-// are quantized together with the plain tiles; groups with more (tau near 1)
-// take further rounds of kCoop.
+// A flagged tile (Eq. 3) is transformed by its own lane with fwht<G>, the
+// stage order of the oracle. The wavefront runs the butterflies whenever one
+// of its 64 tiles is flagged; measured on the 8192x8192 round trip this beats
+// handing the flagged tiles to 16-lane groups through LDS (barriers and
+// round trips per group) at every tau, from 0 (every tile) to 4.
 template <int G, typename TIn, int OUT, bool MIXED>
 __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncArgs a) {
   constexpr int NT = 64;
-  constexpr int V = G / 16;     // elements per lane in a 16-lane transform group
-  constexpr int kCoop = 8;      // transformed tiles per group handled by 16-lane groups
-  constexpr int kSlot = G + 4;  // fp32 slot stride: 16 bytes of padding
   using RI = TileRow<G, TIn>;
   using TOut = typename std::conditional<OUT == 1, float, bf16_t>::type;
   using RO = TileRow<G, TOut>;
@@ -244,13 +238,10 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
 
   __shared__ __attribute__((aligned(16))) uint8_t xs[NT * RI::kStride];
   __shared__ __attribute__((aligned(16))) uint8_t ys_own[kSameRow ? 16 : NT * RO::kStride];
-  __shared__ __attribute__((aligned(16))) float ts[kCoop * kSlot];
-  __shared__ uint32_t flist[NT];
   __shared__ __attribute__((aligned(16))) float lt[256];  // log2 tables of the entropy
   uint8_t* ys = kSameRow ? xs : ys_own;
 
   const int lane = threadIdx.x;
-  const int q4 = lane >> 4, r16 = lane & 15;  // 16-lane group and lane within it
 
   if (blockIdx.x == 0 && a.payload) {
     if (lane < 32) reinterpret_cast<uint32_t*>(a.payload)[lane] = a.hdr.w[lane];
@@ -336,89 +327,32 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
       }
     }
 
-    // ---------------- transformed tiles (§3.3) ----------------
-    // flist[j] names the j-th flagged tile of the group (lane | pivot << 8);
-    // rounds of up to kCoop of them use the LDS slots, tile j in slot j - j_lo.
-    const uint64_t fmask = ballot(act && flag);
-    const int nf = (int)__popcll(fmask);
-    const int slot = (int)lanes_below(fmask);
+    // ---------------- transformed tiles (§3.3) and quantization ----------------
     const int b = hi ? a.b_hi : a.b_lo;
-    // P_d (the first and the d-th element exchange places) and H of Eq. (4)
-    // without the 1/sqrt(G), by 16-lane groups, four tiles at a time.
-    auto forward = [&](int j_lo, int j_hi) {
-      for (int j0 = j_lo; j0 < j_hi; j0 += 4) {
-        const int j = j0 + q4;
-        uint32_t e = 0;
-        if (j < j_hi) {
-          e = flist[j];
-          if (r16 == 0) {
-            uint8_t* row = xs + (e & 255u) * RI::kStride;
-            const int d = (int)(e >> 8);
-            const uint32_t x0 = lds_elem_bits<TIn>(row, 0), xd = lds_elem_bits<TIn>(row, d);
-            lds_elem_set<TIn>(row, 0, xd);
-            lds_elem_set<TIn>(row, d, x0);
-          }
-        }
-        __syncthreads();
-        if (j < j_hi) {
-          float y[V];
-          lds_read_part<V, TIn>(xs + (e & 255u) * RI::kStride, r16, y);
-          fwht16<V>(y, r16);
-          lds_write_part<V, float>(reinterpret_cast<uint8_t*>(ts + (j - j_lo) * kSlot), r16, y);
-        }
+    if (act) {
+      if (flag) {  // P_d in the lane's own row, then H of Eq. (4) in registers
+        uint8_t* row = xs + lane * RI::kStride;
+        const uint32_t x0 = lds_elem_bits<TIn>(row, 0), xd = lds_elem_bits<TIn>(row, piv);
+        lds_elem_set<TIn>(row, 0, xd);
+        lds_elem_set<TIn>(row, piv, x0);
+        lds_read_tile<G, TIn>(row, v);
+        fwht<G>(v);
       }
-      __syncthreads();
-    };
-    // H^T = H, the 1/G, and the swap undone, into the tile's output row.
-    auto inverse = [&](int j_lo, int j_hi) {
-      __syncthreads();
-      for (int j0 = j_lo; j0 < j_hi; j0 += 4) {
-        const int j = j0 + q4;
-        if (j < j_hi) {
-          const uint32_t e = flist[j];
-          uint8_t* row = ys + (e & 255u) * RO::kStride;
-          float y[V];
-          lds_read_part<V, float>(reinterpret_cast<const uint8_t*>(ts + (j - j_lo) * kSlot), r16, y);
-          fwht16<V>(y, r16);
-#pragma unroll
-          for (int i = 0; i < V; ++i) y[i] = y[i] * (1.0f / G);
-          lds_write_part<V, TOut>(row, r16, y);
-          if (r16 == 0) {  // element d takes y_0, element 0 takes y_d
-            const int d = (int)(e >> 8);
-            const uint32_t yd = lds_elem_bits<TOut>(row, d);
-            lds_elem_set<TOut>(row, d, f32_to_elem_bits<TOut>(y[0]));
-            lds_elem_set<TOut>(row, 0, yd);
-          }
-        }
-      }
-    };
-
-    if (nf != 0) {
-      if (act && flag) flist[slot] = (uint32_t)lane | ((uint32_t)piv << 8);
-      __syncthreads();
-    }
-    // Round 0 quantizes the plain tiles and the first kCoop transformed tiles;
-    // further rounds (groups with many transformed tiles) take kCoop more each.
-    for (int j_lo = 0;; j_lo += kCoop) {
-      const int j_hi = nf < j_lo + kCoop ? nf : j_lo + kCoop;
-      const bool mine = act && (flag ? (slot >= j_lo && slot < j_hi) : j_lo == 0);
-      uint8_t* sl = reinterpret_cast<uint8_t*>(ts + (slot - j_lo) * kSlot);
-      if (j_hi > j_lo) {
-        forward(j_lo, j_hi);
-        if (mine && flag) lds_read_tile<G, float>(sl, v);
-      }
-      if (mine) {
-        quantize_tile<G, OUT>(a, v, t, b, code_off);
-        if constexpr (OUT != 0) {
-          if (!flag) lds_write_tile<G, TOut>(ys + lane * RO::kStride, v);
-          else lds_write_tile<G, float>(sl, v);
-        }
-      }
+      quantize_tile<G, OUT>(a, v, t, b, code_off);
       if constexpr (OUT != 0) {
-        if (j_hi > j_lo) inverse(j_lo, j_hi);
+        if (flag) {  // H^T = H, the 1/G
+          fwht<G>(v);
+#pragma unroll
+          for (int k = 0; k < G; ++k) v[k] = v[k] * (1.0f / G);
+        }
+        uint8_t* orow = ys + lane * RO::kStride;
+        lds_write_tile<G, TOut>(orow, v);
+        if (flag) {  // element d takes y_0, element 0 takes y_d
+          const uint32_t y0 = lds_elem_bits<TOut>(orow, 0), yd = lds_elem_bits<TOut>(orow, piv);
+          lds_elem_set<TOut>(orow, piv, y0);
+          lds_elem_set<TOut>(orow, 0, yd);
+        }
       }
-      if (j_hi >= nf) break;
-      __syncthreads();
     }
 
     if constexpr (OUT != 0) {

@@ -257,6 +257,24 @@ def test_allocation_tile_ties_and_entropy_api():
         assert np.array_equal(h.view(np.uint32), st["H"].view(np.uint32)), A
 
 
+@pytest.mark.parametrize("tile", [32, 64, 128])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("tau", [0.0, 0.5])
+def test_small_tau_every_tile_transformed(tile, dtype, tau):
+    # tau < 1 takes the encoder variant that transforms each tile in its own lane
+    for tokens, mult in ((3, 5), (65, 3), (130, 4)):
+        x = synth.random_tensor(tokens, tile * mult, dtype, tokens + mult + 7, n_out=3, mult=20)
+        run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=tau),
+                 f"tau {tau} t{tokens} m{mult} mixed")
+        run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=4.0, candidates=(4, 8), tau=tau),
+                 f"tau {tau} t{tokens} m{mult} uniform")
+    # tied maxima are not transformed even at tau = 0.5; all-zero tiles never are
+    z = np.zeros((8, tile * 2), np.float32)
+    z[:, 3] = 2.0
+    z[:, 5] = -2.0
+    run_case(z, P(tile=tile, tokens_per_sample=0, bit_budget=3.0, candidates=(3,), tau=tau), f"tau {tau} ties")
+
+
 def test_ties_all_zero_and_repeated_tiles():
     # every tile has entropy 0: the selection keeps the lowest indices
     z = np.zeros((16, 256), np.float32)
