@@ -46,6 +46,7 @@ EXPORTS = (
     "tah_naive_payload_bytes",
     "tah_naive_encode",
     "tah_naive_decode",
+    "tah_hadamard",
     "tah_read_device_status",
     "tah_status_string",
     "tah_abi_version",
@@ -132,6 +133,8 @@ def lib() -> ctypes.CDLL:
         L.tah_naive_encode.restype = ctypes.c_int
         L.tah_naive_decode.argtypes = [vp, sz, i64, ctypes.c_int, ctypes.c_float, vp, ctypes.c_int, vp, sz, vp]
         L.tah_naive_decode.restype = ctypes.c_int
+        L.tah_hadamard.argtypes = [vp, ctypes.c_int, i64, ctypes.c_int, ctypes.c_int, vp, vp]
+        L.tah_hadamard.restype = ctypes.c_int
         L.tah_read_device_status.argtypes = [vp, vp, P(ctypes.c_int32)]
         L.tah_read_device_status.restype = ctypes.c_int
         L.tah_status_string.argtypes = [ctypes.c_int]
@@ -316,6 +319,23 @@ def naive_decode(payload: torch.Tensor, n: int, bits: int, c: float, y_dtype: to
     rc = lib().tah_naive_decode(_ptr(payload), payload.numel(), int(n), int(bits), float(c), _ptr(y),
                                 _dtype_code(y.dtype), _ptr(ws), ws.numel(), _stream(stream))
     _check(rc, "tah_naive_decode")
+    return y
+
+
+# ---------------------------------------------------------------- Hadamard alone ----
+HADAMARD_BUTTERFLY, HADAMARD_MFMA = 0, 1
+
+
+def hadamard(x: torch.Tensor, tile: int, method: int = HADAMARD_BUTTERFLY, y: torch.Tensor | None = None,
+             stream=None) -> torch.Tensor:
+    """tah_hadamard: unnormalized H_G over each contiguous tile of x -> fp32."""
+    if not x.is_contiguous() or x.numel() % tile:
+        raise ValueError("x must be contiguous and hold whole tiles")
+    if y is None:
+        y = torch.empty(x.numel(), dtype=torch.float32, device=x.device)
+    rc = lib().tah_hadamard(_ptr(x), _dtype_code(x.dtype), x.numel() // tile, int(tile), int(method), _ptr(y),
+                            _stream(stream))
+    _check(rc, "tah_hadamard")
     return y
 
 

@@ -335,6 +335,16 @@ tah_status_t tah_naive_decode(const void* payload, size_t payload_len, int64_t n
   return hip_status(launch_naive_decode(payload, n, bits, c, y, y_dtype, ws, static_cast<hipStream_t>(stream)));
 }
 
+tah_status_t tah_hadamard(const void* x, tah_dtype_t x_dtype, int64_t n_tiles, int tile, int method, float* y,
+                          void* stream) {
+  if (n_tiles < 0 || (tile != 32 && tile != 64 && tile != 128)) return TAH_ERR_INVALID_ARG;
+  if (x_dtype != TAH_DTYPE_F32 && x_dtype != TAH_DTYPE_BF16) return TAH_ERR_INVALID_ARG;
+  if (method != TAH_HADAMARD_BUTTERFLY && method != TAH_HADAMARD_MFMA) return TAH_ERR_INVALID_ARG;
+  if (n_tiles > 0 && (!x || !aligned16(x) || !y || !aligned16(y))) return TAH_ERR_INVALID_ARG;
+  if (method == TAH_HADAMARD_MFMA && (tile != 64 || x_dtype != TAH_DTYPE_BF16)) return TAH_ERR_UNSUPPORTED;
+  return hip_status(launch_hadamard(x, x_dtype, n_tiles, tile, method, y, static_cast<hipStream_t>(stream)));
+}
+
 tah_status_t tah_read_device_status(const void* ws, void* stream, int32_t* out) {
   if (!ws || !out) return TAH_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -74,6 +74,9 @@ hipError_t launch_naive_encode(const void* g, int g_dtype, int64_t n, int bits, 
 hipError_t launch_naive_decode(const void* payload, int64_t n, int bits, float c, void* y, int y_dtype, void* ws,
                                hipStream_t st);
 
+// Tile-local Hadamard transform alone (tah_hadamard.hip); method 0 butterfly, 1 MFMA.
+hipError_t launch_hadamard(const void* x, int x_dtype, int64_t tiles, int G, int method, float* y, hipStream_t st);
+
 void make_header(const Plan& pl, Header* h);
 void make_pads(const Plan& pl, PadRanges* pr);
 

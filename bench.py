@@ -15,8 +15,10 @@ Prints one JSON line. Extra legs: encode-only and decode-only rates, the same
 shape with a mixed 80% INT4 / 20% INT3 allocation (the paper's default,
 general two-pass path), the backward path on activation gradients of the same
 shape (the 8-bit fixed-point compressor with the scaling of Eq. 24, encode and
-decode, and the TAH-Quant codec at 4 bits), a 512 MB device copy for the
-achievable bandwidth, and the CPU oracle on the host (single thread).
+decode, and the TAH-Quant codec at 4 bits), the tile-local Hadamard alone
+(the butterfly against the dense product on the matrix cores), a 512 MB device
+copy for the achievable bandwidth, and the CPU oracle on the host (single
+thread).
 """
 
 import argparse
@@ -39,12 +41,16 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_encode_c5_roundtrip_traffic.jso
 CSRC = os.path.join(ROOT, "activation_quantization_pipeline_amd", "csrc")
 
 
+# The sources the headline kernel (the fused encode + decode) is built and
+# launched from: a change to any of them makes the stored counters stale.
+HEADLINE_SOURCES = ("tah_abi.hip", "tah_encode.hip", "tah_select.hip", "tah_device.hpp", "tah_internal.hpp")
+
+
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        if f.endswith((".hip", ".hpp")):
-            h.update(f.encode())
-            h.update(open(os.path.join(CSRC, f), "rb").read())
+    for f in HEADLINE_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -235,6 +241,22 @@ def main():
             taus[str(tau)] = round(bytes_step / (t_ms * 1e-3) / 1e9, 1)
             del pt
         extras["tau_sweep_roundtrip_gbps"] = taus
+        # the tile-local Hadamard of Eq. (4) alone on the same tensor, fp32 out: the
+        # codec's butterfly against the dense product on the matrix cores
+        Lb = tah.lib()
+        yh = torch.empty(T * C, dtype=torch.float32, device=dev)
+        n_t = T * C // p.tile
+        had = {}
+        for label, meth in (("butterfly", tah.HADAMARD_BUTTERFLY), ("mfma", tah.HADAMARD_MFMA)):
+            h_args = [(xs[i].data_ptr(), 1, n_t, p.tile, meth, yh.data_ptr(), stream_h) for i in range(n_sets)]
+            rc = Lb.tah_hadamard(*h_args[0])
+            if rc != 0:
+                raise RuntimeError(f"tah_hadamard({label}): {tah.status_string(rc)}")
+            _, h_mean, _, _ = time_launches(torch, lambda i: Lb.tah_hadamard(*h_args[i]), n_sets, args.steps,
+                                            args.warmup)
+            had[label] = round((x_bytes + 4 * T * C) / (h_mean * 1e-3) / 1e9, 1)
+        extras["hadamard_alone_gbps"] = had
+        del yh
         # the backward path (Algorithm 1 lines 6-7): activation gradients of the same shape,
         # fixed-point compressor at 8 bits with the scaling of Eq. (24), and TAH-Quant at 4 bits
         gname = "g1_8192x8192_bf16_grad"
@@ -246,7 +268,6 @@ def main():
         npb = tah.naive_payload_bytes(n_el, nb)
         nps = [torch.empty(npb, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
         wsn = torch.zeros(256, dtype=torch.uint8, device=dev)
-        Lb = tah.lib()
         ne_args = [(gs[i].data_ptr(), 1, n_el, nb, nc, nps[i].data_ptr(), npb, stream_h) for i in range(n_sets)]
         nd_args = [(nps[i].data_ptr(), npb, n_el, nb, nc, ys[i].data_ptr(), 1, wsn.data_ptr(), 256, stream_h)
                    for i in range(n_sets)]

@@ -175,6 +175,27 @@ tah_status_t tah_naive_encode(const void* g, tah_dtype_t g_dtype, int64_t n, int
 tah_status_t tah_naive_decode(const void* payload, size_t payload_len, int64_t n, int bits, float c, void* y,
                               tah_dtype_t y_dtype, void* ws, size_t ws_cap, void* stream);
 
+/*
+ * The tile-local Hadamard transform of Eq. (4) alone (§3.3), unnormalized:
+ * y_t = H_G x_t for each of n_tiles contiguous tiles of `tile` elements
+ * (x: fp32 or bf16, row-major [n_tiles, tile]; y: fp32, same layout; both
+ * device pointers, 16-byte aligned, owned by the caller; no pivot swap).
+ * H_G is the Sylvester matrix, H[i][j] = (-1)^popcount(i & j).
+ * method TAH_HADAMARD_BUTTERFLY: the fast Walsh-Hadamard butterfly the codec
+ *   runs (stages of stride 1, 2, 4, ... in fp32), so its results are the
+ *   codec's transform bit for bit; tile 32, 64 or 128.
+ * method TAH_HADAMARD_MFMA: the same product as a dense matrix multiply on
+ *   the matrix cores (the O(G^2) form §3.4 prices); each entry is the exact
+ *   fp32 sum of G exact products, added in the hardware's order, so it may
+ *   differ from the butterfly's in the last bits. Only tile 64 with bf16
+ *   input (else TAH_ERR_UNSUPPORTED).
+ * The codec never calls this; it exists to compare the two forms.
+ */
+#define TAH_HADAMARD_BUTTERFLY 0
+#define TAH_HADAMARD_MFMA 1
+tah_status_t tah_hadamard(const void* x, tah_dtype_t x_dtype, int64_t n_tiles, int tile, int method, float* y,
+                          void* stream);
+
 /* Waits for `stream`, then copies the device status word of the last
  * tah_decode or tah_naive_decode on this workspace into *out (TAH_OK or
  * TAH_ERR_BAD_PAYLOAD). */

@@ -145,3 +145,16 @@ def test_naive_argument_errors_without_device():
     assert dec(P=0) == 1 and dec(y=0) == 1 and dec(ws=0) == 1 and dec(dt=2) == 1 and dec(bits=0) == 1
     with pytest.raises(tah.TahError):
         tah.naive_payload_bytes(10, 20)
+
+
+def test_hadamard_argument_errors_without_device():
+    L = tah.lib()
+    v = ctypes.c_void_p
+    had = lambda x=16, dt=1, n=10, G=64, m=0, y=16: L.tah_hadamard(v(x), dt, n, G, m, v(y), v(0))
+    assert had(G=16) == 1 and had(G=256) == 1 and had(G=48) == 1
+    assert had(m=2) == 1 and had(m=-1) == 1 and had(dt=3) == 1 and had(n=-1) == 1
+    assert had(x=0) == 1 and had(y=0) == 1 and had(x=8) == 1 and had(y=4) == 1
+    # the matrix-core form exists only for bf16 tiles of 64
+    assert had(m=1, G=32) == 2 and had(m=1, G=128) == 2 and had(m=1, dt=0) == 2
+    # nothing to do: no pointer is needed and no device is touched
+    assert had(n=0, x=0, y=0) == 0 and had(n=0, x=0, y=0, m=1) == 0
