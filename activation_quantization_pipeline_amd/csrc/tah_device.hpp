@@ -409,17 +409,11 @@ template <int G, typename T, int NT>
 __device__ __forceinline__ void group_load(const uint8_t* __restrict__ src, int n_tiles, GroupRegs<G, T>& r) {
   using R = TileRow<G, T>;
   const uint4* s = reinterpret_cast<const uint4*>(src);
-  const int nchunks = n_tiles * R::kChunks;
-  if (n_tiles == NT) {
+  // One straight-line path for full and partial groups (n_tiles >= 1): a chunk
+  // past the end reloads the last one, which group_to_lds never stores.
+  const int last = n_tiles * R::kChunks - 1;
 #pragma unroll
-    for (int i = 0; i < R::kChunks; ++i) r.c[i] = s[threadIdx.x + i * NT];
-  } else {
-#pragma unroll
-    for (int i = 0; i < R::kChunks; ++i) {
-      const int c = threadIdx.x + i * NT;
-      r.c[i] = c < nchunks ? s[c] : make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
+  for (int i = 0; i < R::kChunks; ++i) r.c[i] = s[min((int)threadIdx.x + i * NT, last)];
 }
 
 // Makes the compiler wait for the loads of r here (an empty asm that reads them).
@@ -474,10 +468,14 @@ __device__ __forceinline__ void stage_out(const uint8_t* lds, uint8_t* __restric
   const int nchunks = n_tiles * R::kChunks;
   const uint8_t* base = lds + (threadIdx.x / R::kChunks) * R::kStride + (threadIdx.x % R::kChunks) * 16;
   uint4* d = reinterpret_cast<uint4*>(dst) + threadIdx.x;
+  // every LDS read first (rows past n_tiles hold stale data and are not
+  // stored), so one wait covers them all instead of one per store
+  uint4 buf[R::kChunks];
+#pragma unroll
+  for (int i = 0; i < R::kChunks; ++i) buf[i] = *reinterpret_cast<const uint4*>(base + i * (NT / R::kChunks) * R::kStride);
 #pragma unroll
   for (int i = 0; i < R::kChunks; ++i) {
-    if (n_tiles == NT || (int)threadIdx.x + i * NT < nchunks)
-      d[i * NT] = *reinterpret_cast<const uint4*>(base + i * (NT / R::kChunks) * R::kStride);
+    if (n_tiles == NT || (int)threadIdx.x + i * NT < nchunks) d[i * NT] = buf[i];
   }
 }
 

@@ -349,3 +349,26 @@ def test_determinism_and_tile_entropy_api():
     h = tah.tile_entropy(xt, w.params).cpu().numpy()
     st = oracle.tile_stats(x[:256], synth.Params(tile=64, tokens_per_sample=0, bit_budget=3.5, candidates=(2, 3, 4, 8)))
     assert np.array_equal(h[:st["H"].size].view(np.uint32), st["H"].view(np.uint32))
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_flagged_tiles_per_group(dtype):
+    """Groups of 64 tile-64 tiles (one wavefront's work) with 0, 1, ..., 12
+    flagged tiles each, pivots at the first, the last and other elements,
+    spikes of both signs, and a ragged last group."""
+    rng = np.random.default_rng(17)
+    G, n_tiles, hidden = 64, 64 * 26 + 40, 512
+    x = rng.standard_normal((n_tiles, G)) * 0.5
+    for g in range((n_tiles + 63) // 64):
+        tiles = np.arange(64 * g, min(64 * g + 64, n_tiles))
+        for i, t in enumerate(rng.permutation(tiles)[:(g + 5) % 13]):
+            pos = (0, G - 1, int(rng.integers(1, G - 1)))[i % 3]
+            x[t, pos] = (40.0 + 10 * rng.random()) * (1 if i % 2 else -1)
+    x = x.reshape(-1, hidden)
+    x = x.astype(np.float32) if dtype == synth.F32 else synth.f32_to_bf16_bits(x)
+    for p in (P(tile=G, tokens_per_sample=0, bit_budget=3.0, candidates=(3, 4, 8), tau=2.0),
+              P(tile=G, tokens_per_sample=0, bit_budget=3.6, candidates=(3, 4), tau=2.0)):
+        R, _ = run_case(x, p, f"flagged per group {dtype} budget {p.bit_budget}")
+        y_ref16 = oracle.decode(R, x.shape[0], hidden, p, oracle.BF16)
+        y16, _ = tah.roundtrip(to_dev(x), p, torch.bfloat16)
+        assert_decoded_equal(to_host(y16), y_ref16, R, oracle.plan(x.shape[0], hidden, p), "bf16 out")
