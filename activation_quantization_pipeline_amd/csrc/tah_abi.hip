@@ -108,6 +108,13 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   w = align256(w + 4 * (mixed ? o->nblocks : 0));
   o->ws_bitmap = w;
   w = align256(w + 8 * (mixed ? o->nblocks : 0));
+  // per sample: a count, a pad word, then the (key, index) pairs whose key
+  // matches the threshold's prefix after the second entropy pass (ties at the
+  // threshold are broken among them)
+  o->ncand = o->N < kMaxCand ? o->N : kMaxCand;
+  o->cand_stride = 2 + 2 * o->ncand;
+  o->ws_cand = w;
+  w = align256(w + 4 * o->cand_stride * (mixed ? o->nsamples : 0));
   o->ws_total = w;
 
   // radix-select passes: three digits of the 32-bit entropy key, then enough

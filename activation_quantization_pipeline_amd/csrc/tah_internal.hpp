@@ -14,6 +14,11 @@ namespace tah {
 constexpr int kDigitBits = 11;
 constexpr int kBins = 1 << kDigitBits;
 constexpr int kMaxPasses = 6;
+// Candidates for breaking ties at the threshold, listed by the last entropy
+// pass: (key, tile index) pairs, at most kCandPerChunk per histogram workgroup
+// and kMaxCand per sample.
+constexpr int kCandPerChunk = 512;
+constexpr int64_t kMaxCand = 4096;
 
 struct SelectPass {
   int32_t kind;   // 0: entropy key digit, 1: tile-index digit among tied entropies
@@ -35,7 +40,8 @@ struct Plan {
   // payload layout
   int64_t off_table, off_bitmap, off_side, off_scale, off_zero, off_codes, code_bytes, total;
   // workspace layout
-  int64_t ws_status, ws_state, ws_hist, ws_H, ws_LS, ws_blockcnt, ws_table, ws_bitmap, ws_total;
+  int64_t ws_status, ws_state, ws_hist, ws_H, ws_LS, ws_blockcnt, ws_table, ws_bitmap, ws_cand, ws_total;
+  int64_t ncand, cand_stride;  // capacity of a sample's candidate list; its uint32 words
   int32_t npasses;
   SelectPass passes[kMaxPasses];
 };

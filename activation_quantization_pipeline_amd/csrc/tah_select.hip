@@ -16,14 +16,16 @@
 //              keys that still match the prefix (lanes of a wavefront that
 //              share a digit add once: entropy keys cluster) and adds it into
 //              the sample's global histogram. Three passes cover the 32-bit
-//              order-preserving entropy key; then passes over the tile index
-//              resolve ties (lower index first). Histograms rotate over three
+//              order-preserving entropy key. Histograms rotate over three
 //              buffers (read the previous, add to the current, clear the next)
 //              and states over two, so kernel boundaries are the only
 //              synchronisation: a last-workgroup ticket would need a
 //              device-scope release per workgroup, which on this multi-die part
 //              writes back the L2;
-//   k_pick   - applies the last pass: the final threshold state per sample;
+//   k_resolve - one workgroup per sample applies the last pass: the final
+//              threshold state. Ties at the threshold key are broken by tile
+//              index (lower first) by digit passes over the sample inside this
+//              workgroup, only when they occur;
 //   k_mark   - one bit per quantization tile, from its allocation tile: key
 //              above the threshold, or equal to it with an index up to the last
 //              selected tie; per-64-tile counts;
@@ -149,7 +151,8 @@ struct HistArgs {
   const uint32_t* hist_prev;   // previous pass's histograms
   uint32_t* hist_cur;          // this pass's histograms (zero on entry)
   uint32_t* hist_clear;        // the next pass's histograms, cleared here
-  int64_t N, nsamples, chunks_per_sample, k;
+  uint32_t* cand;  // per sample: count, pad, then up to ncand (key, index) pairs
+  int64_t N, nsamples, chunks_per_sample, k, ncand, cand_stride;
   SelectPass pass, prev;
   int32_t has_prev;
 };
@@ -222,6 +225,8 @@ __device__ __forceinline__ SampleState apply_pass(SampleState S, const uint32_t*
 __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
   __shared__ uint32_t lh[kBins];
   __shared__ SampleState ss;
+  __shared__ uint2 lc[kCandPerChunk];  // candidates of the last entropy pass
+  __shared__ uint32_t lcn, lbase;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t s = blockIdx.x / a.chunks_per_sample;
   const int64_t c = blockIdx.x % a.chunks_per_sample;
@@ -233,6 +238,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
     for (int64_t i = b0 + tid; i < b1; i += kHistThreads) a.hist_clear[s * kBins + i] = 0u;
   }
   for (int i = tid; i < kBins; i += kHistThreads) lh[i] = 0u;
+  if (tid == 0) lcn = 0u;
   if (tid < 64) {
     SampleState S;
     if (a.has_prev) {
@@ -247,6 +253,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
     if (tid == 0) {
       ss = S;
       if (c == 0) a.st_cur[s] = S;
+      if (c == 0 && !a.has_prev) a.cand[s * a.cand_stride] = 0u;  // appended to by the last pass
     }
   }
   __syncthreads();
@@ -276,6 +283,19 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
         digit = (uu >> a.pass.shift) & dmask;
       }
     }
+    if (a.pass.kind == 0 && a.pass.last_h) {
+      // the keys matching the prefix, a superset of the threshold's ties, into
+      // this workgroup's list (LDS, then its own global region)
+      const uint64_t wm = ballot(want);
+      if (wm != 0) {
+        const int leader = __ffsll((unsigned long long)wm) - 1;
+        uint32_t base = 0;
+        if (lane == leader) base = atomicAdd(&lcn, (uint32_t)__popcll(wm));
+        base = (uint32_t)__shfl((int)base, leader, 64);
+        const uint32_t pos = base + lanes_below(wm);
+        if (want && pos < (uint32_t)kCandPerChunk) lc[pos] = make_uint2(orderable(hv[i]), (uint32_t)u);
+      }
+    }
     // lanes with the same digit as the first remaining lane add together (twice),
     // the rest one by one
 #pragma unroll
@@ -294,13 +314,96 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
   __syncthreads();
   for (int i = tid; i < kBins; i += kHistThreads)
     if (lh[i]) atomicAdd(&a.hist_cur[s * kBins + i], lh[i]);
+  if (a.pass.kind == 0 && a.pass.last_h) {
+    // one reservation in the sample's list per workgroup; a count above the
+    // list's capacity (or a workgroup past kCandPerChunk) marks it overflowed
+    const uint32_t n = lcn;
+    if (n != 0) {
+      uint32_t* cl = a.cand + s * a.cand_stride;
+      // (ncand + 1 per overflowing workgroup keeps the sum below 2^32 for any N < 2^31)
+      if (tid == 0) lbase = atomicAdd(cl, n > (uint32_t)kCandPerChunk ? (uint32_t)(a.ncand + 1) : n);
+      __syncthreads();
+      const uint32_t base = lbase;
+      for (uint32_t i = tid; i < n && i < (uint32_t)kCandPerChunk; i += kHistThreads)
+        if ((int64_t)(base + i) < a.ncand) reinterpret_cast<uint2*>(cl + 2)[base + i] = lc[i];
+    }
+  }
 }
 
-// One wavefront per sample: the state after the last pass.
-__global__ __launch_bounds__(64) void k_pick(HistArgs a) {
+// One workgroup per sample: applies the last entropy pass, which fixes the
+// k-th largest key K and the rank r still to place among the keys equal to K.
+// When every tile with key K is selected (the usual case: entropies rarely
+// tie) that is the final state. Otherwise the r-th lowest tile index among the
+// keys equal to K is found here by digit passes over the sample's keys with an
+// LDS histogram: one launch instead of one per index digit. The digit passes
+// run over the (key, index) pairs that the last entropy pass listed (those
+// matching the threshold's prefix: 871 of the 1048576 keys of the 8192 x 8192
+// GeLU tensor); only when the list overflowed does this workgroup scan the
+// whole sample.
+struct ResolveArgs {
+  const float* H;
+  const SampleState* st_prev;
+  SampleState* st_out;
+  const uint32_t* hist_last;
+  const uint32_t* cand;
+  int64_t N, ncand, cand_stride;
+  SelectPass last;
+  int32_t nidx;
+  SelectPass idx[kMaxPasses];
+};
+
+constexpr int kResolveThreads = 1024;
+
+__global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ SampleState ss;
+  __shared__ uint2 lk[kMaxCand];  // the sample's candidate list
+  const int tid = threadIdx.x;
   const int64_t s = blockIdx.x;
-  const SampleState S = apply_pass(a.st_prev[s], a.hist_prev + s * kBins, a.prev);
-  if (threadIdx.x == 0) a.st_cur[s] = S;
+  if (tid < 64) {
+    const SampleState S = apply_pass(a.st_prev[s], a.hist_last + s * kBins, a.last);
+    if (tid == 0) ss = S;
+  }
+  __syncthreads();
+  SampleState S = ss;
+  if (!S.tie_all) {
+    const float* h = a.H + s * a.N;
+    const uint32_t* cl = a.cand + s * a.cand_stride;
+    const int64_t nc = cl[0];
+    const bool listed = nc <= a.ncand;  // else scan the whole sample
+    const int64_t n = listed ? nc : a.N;
+    if (listed) {
+      for (int64_t i = tid; i < nc; i += kResolveThreads) lk[i] = reinterpret_cast<const uint2*>(cl + 2)[i];
+      __syncthreads();
+    }
+    for (int p = 0; p < a.nidx; ++p) {
+      const SelectPass ps = a.idx[p];
+      for (int i = tid; i < kBins; i += kResolveThreads) lh[i] = 0u;
+      __syncthreads();
+      const int hs = ps.shift + ps.width;  // index bits above the current digit
+      const uint32_t dmask = (1u << ps.width) - 1u;
+      for (int64_t i = tid; i < n; i += kResolveThreads) {
+        uint32_t key, uu;
+        if (listed) {
+          key = lk[i].x;
+          uu = lk[i].y;
+        } else {
+          key = orderable(h[i]);
+          uu = (uint32_t)i;
+        }
+        if (key == S.key && (hs >= 32 || (uu >> hs) == (S.upos >> hs)))
+          atomicAdd(&lh[(uu >> ps.shift) & dmask], 1u);
+      }
+      __syncthreads();
+      if (tid < 64) {
+        const SampleState T = apply_pass(S, lh, ps);
+        if (tid == 0) ss = T;
+      }
+      __syncthreads();
+      S = ss;
+    }
+  }
+  if (tid == 0) a.st_out[s] = S;
 }
 
 // ------------------------------------------------------------------ mark ----
@@ -403,9 +506,16 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   h.nsamples = pl.nsamples;
   h.k = pl.k;
   h.chunks_per_sample = (pl.N + kHistChunk - 1) / kHistChunk;
+  h.cand = reinterpret_cast<uint32_t*>(w + pl.ws_cand);
+  h.ncand = pl.ncand;
+  h.cand_stride = pl.cand_stride;
   const int64_t nwg = h.chunks_per_sample * pl.nsamples;
-  // pass p: state p in states[p % 2], histogram p in hists[p % 3] (zeroed by k_stats for p = 0)
-  for (int p = 0; p < pl.npasses; ++p) {
+  // entropy-key passes; pass p: state p in states[p % 2], histogram p in
+  // hists[p % 3] (zeroed by k_stats for p = 0). The tile-index passes that
+  // follow them in the plan run inside k_resolve.
+  int nkey = 0;
+  while (nkey < pl.npasses && pl.passes[nkey].kind == 0) ++nkey;
+  for (int p = 0; p < nkey; ++p) {
     h.pass = pl.passes[p];
     h.has_prev = p > 0;
     h.prev = p > 0 ? pl.passes[p - 1] : pl.passes[p];
@@ -418,18 +528,25 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  // the final state (after the last pass) goes to states[npasses % 2]
-  const int p = pl.npasses;
-  h.prev = pl.passes[p - 1];
-  h.st_prev = states + ((p + 1) % 2) * pl.nsamples;
-  h.st_cur = states + (p % 2) * pl.nsamples;
-  h.hist_prev = hists + ((p + 2) % 3) * hsz;
-  hipLaunchKernelGGL(k_pick, dim3((unsigned)pl.nsamples), dim3(64), 0, st, h);
+  // the final state goes to states[nkey % 2]
+  ResolveArgs rs;
+  rs.H = h.H;
+  rs.st_prev = states + ((nkey + 1) % 2) * pl.nsamples;
+  rs.st_out = states + (nkey % 2) * pl.nsamples;
+  rs.hist_last = hists + ((nkey + 2) % 3) * hsz;
+  rs.cand = h.cand;
+  rs.N = pl.N;
+  rs.ncand = pl.ncand;
+  rs.cand_stride = pl.cand_stride;
+  rs.last = pl.passes[nkey - 1];
+  rs.nidx = pl.npasses - nkey;
+  for (int i = 0; i < rs.nidx; ++i) rs.idx[i] = pl.passes[nkey + i];
+  hipLaunchKernelGGL(k_resolve, dim3((unsigned)pl.nsamples), dim3(kResolveThreads), 0, st, rs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   MarkArgs m;
   m.H = h.H;
-  m.st = h.st_cur;
+  m.st = rs.st_out;
   m.bitmap = reinterpret_cast<uint32_t*>(P ? P + pl.off_bitmap : w + pl.ws_bitmap);
   m.blockcnt = reinterpret_cast<uint32_t*>(w + pl.ws_blockcnt);
   m.tiles = pl.tiles;

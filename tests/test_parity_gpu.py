@@ -372,3 +372,31 @@ def test_flagged_tiles_per_group(dtype):
         y_ref16 = oracle.decode(R, x.shape[0], hidden, p, oracle.BF16)
         y16, _ = tah.roundtrip(to_dev(x), p, torch.bfloat16)
         assert_decoded_equal(to_host(y16), y_ref16, R, oracle.plan(x.shape[0], hidden, p), "bf16 out")
+
+
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_threshold_inside_a_large_tie(dtype):
+    """One sample of 8192 tiles (two digits of tile index): 30% flat tiles
+    (highest entropy), 60% copies of one tile (all the same entropy), 10% spiky
+    tiles (lowest). At budget 3.5 over {3, 4} the 4096 selected tiles end inside
+    the tied class, so the lowest-index tied tiles must be the ones selected."""
+    rng = np.random.default_rng(23)
+    T, H, G = 512, 1024, 64
+    tiles = np.empty((T * H // G, G))
+    n = tiles.shape[0]
+    kind = rng.permutation(np.repeat([0, 1, 2], [int(0.3 * n), int(0.6 * n), n - int(0.3 * n) - int(0.6 * n)]))
+    tied = np.where(np.arange(G) % 2 == 0, 1.0, 0.0) * np.linspace(0.5, 1.5, G)
+    for t in range(n):
+        if kind[t] == 0:
+            tiles[t] = rng.uniform(0.9, 1.1, G) * rng.choice([-1, 1], G)
+        elif kind[t] == 1:
+            tiles[t] = tied
+        else:
+            tiles[t] = rng.standard_normal(G) * 0.01
+            tiles[t, rng.integers(G)] = 5.0
+    x = tiles.reshape(T, H)
+    x = x.astype(np.float32) if dtype == synth.F32 else synth.f32_to_bf16_bits(x)
+    p = P(tile=G, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0)
+    pl = oracle.plan(T, H, p)
+    assert pl["atiles_per_sample"] == n and pl["k"] == n // 2
+    run_case(x, p, f"large tie {dtype}")
