@@ -101,24 +101,24 @@ __device__ __forceinline__ void region_of(const DecArgs& a, int64_t g, const Dec
 }
 
 // Region bytes of a group go through registers in 16-byte chunks: the region
-// holds at most NT * G bytes (8-bit codes), plus one chunk of misalignment.
-// (A native 4 x u32 vector, not the uint4 struct: struct copies become
-// memcpy and keep the array in scratch memory.)
+// holds at most NT * G * MAXB / 8 bytes (codes of at most MAXB bits), plus one
+// chunk of misalignment. (A native 4 x u32 vector, not the uint4 struct:
+// struct copies become memcpy and keep the array in scratch memory.)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-template <int G, int NT>
+template <int G, int NT, int MAXB>
 struct RegionRegs {
-  static constexpr int kChunks = (NT * G + 16 + 16 * NT - 1) / (16 * NT);
+  static constexpr int kChunks = (NT * G * MAXB / 8 + 16 + 16 * NT - 1) / (16 * NT);
   u32x4 c[kChunks];
 };
 
-template <int G, int NT>
-__device__ __forceinline__ void load_region(const DecArgs& a, int64_t rs, int rlen, RegionRegs<G, NT>& r) {
+template <int G, int NT, int MAXB>
+__device__ __forceinline__ void load_region(const DecArgs& a, int64_t rs, int rlen, RegionRegs<G, NT, MAXB>& r) {
   const int64_t base = rs & ~(int64_t)15;
   const int nchunks = (int)((rs - base + rlen + 15) >> 4);
   const int64_t last = (a.len >> 4) - 1;  // the payload's last whole chunk (bounds on a corrupt table)
 #pragma unroll
-  for (int i = 0; i < RegionRegs<G, NT>::kChunks; ++i) {
+  for (int i = 0; i < RegionRegs<G, NT, MAXB>::kChunks; ++i) {
     const int c = (int)threadIdx.x + i * NT;
     int64_t q = (base >> 4) + (c < nchunks ? c : 0);
     q = q < last ? q : last;
@@ -127,17 +127,24 @@ __device__ __forceinline__ void load_region(const DecArgs& a, int64_t rs, int rl
   }
 }
 
-template <int G, typename TOut>
+// MAXB: the widest code the payload can hold (4 or 8 bits), which sizes the
+// code region in LDS and in registers; fewer LDS bytes per workgroup let more
+// workgroups share a compute unit.
+template <int G, typename TOut, int MAXB>
 __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   constexpr int NT = 64;
   constexpr int V = G / 16;     // elements per lane in a 16-lane transform group
   constexpr int kCoop = 8;      // flagged tiles per round
   constexpr int kSlot = G + 4;  // fp32 slot stride
   using RO = TileRow<G, TOut>;
-  using RR = RegionRegs<G, NT>;
+  using RR = RegionRegs<G, NT, MAXB>;
   __shared__ __attribute__((aligned(16))) uint8_t ys[NT * RO::kStride];
+  // The code region, and once every lane has unpacked its codes, the fp32
+  // slots of the flagged tiles' transforms (the region is not read again
+  // before the next group is written there).
   __shared__ __attribute__((aligned(16))) u32x4 region[NT * RR::kChunks];
-  __shared__ __attribute__((aligned(16))) float ts[kCoop * kSlot];
+  static_assert(sizeof(region) >= sizeof(float) * kCoop * kSlot, "the slots fit in the region buffer");
+  float* ts = reinterpret_cast<float*>(region);
   __shared__ uint32_t flist[NT];
 
   const int lane = threadIdx.x;
@@ -217,6 +224,7 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     const int slot = (int)lanes_below(fmask);
     if (act && !flag) lds_write_tile<G, TOut>(ys + lane * RO::kStride, v);
     if (nf != 0) {
+      __syncthreads();  // every code read from the region before a slot overwrites it
       if (act && flag) flist[slot] = (uint32_t)lane | ((uint32_t)piv << 8);
       // rounds of kCoop flagged tiles: owners fill the slots, 16-lane groups
       // apply H^T / G and undo the swap into the tile's row
@@ -271,14 +279,19 @@ static int dec_cu_count() {
   return cus;
 }
 
-template <int G, typename TOut>
-static hipError_t launch_dec_t(const DecArgs& a, hipStream_t st) {
-  static const int per_cu = dec_wgs_per_cu(k_decode<G, TOut>);
+template <int G, typename TOut, int MAXB>
+static hipError_t launch_dec_b(const DecArgs& a, hipStream_t st) {
+  static const int per_cu = dec_wgs_per_cu(k_decode<G, TOut, MAXB>);
   const int64_t ngroups = a.tiles > 0 ? (a.tiles + 63) / 64 : 1;
   const int64_t resident = (int64_t)per_cu * dec_cu_count();
   const int64_t nwg = ngroups < resident ? ngroups : resident;
-  hipLaunchKernelGGL((k_decode<G, TOut>), dim3((unsigned)nwg), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((k_decode<G, TOut, MAXB>), dim3((unsigned)nwg), dim3(64), 0, st, a);
   return hipGetLastError();
+}
+
+template <int G, typename TOut>
+static hipError_t launch_dec_t(const DecArgs& a, hipStream_t st) {
+  return a.b_hi <= 4 ? launch_dec_b<G, TOut, 4>(a, st) : launch_dec_b<G, TOut, 8>(a, st);
 }
 
 hipError_t launch_decode(const Plan& pl, const void* payload, void* y, int y_dtype, void* ws, hipStream_t st) {
