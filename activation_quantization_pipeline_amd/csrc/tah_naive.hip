@@ -30,16 +30,22 @@ struct NaiveArgs {
 
 constexpr int kNaiveThreads = 256;  // groups per workgroup
 
+// The B words of a packed group to dst (LDS, 4 B-aligned; 16-byte aligned
+// when B is a multiple of 4).
 template <int B>
-__device__ __forceinline__ void pack_store(const uint32_t (&q)[32], uint8_t* dst) {
+__device__ __forceinline__ void pack_store(const uint32_t (&q)[32], uint32_t* dst) {
   uint32_t w[B];
   pack_codes<32, B>(q, w);
-  if constexpr (B % 2 == 0) {
+  if constexpr (B % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < B / 4; ++i)
+      reinterpret_cast<uint4*>(dst)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  } else if constexpr (B % 2 == 0) {
 #pragma unroll
     for (int i = 0; i < B / 2; ++i) reinterpret_cast<uint2*>(dst)[i] = make_uint2(w[2 * i], w[2 * i + 1]);
   } else {
 #pragma unroll
-    for (int i = 0; i < B; ++i) reinterpret_cast<uint32_t*>(dst)[i] = w[i];
+    for (int i = 0; i < B; ++i) dst[i] = w[i];
   }
 }
 
@@ -138,9 +144,9 @@ __global__ __launch_bounds__(kNaiveThreads) void k_naive_encode(NaiveArgs a) {
   naive_stage_in<TIn, kStride>(a.in + e0 * Elem<TIn>::kBytes, ne, rows);
   __syncthreads();
   const int64_t g = gbase + tid;
-  if (g >= a.ngroups) return;
+  const bool act = g < a.ngroups;
   float v[32];
-  lds_read_tile<32, TIn>(rows + tid * kStride, v);
+  if (act) lds_read_tile<32, TIn>(rows + tid * kStride, v);
   const float lo = -(float)(1 << (a.bits - 1)), hi = (float)((1 << (a.bits - 1)) - 1);
   uint32_t q[32];
 #pragma unroll
@@ -148,8 +154,13 @@ __global__ __launch_bounds__(kNaiveThreads) void k_naive_encode(NaiveArgs a) {
     const float r = __builtin_rintf(v[k] * a.cq);  // round half to even
     q[k] = (uint32_t)(int32_t)__builtin_amdgcn_fmed3f(lo, r, hi);
   }
-  uint8_t* dst = a.out + 256 + g * 4 * a.bits;
-  switch (a.bits) {
+  __syncthreads();  // every row read: the buffer now takes the packed groups
+  // the workgroup's groups are contiguous in the payload: packed into LDS in
+  // group order, then stored with 16-byte coalesced writes
+  uint32_t* pw = reinterpret_cast<uint32_t*>(rows);
+  if (act) {
+    uint32_t* dst = pw + tid * a.bits;
+    switch (a.bits) {
     case 2: pack_store<2>(q, dst); break;
     case 3: pack_store<3>(q, dst); break;
     case 4: pack_store<4>(q, dst); break;
@@ -165,7 +176,15 @@ __global__ __launch_bounds__(kNaiveThreads) void k_naive_encode(NaiveArgs a) {
     case 14: pack_store<14>(q, dst); break;
     case 15: pack_store<15>(q, dst); break;
     default: pack_store<16>(q, dst); break;
+    }
   }
+  __syncthreads();
+  const int64_t ng = a.ngroups - gbase < kNaiveThreads ? a.ngroups - gbase : kNaiveThreads;
+  const int nw = (int)ng * a.bits;  // words of this workgroup's groups
+  uint32_t* out = reinterpret_cast<uint32_t*>(a.out + 256 + gbase * 4 * a.bits);  // 16-byte aligned
+  const int nq = nw >> 2;
+  for (int i = tid; i < nq; i += kNaiveThreads) reinterpret_cast<uint4*>(out)[i] = reinterpret_cast<const uint4*>(pw)[i];
+  for (int i = 4 * nq + tid; i < nw; i += kNaiveThreads) out[i] = pw[i];
 }
 
 template <typename TOut>
