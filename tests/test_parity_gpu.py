@@ -400,3 +400,39 @@ def test_threshold_inside_a_large_tie(dtype):
     pl = oracle.plan(T, H, p)
     assert pl["atiles_per_sample"] == n and pl["k"] == n // 2
     run_case(x, p, f"large tie {dtype}")
+
+
+def test_threshold_inside_a_tie_across_workgroups():
+    """One sample of 40960 tiles (three histogram workgroups of the select):
+    20400 flat tiles above, 200 copies of one tile spread over the sample, the
+    rest spiky below; k = 20480, so 80 of the 200 tied tiles (the lowest
+    indices) are selected, from candidate lists that three workgroups append
+    to the same sample's list."""
+    rng = np.random.default_rng(29)
+    T, H, G = 640, 4096, 64
+    n = T * H // G
+    kind = np.full(n, 2)
+    idx = rng.permutation(n)
+    kind[idx[:20400]] = 0
+    kind[idx[20400:20600]] = 1
+    tiles = np.empty((n, G))
+    tied = np.where(np.arange(G) % 2 == 0, 1.0, 0.0) * np.linspace(0.5, 1.5, G)
+    for t in range(n):
+        if kind[t] == 0:
+            tiles[t] = rng.uniform(0.9, 1.1, G) * rng.choice([-1, 1], G)
+        elif kind[t] == 1:
+            tiles[t] = tied
+        else:
+            tiles[t] = rng.standard_normal(G) * 0.01
+            tiles[t, rng.integers(G)] = 5.0
+    x = tiles.reshape(T, H).astype(np.float32)
+    p = P(tile=G, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0)
+    assert oracle.plan(T, H, p)["k"] == 20480
+    R, _ = run_case(x, p, "tie across workgroups")
+    # the width map: every flat tile and the 80 lowest-index tied tiles are at 4 bits
+    pl = oracle.plan(T, H, p)
+    bm = R[pl["off_bitmap"]:pl["off_bitmap"] + 8 * pl["nblocks"]].view(np.uint64)
+    hi = np.unpackbits(bm.view(np.uint8), bitorder="little")[:n].astype(bool)
+    tied_idx = np.flatnonzero(kind == 1)
+    assert hi[kind == 0].all() and not hi[kind == 2].any()
+    assert hi[tied_idx[:80]].all() and not hi[tied_idx[80:]].any()
