@@ -258,7 +258,6 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
   }
   __syncthreads();
   const SampleState S = ss;
-  if (a.pass.kind == 1 && S.tie_all) return;  // no tie to resolve in this sample
   const int hs = a.pass.shift + a.pass.width;  // bits above the current digit
   const uint32_t dmask = (1u << a.pass.width) - 1u;
   float hv[kHistPerThread];  // all loads in flight before the first use
@@ -272,20 +271,14 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
     const int64_t u = u0 + i * kHistThreads + tid;
     bool want = false;
     uint32_t digit = 0;
-    if (u < a.N) {
+    if (u < a.N) {  // entropy-key digits only: tile-index digits run in k_resolve
       const uint32_t key = orderable(hv[i]);
-      if (a.pass.kind == 0) {
-        want = hs >= 32 || (key >> hs) == (S.key >> hs);
-        digit = (key >> a.pass.shift) & dmask;
-      } else {
-        const uint32_t uu = (uint32_t)u;
-        want = key == S.key && (hs >= 32 || (uu >> hs) == (S.upos >> hs));
-        digit = (uu >> a.pass.shift) & dmask;
-      }
+      want = hs >= 32 || (key >> hs) == (S.key >> hs);
+      digit = (key >> a.pass.shift) & dmask;
     }
-    if (a.pass.kind == 0 && a.pass.last_h) {
+    if (a.pass.last_h) {
       // the keys matching the prefix, a superset of the threshold's ties, into
-      // this workgroup's list (LDS, then its own global region)
+      // this workgroup's LDS list (appended to the sample's list at the end)
       const uint64_t wm = ballot(want);
       if (wm != 0) {
         const int leader = __ffsll((unsigned long long)wm) - 1;
@@ -314,7 +307,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
   __syncthreads();
   for (int i = tid; i < kBins; i += kHistThreads)
     if (lh[i]) atomicAdd(&a.hist_cur[s * kBins + i], lh[i]);
-  if (a.pass.kind == 0 && a.pass.last_h) {
+  if (a.pass.last_h) {
     // one reservation in the sample's list per workgroup; a count above the
     // list's capacity (or a workgroup past kCandPerChunk) marks it overflowed
     const uint32_t n = lcn;
