@@ -374,13 +374,15 @@ static int wgs_per_cu(K kernel, int threads) {
   return n;
 }
 
+// Compute units of the device current at the first call (initialised once,
+// safe under concurrent first calls).
 static int cu_count() {
-  static int cus = 0;
-  if (!cus) {
-    int dev = 0;
+  static const int cus = [] {
+    int dev = 0, n = 0;
     (void)hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1) cus = 256;
-  }
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
+    return n;
+  }();
   return cus;
 }
 
