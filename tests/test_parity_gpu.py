@@ -436,3 +436,36 @@ def test_threshold_inside_a_tie_across_workgroups():
     tied_idx = np.flatnonzero(kind == 1)
     assert hi[kind == 0].all() and not hi[kind == 2].any()
     assert hi[tied_idx[:80]].all() and not hi[tied_idx[80:]].any()
+
+
+def random_config(seed):
+    """A seeded random shape and parameter set within the library's limits."""
+    r = np.random.default_rng(1000 + seed)
+    G = int(r.choice([32, 64, 128]))
+    M = int(r.integers(1, 17))
+    hidden = G * M
+    tokens = int(r.integers(1, 200))
+    divisors = [d for d in range(1, tokens + 1) if tokens % d == 0]
+    S = int(r.choice([0] + divisors))
+    kAs = [k for k in range(1, M + 1) if M % k == 0]
+    A = G * int(r.choice(kAs))
+    n_c = int(r.integers(1, 5))
+    cands = tuple(sorted(int(c) for c in r.choice(np.arange(1, 9), size=n_c, replace=False)))
+    budget = float(np.float32(r.uniform(cands[0], cands[-1] + 0.5)))
+    tau = float(r.choice([0.0, 0.5, 1.0, 2.0, 4.0, math.inf]))
+    dtype = synth.F32 if r.random() < 0.5 else synth.BF16
+    x = synth.random_tensor(tokens, hidden, dtype, 2000 + seed, scale=float(r.choice([1e-3, 1.0, 50.0])),
+                            n_out=int(r.integers(0, 4)), mult=float(r.choice([5.0, 40.0, 300.0])))
+    p = P(tile=G, tokens_per_sample=S, bit_budget=budget, candidates=cands, tau=tau, alloc_tile=A)
+    return x, p
+
+
+@pytest.mark.parametrize("seed", range(120))
+def test_random_configurations(seed):
+    x, p = random_config(seed)
+    R, y_ref = run_case(x, p, f"random config {seed}")
+    if x.dtype == np.uint16:
+        tokens, hidden = x.shape
+        y16, _ = tah.roundtrip(to_dev(x), p, torch.bfloat16)
+        assert_decoded_equal(to_host(y16), oracle.decode(R, tokens, hidden, p, oracle.BF16), R,
+                             oracle.plan(tokens, hidden, p), f"random config {seed} bf16 out")
