@@ -164,14 +164,43 @@ def _torch_dtype(code: int) -> torch.dtype:
     return torch.float32 if code == TAH_DTYPE_F32 else torch.bfloat16
 
 
-def _ptr(t):
-    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+def _nbytes(t: torch.Tensor) -> int:
+    return t.numel() * t.element_size()
 
 
-def _stream(stream):
+def _dev(t, what: str) -> torch.device:
+    """The GPU a call runs on: that of its main tensor (a host pointer handed
+    to a kernel would be a device memory fault, so CPU tensors are refused)."""
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TahError(1, f"{what} must be a GPU tensor")
+    return t.device
+
+
+def _ptr(t, dev: torch.device | None = None, what: str = "tensor"):
+    """Device address of a contiguous GPU tensor on `dev` (NULL for None)."""
+    if t is None:
+        return ctypes.c_void_p(0)
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TahError(1, f"{what} must be a GPU tensor")
+    if dev is not None and t.device != dev:
+        raise TahError(1, f"{what} is on {t.device}, the call runs on {dev}")
+    if not t.is_contiguous():
+        raise TahError(1, f"{what} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, dev: torch.device | None = None):
     if stream is None:
-        stream = torch.cuda.current_stream()
+        stream = torch.cuda.current_stream(dev)
+    elif dev is not None and stream.device != dev:
+        raise TahError(1, f"stream is on {stream.device}, the call runs on {dev}")
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, n: int, what: str) -> None:
+    """The kernels write n elements of t: it must hold them."""
+    if t.numel() < n:
+        raise TahError(3, f"{what} holds {t.numel()} elements, the call writes {n}")
 
 
 def _size_query(fn: str, tokens: int, hidden: int, p) -> int:
@@ -228,13 +257,16 @@ def encode(x: torch.Tensor, p, payload: torch.Tensor | None = None, ws: torch.Te
            stream=None) -> torch.Tensor:
     """tah_encode: x [tokens, hidden] -> payload (uint8 device tensor)."""
     tokens, hidden = _shape(x)
+    dev = _dev(x, "x")
     if payload is None:
-        payload = alloc_payload(tokens, hidden, p, x.device)
+        payload = alloc_payload(tokens, hidden, p, dev)
     if ws is None:
-        ws = alloc_workspace(tokens, hidden, p, x.device)
+        ws = alloc_workspace(tokens, hidden, p, dev)
     cp = _cparams(p)
-    rc = lib().tah_encode(_ptr(x), _dtype_code(x.dtype), tokens, hidden, ctypes.byref(cp), _ptr(payload),
-                          payload.numel(), _ptr(ws), ws.numel(), _stream(stream))
+    with torch.cuda.device(dev):
+        rc = lib().tah_encode(_ptr(x, dev, "x"), _dtype_code(x.dtype), tokens, hidden, ctypes.byref(cp),
+                              _ptr(payload, dev, "payload"), _nbytes(payload), _ptr(ws, dev, "ws"), _nbytes(ws),
+                              _stream(stream, dev))
     _check(rc, "tah_encode")
     return payload
 
@@ -242,13 +274,17 @@ def encode(x: torch.Tensor, p, payload: torch.Tensor | None = None, ws: torch.Te
 def decode(payload: torch.Tensor, tokens: int, hidden: int, p, y_dtype: torch.dtype = torch.float32,
            y: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """tah_decode: payload -> y [tokens, hidden] (y_dtype)."""
+    dev = _dev(payload, "payload")
     if y is None:
-        y = torch.empty((tokens, hidden), dtype=y_dtype, device=payload.device)
+        y = torch.empty((tokens, hidden), dtype=y_dtype, device=dev)
+    _need(y, int(tokens) * int(hidden), "y")
     if ws is None:
-        ws = alloc_workspace(tokens, hidden, p, payload.device)
+        ws = alloc_workspace(tokens, hidden, p, dev)
     cp = _cparams(p)
-    rc = lib().tah_decode(_ptr(payload), payload.numel(), int(tokens), int(hidden), ctypes.byref(cp), _ptr(y),
-                          _dtype_code(y.dtype), _ptr(ws), ws.numel(), _stream(stream))
+    with torch.cuda.device(dev):
+        rc = lib().tah_decode(_ptr(payload, dev, "payload"), _nbytes(payload), int(tokens), int(hidden),
+                              ctypes.byref(cp), _ptr(y, dev, "y"), _dtype_code(y.dtype), _ptr(ws, dev, "ws"),
+                              _nbytes(ws), _stream(stream, dev))
     _check(rc, "tah_decode")
     return y
 
@@ -258,16 +294,20 @@ def roundtrip(x: torch.Tensor, p, y_dtype: torch.dtype | None = None, payload: t
               stream=None):
     """tah_roundtrip: encode and decode in one pass. Returns (y, payload or None)."""
     tokens, hidden = _shape(x)
+    dev = _dev(x, "x")
     if y is None:
-        y = torch.empty((tokens, hidden), dtype=y_dtype or x.dtype, device=x.device)
+        y = torch.empty((tokens, hidden), dtype=y_dtype or x.dtype, device=dev)
+    _need(y, tokens * hidden, "y")
     if payload is None and write_payload:
-        payload = alloc_payload(tokens, hidden, p, x.device)
+        payload = alloc_payload(tokens, hidden, p, dev)
     if ws is None:
-        ws = alloc_workspace(tokens, hidden, p, x.device)
+        ws = alloc_workspace(tokens, hidden, p, dev)
     cp = _cparams(p)
-    rc = lib().tah_roundtrip(_ptr(x), _dtype_code(x.dtype), tokens, hidden, ctypes.byref(cp), _ptr(payload),
-                             payload.numel() if payload is not None else 0, _ptr(y), _dtype_code(y.dtype), _ptr(ws),
-                             ws.numel(), _stream(stream))
+    with torch.cuda.device(dev):
+        rc = lib().tah_roundtrip(_ptr(x, dev, "x"), _dtype_code(x.dtype), tokens, hidden, ctypes.byref(cp),
+                                 _ptr(payload, dev, "payload"), _nbytes(payload) if payload is not None else 0,
+                                 _ptr(y, dev, "y"), _dtype_code(y.dtype), _ptr(ws, dev, "ws"), _nbytes(ws),
+                                 _stream(stream, dev))
     _check(rc, "tah_roundtrip")
     return y, payload
 
@@ -276,14 +316,19 @@ def tile_entropy(x: torch.Tensor, p, h: torch.Tensor | None = None, ws: torch.Te
                  stream=None) -> torch.Tensor:
     """tah_tile_entropy: fp32 entropy of each of the tokens*hidden/A allocation tiles."""
     tokens, hidden = _shape(x)
+    dev = _dev(x, "x")
+    A = int(getattr(p, "alloc_tile", 0)) or int(p.tile)
     if h is None:
-        A = int(getattr(p, "alloc_tile", 0)) or int(p.tile)
-        h = torch.empty(tokens * (hidden // A), dtype=torch.float32, device=x.device)
+        h = torch.empty(tokens * (hidden // A), dtype=torch.float32, device=dev)
+    if h.dtype != torch.float32:
+        raise TahError(1, "h must be float32")
+    _need(h, tokens * (hidden // A), "h")
     if ws is None:
-        ws = alloc_workspace(tokens, hidden, p, x.device)
+        ws = alloc_workspace(tokens, hidden, p, dev)
     cp = _cparams(p)
-    rc = lib().tah_tile_entropy(_ptr(x), _dtype_code(x.dtype), tokens, hidden, ctypes.byref(cp), _ptr(h), _ptr(ws),
-                                ws.numel(), _stream(stream))
+    with torch.cuda.device(dev):
+        rc = lib().tah_tile_entropy(_ptr(x, dev, "x"), _dtype_code(x.dtype), tokens, hidden, ctypes.byref(cp),
+                                    _ptr(h, dev, "h"), _ptr(ws, dev, "ws"), _nbytes(ws), _stream(stream, dev))
     _check(rc, "tah_tile_entropy")
     return h
 
@@ -298,13 +343,13 @@ def naive_payload_bytes(n: int, bits: int) -> int:
 def naive_encode(g: torch.Tensor, bits: int, c: float, payload: torch.Tensor | None = None,
                  stream=None) -> torch.Tensor:
     """tah_naive_encode: gradient tensor g (any shape, contiguous) -> payload."""
-    if not g.is_contiguous():
-        raise ValueError("g must be contiguous")
+    dev = _dev(g, "g")
     n = g.numel()
     if payload is None:
-        payload = torch.zeros(naive_payload_bytes(n, bits), dtype=torch.uint8, device=g.device)
-    rc = lib().tah_naive_encode(_ptr(g), _dtype_code(g.dtype), n, int(bits), float(c), _ptr(payload),
-                                payload.numel(), _stream(stream))
+        payload = torch.empty(naive_payload_bytes(n, bits), dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().tah_naive_encode(_ptr(g, dev, "g"), _dtype_code(g.dtype), n, int(bits), float(c),
+                                    _ptr(payload, dev, "payload"), _nbytes(payload), _stream(stream, dev))
     _check(rc, "tah_naive_encode")
     return payload
 
@@ -312,12 +357,16 @@ def naive_encode(g: torch.Tensor, bits: int, c: float, payload: torch.Tensor | N
 def naive_decode(payload: torch.Tensor, n: int, bits: int, c: float, y_dtype: torch.dtype = torch.float32,
                  y: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
     """tah_naive_decode: payload -> n gradient values (y_dtype)."""
+    dev = _dev(payload, "payload")
     if y is None:
-        y = torch.empty(int(n), dtype=y_dtype, device=payload.device)
+        y = torch.empty(int(n), dtype=y_dtype, device=dev)
+    _need(y, int(n), "y")
     if ws is None:
-        ws = torch.empty(256, dtype=torch.uint8, device=payload.device)
-    rc = lib().tah_naive_decode(_ptr(payload), payload.numel(), int(n), int(bits), float(c), _ptr(y),
-                                _dtype_code(y.dtype), _ptr(ws), ws.numel(), _stream(stream))
+        ws = torch.empty(256, dtype=torch.uint8, device=dev)
+    with torch.cuda.device(dev):
+        rc = lib().tah_naive_decode(_ptr(payload, dev, "payload"), _nbytes(payload), int(n), int(bits), float(c),
+                                    _ptr(y, dev, "y"), _dtype_code(y.dtype), _ptr(ws, dev, "ws"), _nbytes(ws),
+                                    _stream(stream, dev))
     _check(rc, "tah_naive_decode")
     return y
 
@@ -329,19 +378,27 @@ HADAMARD_BUTTERFLY, HADAMARD_MFMA = 0, 1
 def hadamard(x: torch.Tensor, tile: int, method: int = HADAMARD_BUTTERFLY, y: torch.Tensor | None = None,
              stream=None) -> torch.Tensor:
     """tah_hadamard: unnormalized H_G over each contiguous tile of x -> fp32."""
-    if not x.is_contiguous() or x.numel() % tile:
-        raise ValueError("x must be contiguous and hold whole tiles")
+    dev = _dev(x, "x")
+    if x.numel() % tile:
+        raise TahError(1, "x must hold whole tiles")
     if y is None:
-        y = torch.empty(x.numel(), dtype=torch.float32, device=x.device)
-    rc = lib().tah_hadamard(_ptr(x), _dtype_code(x.dtype), x.numel() // tile, int(tile), int(method), _ptr(y),
-                            _stream(stream))
+        y = torch.empty(x.numel(), dtype=torch.float32, device=dev)
+    if y.dtype != torch.float32:
+        raise TahError(1, "y must be float32")
+    _need(y, x.numel(), "y")
+    with torch.cuda.device(dev):
+        rc = lib().tah_hadamard(_ptr(x, dev, "x"), _dtype_code(x.dtype), x.numel() // tile, int(tile), int(method),
+                                _ptr(y, dev, "y"), _stream(stream, dev))
     _check(rc, "tah_hadamard")
     return y
 
 
 def read_device_status(ws: torch.Tensor, stream=None) -> int:
     out = ctypes.c_int32()
-    _check(lib().tah_read_device_status(_ptr(ws), _stream(stream), ctypes.byref(out)), "tah_read_device_status")
+    dev = _dev(ws, "ws")
+    with torch.cuda.device(dev):
+        _check(lib().tah_read_device_status(_ptr(ws, dev, "ws"), _stream(stream, dev), ctypes.byref(out)),
+               "tah_read_device_status")
     return int(out.value)
 
 
@@ -361,7 +418,21 @@ class Codec:
         L = lib()
         self._rt, self._enc, self._dec = L.tah_roundtrip, L.tah_encode, L.tah_decode
 
+    def _bufs(self, x, payload, y, ws) -> None:
+        # GPU tensors of the sizes the calls read and write (a host pointer or a
+        # short buffer would be a device memory fault)
+        elems = self.tokens * self.hidden
+        for t, what, nbytes in ((x, "x", elems * (4 if self.x_code == TAH_DTYPE_F32 else 2)),
+                                (payload, "payload", self.payload_bytes),
+                                (y, "y", elems * (4 if self.y_code == TAH_DTYPE_F32 else 2)),
+                                (ws, "ws", self.workspace_bytes)):
+            if t is None:
+                continue
+            if not t.is_cuda or not t.is_contiguous() or _nbytes(t) < nbytes:
+                raise TahError(1, f"{what} must be a contiguous GPU tensor of at least {nbytes} bytes")
+
     def roundtrip(self, x, payload, y, ws, stream_handle: int) -> None:
+        self._bufs(x, payload, y, ws)
         rc = self._rt(x.data_ptr(), self.x_code, self.tokens, self.hidden, self._pref,
                       payload.data_ptr() if payload is not None else None, self.payload_bytes if payload is not None else 0,
                       y.data_ptr(), self.y_code, ws.data_ptr(), self.workspace_bytes, stream_handle)
@@ -369,12 +440,14 @@ class Codec:
             raise TahError(rc, "tah_roundtrip")
 
     def encode(self, x, payload, ws, stream_handle: int) -> None:
+        self._bufs(x, payload, None, ws)
         rc = self._enc(x.data_ptr(), self.x_code, self.tokens, self.hidden, self._pref, payload.data_ptr(),
                        self.payload_bytes, ws.data_ptr(), self.workspace_bytes, stream_handle)
         if rc:
             raise TahError(rc, "tah_encode")
 
     def decode(self, payload, y, ws, stream_handle: int) -> None:
+        self._bufs(None, payload, y, ws)
         rc = self._dec(payload.data_ptr(), self.payload_bytes, self.tokens, self.hidden, self._pref, y.data_ptr(),
                        self.y_code, ws.data_ptr(), self.workspace_bytes, stream_handle)
         if rc:

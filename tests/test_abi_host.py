@@ -158,3 +158,27 @@ def test_hadamard_argument_errors_without_device():
     assert had(m=1, G=32) == 2 and had(m=1, G=128) == 2 and had(m=1, dt=0) == 2
     # nothing to do: no pointer is needed and no device is touched
     assert had(n=0, x=0, y=0) == 0 and had(n=0, x=0, y=0, m=1) == 0
+
+
+def test_binding_refuses_host_tensors_before_any_device_call():
+    """A host pointer handed to a kernel would be a device memory fault: every
+    entry point of the binding refuses CPU tensors up front."""
+    import torch
+
+    p = tah.TahParams(tile=64, bit_budget=3.5, candidates=(3, 4))
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    u8 = torch.zeros(1 << 16, dtype=torch.uint8)
+    calls = [
+        lambda: tah.encode(x, p),
+        lambda: tah.roundtrip(x, p),
+        lambda: tah.tile_entropy(x, p),
+        lambda: tah.decode(u8, 4, 64, p),
+        lambda: tah.naive_encode(x, 8, 1.0),
+        lambda: tah.naive_decode(u8, 10, 8, 1.0),
+        lambda: tah.hadamard(x, 64),
+        lambda: tah.read_device_status(u8),
+        lambda: tah.Codec(4, 64, p, torch.bfloat16).roundtrip(x, u8, x, u8, 0),
+    ]
+    for i, call in enumerate(calls):
+        with pytest.raises(tah.TahError):
+            call()
