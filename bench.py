@@ -55,17 +55,29 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(bytes_alg):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs (scaled by the same counters on a plain copy), or None when the kernel
-    sources changed since the counters were taken."""
+def _profiled():
+    """The committed counter file, or None when it is missing or the kernel
+    sources changed since its counters were taken."""
     try:
         t = json.load(open(TRAFFIC_FILE))
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
-        return None
-    return t.get("traffic_bytes_per_launch")
+    return t if t.get("kernel_source_hash") == kernel_source_hash() else None
+
+
+def measured_traffic(bytes_alg):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (scaled by the same counters on a plain copy), or None when stale."""
+    t = _profiled()
+    return t.get("traffic_bytes_per_launch") if t else None
+
+
+def measured_valu():
+    """VALU lane-ops per element and VALU busy fraction of the same kernel from
+    the committed SQ counter runs, or None when stale."""
+    t = _profiled()
+    sq = t.get("sq") if t else None
+    return {"lane_ops_per_element": sq["valu_lane_ops_per_element"], "busy_frac": sq["valu_busy_frac"]} if sq else None
 
 
 def to_dev(x, torch):
@@ -194,6 +206,7 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
             "traffic": measured_traffic(bytes_step),
+            "valu": measured_valu(),  # from the SQ counters: the kernel's practical limiter
             "kernel_ms_mean": round(k_mean, 5),
             "kernel_ms_median_separate_pass": round(k_med, 5),
             "kernel_ms_min_separate_pass": round(k_min, 5),

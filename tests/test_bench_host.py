@@ -45,3 +45,13 @@ def test_committed_traffic_file_names_its_commands():
     for cmd in t["commands"]["kernel"] + t["commands"]["copy"]:
         assert "rocprofv3 --pmc" in cmd and "bench.py" in cmd
     assert abs(t["traffic_bytes_per_launch"] - t["fetch_bytes_per_launch"] - t["write_bytes_per_launch"]) <= 1
+
+
+def test_valu_figures_follow_the_same_staleness_rule(tmp_path, monkeypatch):
+    f = tmp_path / "traffic.json"
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    sq = {"valu_lane_ops_per_element": 32.5, "valu_busy_frac": 0.8}
+    f.write_text(json.dumps({"kernel_source_hash": bench.kernel_source_hash(), "sq": sq}))
+    assert bench.measured_valu() == {"lane_ops_per_element": 32.5, "busy_frac": 0.8}
+    f.write_text(json.dumps({"kernel_source_hash": "0" * 16, "sq": sq}))
+    assert bench.measured_valu() is None
