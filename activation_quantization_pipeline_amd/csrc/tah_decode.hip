@@ -12,9 +12,10 @@
 //    coalesced loads into registers;
 //  - processing: the region goes to LDS, each lane reads its code block,
 //    unpacks and dequantizes (fmaf(q, s, lo)); flagged tiles get H^T / G and
-//    the swap undone (§3.3) by 16-lane groups through fp32 LDS slots, as in
-//    the encoder; rows are written to LDS and leave it with 16-byte coalesced
-//    stores at the top of the next iteration.
+//    the swap undone (§3.3) by 16-lane groups through fp32 LDS slots (which
+//    reuse the region's buffer once every code is read); rows are written to
+//    LDS and leave it with 16-byte coalesced stores at the top of the next
+//    iteration.
 #include <type_traits>
 
 #include "tah_device.hpp"
