@@ -38,6 +38,7 @@ class _Params(ctypes.Structure):
         ("candidates", ctypes.c_uint8 * 4),
         ("tau", ctypes.c_float),
         ("alloc_tile", ctypes.c_int32),
+        ("allocator", ctypes.c_int32),
     ]
 
 
@@ -45,7 +46,7 @@ class _Plan(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in ("tokens", "hidden", "S", "nsamples", "M", "tiles", "tiles_per_sample", "nblocks")] + [
         (n, ctypes.c_int32) for n in ("G", "log2G", "b_lo", "b_hi")
     ] + [(n, ctypes.c_int64) for n in ("k", "off_table", "off_bitmap", "off_side", "off_scale", "off_zero", "off_codes", "code_bytes", "total",
-                                  "A", "kA", "MA", "atiles", "atiles_per_sample")]
+                                  "A", "kA", "MA", "atiles", "atiles_per_sample", "allocator", "R")]
 
 
 def build(force: bool = False) -> str:
@@ -83,6 +84,8 @@ def lib():
         L.tahref_quantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, P(ctypes.c_float), P(ctypes.c_float), ctypes.c_void_p]
         L.tahref_dequantize.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_float, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.tahref_allocate.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int64, ctypes.c_void_p]
+        L.tahref_greedy_lambda.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+        L.tahref_allocate_greedy.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
         L.tahref_encode.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, P(_Params), ctypes.c_void_p, ctypes.c_size_t]
         L.tahref_decode.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64, ctypes.c_int64, P(_Params), ctypes.c_void_p, ctypes.c_int]
         L.tahref_tile_stats.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_int64, P(_Params)] + [ctypes.c_void_p] * 6
@@ -107,6 +110,7 @@ def _params(p) -> _Params:
         c.candidates[i] = int(cands[i]) if i < len(cands) else 0
     c.tau = float(p.tau)
     c.alloc_tile = int(getattr(p, "alloc_tile", 0))
+    c.allocator = int(getattr(p, "allocator", 0))
     return c
 
 
@@ -187,6 +191,27 @@ def allocate(H: np.ndarray, k: int) -> np.ndarray:
     if rc:
         raise OracleError(rc, "allocate")
     return hi
+
+
+def greedy_lambda(cands) -> np.ndarray:
+    """The n-1 per-upgrade constants lambda_j of the greedy allocator (fp32)."""
+    c = np.ascontiguousarray(cands, dtype=np.uint8)
+    lam = np.zeros(max(c.size - 1, 1), np.float32)
+    rc = lib().tahref_greedy_lambda(c.size, _ptr(c), _ptr(lam))
+    if rc:
+        raise OracleError(rc, "greedy_lambda")
+    return lam[: c.size - 1]
+
+
+def allocate_greedy(H: np.ndarray, cands, R: int) -> np.ndarray:
+    """Candidate index of each of the H.size allocation tiles of one sample."""
+    H = np.ascontiguousarray(H, dtype=np.float32)
+    c = np.ascontiguousarray(cands, dtype=np.uint8)
+    level = np.zeros(H.size, dtype=np.uint8)
+    rc = lib().tahref_allocate_greedy(_ptr(H), H.size, c.size, _ptr(c), int(R), _ptr(level))
+    if rc:
+        raise OracleError(rc, "allocate_greedy")
+    return level
 
 
 def encode(x: np.ndarray, p) -> np.ndarray:

@@ -119,6 +119,7 @@ int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tah
   if (S > 0 && tokens % S) return TAHREF_ERR_INVALID_ARG;
   int64_t A = p->alloc_tile == 0 ? G : p->alloc_tile;
   if (A < G || A % G || hidden % A) return TAHREF_ERR_INVALID_ARG;
+  if (p->allocator != 0 && p->allocator != 1) return TAHREF_ERR_INVALID_ARG;
   if ((float)p->candidates[0] > p->bit_budget) return TAHREF_ERR_BUDGET_INFEASIBLE;
 
   int b_lo = p->candidates[0], b_hi = -1;
@@ -142,24 +143,49 @@ int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tah
   o->MA = hidden / A;
   o->atiles = tokens * o->MA;
   o->atiles_per_sample = S * o->MA;
-  o->b_lo = b_lo;
-  o->b_hi = b_hi;
-  if (b_hi == b_lo || o->atiles_per_sample == 0) {
-    o->k = 0;
-  } else {
-    double kk = floor(((double)p->bit_budget - (double)b_lo) * (double)o->atiles_per_sample /
-                      (double)(b_hi - b_lo));
-    o->k = (int64_t)kk;
-  }
+  o->allocator = p->allocator;
   o->nblocks = (o->tiles + 63) / 64;
-  int64_t nhi = o->k * o->kA * o->nsamples; /* quantization tiles at b_hi */
+  if (p->allocator == 0) {
+    o->b_lo = b_lo;
+    o->b_hi = b_hi;
+    if (b_hi == b_lo || o->atiles_per_sample == 0) {
+      o->k = 0;
+    } else {
+      double kk = floor(((double)p->bit_budget - (double)b_lo) * (double)o->atiles_per_sample /
+                        (double)(b_hi - b_lo));
+      o->k = (int64_t)kk;
+    }
+  } else {
+    /* greedy (tahref_allocate_greedy): every candidate may occur; b_lo and b_hi
+     * record the narrowest and the widest, and a sample may spend R bits above
+     * c_1 over its allocation tiles, R = floor((B - c_1) N), at most what
+     * every tile at the widest candidate would take */
+    const int c1 = p->candidates[0], cn = p->candidates[p->n_candidates - 1];
+    o->b_lo = c1;
+    o->b_hi = cn;
+    o->k = 0;
+    const int64_t N = o->atiles_per_sample;
+    const double r = floor(((double)p->bit_budget - (double)c1) * (double)N);
+    const int64_t cap = (int64_t)(cn - c1) * N;
+    o->R = r < (double)cap ? (int64_t)r : cap;
+    /* the block table holds the running sum of code widths in 32 bits */
+    if ((uint64_t)o->tiles * (uint64_t)cn > 0xffffffffull) return TAHREF_ERR_INVALID_ARG;
+  }
   o->off_table = 256;
   o->off_bitmap = align256(o->off_table + 4 * o->nblocks);
-  o->off_side = align256(o->off_bitmap + 8 * o->nblocks);
+  /* width map: 1 bit per tile (allocator 0) or 2 bits (allocator 1) */
+  o->off_side = align256(o->off_bitmap + (p->allocator == 0 ? 8 : 16) * o->nblocks);
   o->off_scale = align256(o->off_side + o->tiles);
   o->off_zero = align256(o->off_scale + 2 * o->tiles);
   o->off_codes = align256(o->off_zero + 4 * o->tiles);
-  o->code_bytes = (o->tiles * G * b_lo + nhi * G * (b_hi - b_lo)) / 8;
+  if (p->allocator == 0) {
+    int64_t nhi = o->k * o->kA * o->nsamples; /* quantization tiles at b_hi */
+    o->code_bytes = (o->tiles * G * o->b_lo + nhi * G * (o->b_hi - o->b_lo)) / 8;
+  } else {
+    /* the most a sample's code blocks can take: (A/8) bytes per unit of width
+     * per allocation tile, c_1 N + R units (A is a multiple of 8) */
+    o->code_bytes = o->nsamples * (o->A / 8) * ((int64_t)o->b_lo * o->atiles_per_sample + o->R);
+  }
   o->total = align256(o->off_codes + o->code_bytes);
   return TAHREF_OK;
 }
@@ -180,7 +206,7 @@ static void write_header(uint8_t* P, const tahref_plan* pl, const tahref_params*
   for (int i = 0; i < p->n_candidates; ++i) put_u8(P, 41 + i, p->candidates[i]);
   put_u8(P, 45, (uint32_t)pl->b_lo);
   put_u8(P, 46, (uint32_t)pl->b_hi);
-  put_u64(P, 48, (uint64_t)pl->k);
+  put_u64(P, 48, (uint64_t)(pl->allocator == 0 ? pl->k : pl->R));
   put_u64(P, 56, (uint64_t)pl->tiles);
   put_u64(P, 64, (uint64_t)pl->off_table);
   put_u64(P, 72, (uint64_t)pl->off_bitmap);
@@ -190,6 +216,7 @@ static void write_header(uint8_t* P, const tahref_plan* pl, const tahref_params*
   put_u64(P, 104, (uint64_t)pl->off_codes);
   put_u64(P, 112, (uint64_t)pl->total);
   put_u32(P, 120, (uint32_t)pl->A);
+  put_u8(P, 124, (uint32_t)pl->allocator);
 }
 
 /* ------------------------------------------------------------------ */
@@ -419,6 +446,87 @@ int tahref_allocate(const float* H, int64_t N, int64_t k, uint8_t* hi) {
   return TAHREF_OK;
 }
 
+/*
+ * Allocation over every candidate width (allocator 1). The pages rank tiles by
+ * entropy and give the top p% the higher of two widths; they define no rule
+ * for three or more widths in one sample, so this one is a reading of that
+ * ranking as a distortion budget:
+ *   - a uniform quantizer of width b over a range D has mean-square error
+ *     proportional to D^2 Delta(b), Delta(b) = (2^b - 1)^-2;
+ *   - tile u weighs w_u = 2^(2 H_u) (higher entropy, larger weight, as the
+ *     ranking of §3.2 asks), so the sample's objective is
+ *     sum_u w_u Delta(b_u) under sum_u (b_u - c_1) <= R;
+ *   - every tile starts at c_1; upgrade j of tile u (c_j -> c_(j+1), costing
+ *     c_(j+1) - c_j bits) lowers the objective by w_u (Delta(c_j) - Delta(c_(j+1))),
+ *     and its gain per bit has the base-2 logarithm
+ *       kappa(u, j) = 2 H_u + lambda_j,
+ *       lambda_j = log2((Delta(c_j) - Delta(c_(j+1))) / (c_(j+1) - c_j));
+ *   - upgrades are taken in the order kappa descending, then u ascending,
+ *     then j ascending, for as long as the bits taken stay within R; the
+ *     first upgrade that would exceed R ends the allocation.
+ * Delta is convex, so lambda_j decreases with j and a tile's upgrades come in
+ * order. With two candidates every upgrade costs the same, the order is the
+ * entropy ranking and the rule is §3.2's top-k.
+ * Precision: lambda_j in double from the C library's log2, rounded once to
+ * fp32; kappa = 2 H_u + lambda_j in fp32 (2 H_u is exact), the precision the
+ * GPU decides in.
+ */
+static double greedy_delta(int b) {
+  const double L = ldexp(1.0, b) - 1.0;
+  return 1.0 / (L * L);
+}
+
+int tahref_greedy_lambda(int n, const uint8_t* cand, float* lam) {
+  if (n < 1 || n > 4 || !cand || !lam) return TAHREF_ERR_INVALID_ARG;
+  for (int j = 0; j + 1 < n; ++j) {
+    const double gain = greedy_delta(cand[j]) - greedy_delta(cand[j + 1]);
+    lam[j] = (float)log2(gain / (double)(cand[j + 1] - cand[j]));
+  }
+  return TAHREF_OK;
+}
+
+typedef struct {
+  float kappa;
+  int64_t u;
+  int j;
+} upgrade;
+
+static int cmp_upgrade(const void* a, const void* b) {
+  const upgrade* x = (const upgrade*)a;
+  const upgrade* y = (const upgrade*)b;
+  if (x->kappa > y->kappa) return -1;
+  if (x->kappa < y->kappa) return 1;
+  if (x->u != y->u) return x->u < y->u ? -1 : 1;
+  return (x->j > y->j) - (x->j < y->j);
+}
+
+int tahref_allocate_greedy(const float* H, int64_t N, int n, const uint8_t* cand, int64_t R, uint8_t* level) {
+  float lam[3];
+  if (N < 0 || R < 0 || tahref_greedy_lambda(n, cand, lam) != TAHREF_OK) return TAHREF_ERR_INVALID_ARG;
+  for (int64_t u = 0; u < N; ++u) level[u] = 0;
+  const int64_t nu = N * (n - 1);
+  if (nu == 0) return TAHREF_OK;
+  upgrade* up = (upgrade*)malloc(sizeof(upgrade) * (size_t)nu);
+  if (!up) return TAHREF_ERR_INVALID_ARG;
+  for (int64_t u = 0; u < N; ++u)
+    for (int j = 0; j + 1 < n; ++j) {
+      upgrade* e = &up[u * (n - 1) + j];
+      e->kappa = 2.0f * H[u] + lam[j];
+      e->u = u;
+      e->j = j;
+    }
+  qsort(up, (size_t)nu, sizeof(upgrade), cmp_upgrade);
+  int64_t spent = 0;
+  for (int64_t i = 0; i < nu; ++i) {
+    const int cost = cand[up[i].j + 1] - cand[up[i].j];
+    if (spent + cost > R) break;
+    spent += cost;
+    level[up[i].u] += 1; /* the order takes a tile's upgrades j = 0, 1, ... in turn */
+  }
+  free(up);
+  return TAHREF_OK;
+}
+
 /* ------------------------------------------------------------------ */
 /* whole tensor                                                       */
 /* ------------------------------------------------------------------ */
@@ -437,9 +545,11 @@ static void load_tile(const void* x, int dtype, const tahref_plan* pl, int64_t t
 }
 
 /* Entropy of every allocation tile (H[atiles]), the per-sample selection over
- * allocation tiles, and each quantization tile's width flag (hi[tiles]):
+ * allocation tiles, and each quantization tile's width index (hi[tiles]: 0/1
+ * for b_lo/b_hi under allocator 0, the candidate index under allocator 1):
  * allocation tile u of the tensor covers quantization tiles u*kA ... u*kA + kA - 1. */
-static int entropy_and_widths(const void* x, int dtype, const tahref_plan* pl, float* H, uint8_t* hi) {
+static int entropy_and_widths(const void* x, int dtype, const tahref_plan* pl, const tahref_params* p, float* H,
+                              uint8_t* hi) {
   float* a = (float*)malloc(sizeof(float) * (size_t)pl->A);
   uint8_t* hiA = (uint8_t*)malloc((size_t)(pl->atiles + 1));
   if (!a || !hiA) {
@@ -454,12 +564,22 @@ static int entropy_and_widths(const void* x, int dtype, const tahref_plan* pl, f
   int rc = TAHREF_OK;
   for (int64_t s = 0; s < pl->nsamples && rc == TAHREF_OK; ++s) {
     int64_t first = s * pl->atiles_per_sample;
-    rc = tahref_allocate(H + first, pl->atiles_per_sample, pl->k, hiA + first);
+    if (pl->allocator == 0)
+      rc = tahref_allocate(H + first, pl->atiles_per_sample, pl->k, hiA + first);
+    else
+      rc = tahref_allocate_greedy(H + first, pl->atiles_per_sample, p->n_candidates, p->candidates, pl->R,
+                                  hiA + first);
   }
   for (int64_t t = 0; t < pl->tiles; ++t) hi[t] = hiA[t / pl->kA];
   free(a);
   free(hiA);
   return rc;
+}
+
+/* Code width of a tile from its width index. */
+static int width_of(const tahref_plan* pl, const tahref_params* p, int idx) {
+  if (pl->allocator == 0) return idx ? pl->b_hi : pl->b_lo;
+  return p->candidates[idx];
 }
 
 int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden, const tahref_params* p,
@@ -468,7 +588,7 @@ int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden
   tahref_plan pl;
   int rc = tahref_plan_make(tokens, hidden, p, &pl);
   if (rc) return rc;
-  rc = entropy_and_widths(x, x_dtype, &pl, H, hi);
+  rc = entropy_and_widths(x, x_dtype, &pl, p, H, hi);
   if (rc) return rc;
   float a[128];
   uint32_t q[128];
@@ -482,7 +602,7 @@ int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden
       a[d] = tmp;
       tahref_fwht(a, pl.G);
     }
-    int b = hi[t] ? pl.b_hi : pl.b_lo;
+    int b = width_of(&pl, p, hi[t]);
     tahref_quantize(a, pl.G, b, &lo[t], &scale[t], q);
     flag[t] = (uint8_t)f;
     pivot[t] = (uint8_t)d;
@@ -496,9 +616,13 @@ int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden
  * codes and metadata into one fixed-size byte stream (§3.4).
  *
  * Payload (little-endian, sections start on 256-byte boundaries):
- *   header (128 B, zero padded to 256) | block table: u32 count of b_hi tiles
- *   before each run of 64 tiles | width map: u32 words, bit t%32 of word t/32
- *   is 1 iff tile t has b_hi (2 words per 64 tiles) | side byte per tile:
+ *   header (128 B, zero padded to 256; byte 124 = allocator) | block table:
+ *   u32 per run of 64 tiles, the count of b_hi tiles before it (allocator 0)
+ *   or the sum of the code widths of the tiles before it (allocator 1) |
+ *   width map: u32 words; allocator 0: bit t%32 of word t/32 is 1 iff tile t
+ *   has b_hi (2 words per 64 tiles); allocator 1: bits 2(t%16), 2(t%16)+1 of
+ *   word t/16 hold the candidate index of tile t (4 words per 64 tiles) |
+ *   side byte per tile:
  *   bit 7 = transformed, bits 0..6 = pivot d of a transformed tile (0 for
  *   the others) | scale per tile: bf16 bits |
  *   zero-point per tile: fp32 | codes: one block of G*b/8 bytes per tile in
@@ -523,7 +647,7 @@ int tahref_encode(const void* x, int x_dtype, int64_t tokens, int64_t hidden, co
     free(hi);
     return TAHREF_ERR_INVALID_ARG;
   }
-  rc = entropy_and_widths(x, x_dtype, &pl, H, hi);
+  rc = entropy_and_widths(x, x_dtype, &pl, p, H, hi);
   if (rc) {
     free(H);
     free(hi);
@@ -533,13 +657,18 @@ int tahref_encode(const void* x, int x_dtype, int64_t tokens, int64_t hidden, co
   float a[128];
   uint32_t q[128];
   int64_t code_off = pl.off_codes;
-  int64_t hi_count = 0;
+  int64_t hi_count = 0, width_sum = 0;
   for (int64_t t = 0; t < pl.tiles; ++t) {
-    if (t % 64 == 0) put_u32(P, pl.off_table + 4 * (t / 64), (uint32_t)hi_count);
-    if (hi[t]) {
+    if (t % 64 == 0)
+      put_u32(P, pl.off_table + 4 * (t / 64), (uint32_t)(pl.allocator == 0 ? hi_count : width_sum));
+    if (pl.allocator == 0 && hi[t]) {
       int64_t w = pl.off_bitmap + 4 * (t / 32);
       put_u32(P, w, get_u32(P, w) | (1u << (t % 32)));
       ++hi_count;
+    }
+    if (pl.allocator == 1) {
+      int64_t w = pl.off_bitmap + 4 * (t / 16);
+      put_u32(P, w, get_u32(P, w) | ((uint32_t)hi[t] << (2 * (t % 16))));
     }
     load_tile(x, x_dtype, &pl, t, a);
     int d;
@@ -550,7 +679,8 @@ int tahref_encode(const void* x, int x_dtype, int64_t tokens, int64_t hidden, co
       a[d] = tmp;
       tahref_fwht(a, pl.G);
     }
-    int b = hi[t] ? pl.b_hi : pl.b_lo;
+    int b = width_of(&pl, p, hi[t]);
+    width_sum += b;
     float lo, s;
     tahref_quantize(a, pl.G, b, &lo, &s, q);
     put_u8(P, pl.off_side + t, (uint32_t)(f ? (0x80 | d) : 0)); /* the pivot only matters to a transformed tile */
@@ -572,7 +702,10 @@ int tahref_encode(const void* x, int x_dtype, int64_t tokens, int64_t hidden, co
  * Decoder (Algorithm 1 line 5). The shape and parameters come from the caller
  * (pipeline stages know them statically); the header must agree with them.
  * Code blocks are located by a running sum over the width map in tile order;
- * the block table is checked against that sum.
+ * the block table is checked against that sum, and so is the allocation: k
+ * b_hi allocation tiles per sample (allocator 0), or candidate indexes in
+ * range, equal across an allocation tile, whose widths above c_1 add up to at
+ * most R per sample (allocator 1).
  */
 int tahref_decode(const uint8_t* P, size_t len, int64_t tokens, int64_t hidden, const tahref_params* p,
                   void* y, int y_dtype) {
@@ -589,13 +722,27 @@ int tahref_decode(const uint8_t* P, size_t len, int64_t tokens, int64_t hidden, 
   float xhat[128];
   uint32_t q[128];
   int64_t code_off = pl.off_codes;
-  int64_t hi_count = 0;
+  int64_t hi_count = 0, width_sum = 0, extra = 0;
+  int prev_idx = 0;
   for (int64_t t = 0; t < pl.tiles; ++t) {
-    if (t % 64 == 0 && get_u32(P, pl.off_table + 4 * (t / 64)) != (uint32_t)hi_count)
+    if (t % 64 == 0 &&
+        get_u32(P, pl.off_table + 4 * (t / 64)) != (uint32_t)(pl.allocator == 0 ? hi_count : width_sum))
       return TAHREF_ERR_BAD_PAYLOAD;
-    int hi = (get_u32(P, pl.off_bitmap + 4 * (t / 32)) >> (t % 32)) & 1u;
-    hi_count += hi;
-    int b = hi ? pl.b_hi : pl.b_lo;
+    int idx;
+    if (pl.allocator == 0) {
+      idx = (get_u32(P, pl.off_bitmap + 4 * (t / 32)) >> (t % 32)) & 1u;
+      hi_count += idx;
+    } else {
+      idx = (get_u32(P, pl.off_bitmap + 4 * (t / 16)) >> (2 * (t % 16))) & 3u;
+      if (idx >= p->n_candidates) return TAHREF_ERR_BAD_PAYLOAD;
+      if (t % pl.kA != 0 && idx != prev_idx) return TAHREF_ERR_BAD_PAYLOAD; /* one width per allocation tile */
+      if (t % pl.tiles_per_sample == 0) extra = 0;
+      if (t % pl.kA == 0) extra += p->candidates[idx] - p->candidates[0];
+      if (extra > pl.R) return TAHREF_ERR_BAD_PAYLOAD;
+      prev_idx = idx;
+    }
+    int b = width_of(&pl, p, idx);
+    width_sum += b;
     uint32_t side = P[pl.off_side + t];
     int f = (side >> 7) & 1, d = side & 0x7f;
     if (d >= pl.G) return TAHREF_ERR_BAD_PAYLOAD;
@@ -620,7 +767,7 @@ int tahref_decode(const uint8_t* P, size_t len, int64_t tokens, int64_t hidden, 
       for (int k = 0; k < pl.G; ++k) yh[base + k] = f32_to_bf16_rne(xhat[k]);
     }
   }
-  if (hi_count != pl.k * pl.kA * pl.nsamples) return TAHREF_ERR_BAD_PAYLOAD;
+  if (pl.allocator == 0 && hi_count != pl.k * pl.kA * pl.nsamples) return TAHREF_ERR_BAD_PAYLOAD;
   return TAHREF_OK;
 }
 

@@ -47,6 +47,8 @@ typedef struct {
   uint8_t candidates[4];     /* strictly increasing, each 1..8 */
   float tau;                 /* outlier threshold tau of Eq. (3); 0 = always, +inf = never (App. F) */
   int32_t alloc_tile;        /* A: allocation tile (§3.2), a multiple of G dividing hidden; 0 = G */
+  int32_t allocator;         /* 0: top-p% between the two widths around the budget (§3.2);
+                                1: greedy over every candidate width (see tahref_allocate_greedy) */
 } tahref_params;
 
 /* Derived sizes and the payload section layout. */
@@ -58,6 +60,9 @@ typedef struct {
   /* allocation tiles (§3.2): A channels = kA quantization tiles; MA = hidden / A per
    * token (the paper's M); atiles in all, atiles_per_sample = S * MA per sample */
   int64_t A, kA, MA, atiles, atiles_per_sample;
+  /* allocator 1: R bounds the sum over a sample's allocation tiles of their width
+   * minus c_1 (see tahref_allocate_greedy) */
+  int64_t allocator, R;
 } tahref_plan;
 
 int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tahref_plan* out);
@@ -71,13 +76,18 @@ int tahref_outlier(const float* alpha, int G, float tau, int* d, float* m1, floa
 void tahref_quantize(const float* y, int G, int b, float* lo, float* s, uint32_t* q);
 void tahref_dequantize(const uint32_t* q, int G, float s, float lo, int flag, int d, float* xhat);
 int tahref_allocate(const float* H, int64_t N, int64_t k, uint8_t* hi);
+/* Greedy allocation over n candidate widths (allocator 1): lam receives the n-1
+ * per-upgrade constants, level[u] the index of tile u's width. */
+int tahref_greedy_lambda(int n, const uint8_t* cand, float* lam);
+int tahref_allocate_greedy(const float* H, int64_t N, int n, const uint8_t* cand, int64_t R, uint8_t* level);
 
 /* Whole codec over a [tokens, hidden] row-major tensor (host pointers). */
 int tahref_encode(const void* x, int x_dtype, int64_t tokens, int64_t hidden, const tahref_params* p,
                   uint8_t* payload, size_t payload_cap);
 int tahref_decode(const uint8_t* payload, size_t payload_len, int64_t tokens, int64_t hidden,
                   const tahref_params* p, void* y, int y_dtype);
-/* H: one entropy per allocation tile (atiles); the other outputs one per quantization tile. */
+/* H: one entropy per allocation tile (atiles); the other outputs one per quantization tile
+ * (hi: 0/1 for b_lo/b_hi under allocator 0, the candidate index under allocator 1). */
 int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden, const tahref_params* p,
                       float* H, uint8_t* flag, uint8_t* pivot, uint8_t* hi, float* lo, float* scale);
 

@@ -28,8 +28,9 @@ BF16 = 1
 @dataclasses.dataclass(frozen=True)
 class Params:
     """Codec parameters: quantization tile G, ranking scope S in tokens (0 = all),
-    average code-bit budget, candidate widths, outlier threshold tau and
-    allocation tile A in channels (0 = G)."""
+    average code-bit budget, candidate widths, outlier threshold tau,
+    allocation tile A in channels (0 = G) and allocator (0 = top-p% between two
+    widths, 1 = greedy over every candidate)."""
 
     tile: int = 64
     tokens_per_sample: int = 0
@@ -37,6 +38,7 @@ class Params:
     candidates: tuple = (3, 4)
     tau: float = 2.0
     alloc_tile: int = 0
+    allocator: int = 0
 
 
 @dataclasses.dataclass(frozen=True)
