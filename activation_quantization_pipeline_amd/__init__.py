@@ -63,7 +63,8 @@ class TahError(RuntimeError):
 class TahParams:
     """Codec parameters (see tah_params_t): tile G, ranking scope S in tokens
     (0 = all tokens), average code-bit budget, candidate widths, outlier tau,
-    allocation tile A in channels (0 = G)."""
+    allocation tile A in channels (0 = G), allocator (ALLOC_TOP_P or
+    ALLOC_GREEDY)."""
 
     tile: int = 64
     tokens_per_sample: int = 0
@@ -71,6 +72,7 @@ class TahParams:
     candidates: tuple = (3, 4)
     tau: float = 2.0
     alloc_tile: int = 0
+    allocator: int = 0
 
 
 class _CParams(ctypes.Structure):
@@ -82,6 +84,7 @@ class _CParams(ctypes.Structure):
         ("candidates", ctypes.c_uint8 * 4),
         ("tau", ctypes.c_float),
         ("alloc_tile", ctypes.c_int32),
+        ("allocator", ctypes.c_int32),
     ]
 
 
@@ -98,11 +101,13 @@ def _cparams(p) -> _CParams:
         c.candidates[i] = cands[i] if i < len(cands) else 0
     c.tau = float(p.tau)
     c.alloc_tile = int(getattr(p, "alloc_tile", 0))
+    c.allocator = int(getattr(p, "allocator", 0))
     return c
 
 
 _lib = None
-ABI_VERSION = 2  # TAH_ABI_VERSION of include/tah.h
+ABI_VERSION = 3  # TAH_ABI_VERSION of include/tah.h
+ALLOC_TOP_P, ALLOC_GREEDY = 0, 1  # TAH_ALLOC_* of include/tah.h
 
 
 def lib() -> ctypes.CDLL:

@@ -10,7 +10,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIBDIR = os.path.join(HERE, "lib")
 LIB_PATH = os.path.join(LIBDIR, "libtah.so")
-SOURCES = ["tah_abi.hip", "tah_encode.hip", "tah_decode.hip", "tah_select.hip", "tah_naive.hip", "tah_hadamard.hip"]
+SOURCES = ["tah_abi.hip", "tah_encode.hip", "tah_decode.hip", "tah_select.hip", "tah_naive.hip", "tah_hadamard.hip",
+           "tah_greedy.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # -ffp-contract=off: every fused multiply-add is written out (fmaf), none is

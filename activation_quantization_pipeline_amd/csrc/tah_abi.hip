@@ -43,6 +43,7 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   if (S > 0 && tokens % S) return TAH_ERR_INVALID_ARG;
   const int64_t A = p->alloc_tile == 0 ? G : p->alloc_tile;
   if (A < G || A % G || hidden % A) return TAH_ERR_INVALID_ARG;
+  if (p->allocator != TAH_ALLOC_TOP_P && p->allocator != TAH_ALLOC_GREEDY) return TAH_ERR_INVALID_ARG;
   if ((float)p->candidates[0] > p->bit_budget) return TAH_ERR_BUDGET_INFEASIBLE;
   // tile indices of a sample and block-table counts are 32-bit on the device
   const int64_t M = hidden / G;
@@ -69,35 +70,81 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   o->N = S * (hidden / A);
   o->G = G;
   o->log2G = ilog2(G);
-  o->b_lo = b_lo;
-  o->b_hi = b_hi;
-  o->k = (b_hi == b_lo || o->N == 0)
-             ? 0
-             : (int64_t)floor(((double)p->bit_budget - (double)b_lo) * (double)o->N / (double)(b_hi - b_lo));
+  o->allocator = p->allocator;
+  if (p->allocator == TAH_ALLOC_TOP_P) {
+    o->b_lo = b_lo;
+    o->b_hi = b_hi;
+    o->k = (b_hi == b_lo || o->N == 0)
+               ? 0
+               : (int64_t)floor(((double)p->bit_budget - (double)b_lo) * (double)o->N / (double)(b_hi - b_lo));
+    o->mode = o->k > 0 ? 1 : 0;
+  } else {
+    // greedy: any candidate per allocation tile; R = floor((B - c_1) N) bits a
+    // sample may add above c_1, at most what every tile at c_n would take
+    const int c1 = p->candidates[0], cn = p->candidates[p->n_candidates - 1];
+    o->b_lo = c1;
+    o->b_hi = cn;
+    o->k = 0;
+    o->mode = 2;
+    o->nl = p->n_candidates - 1;
+    const int64_t cap = (int64_t)(cn - c1) * o->N;
+    const double r = floor(((double)p->bit_budget - (double)c1) * (double)o->N);
+    o->R = r < (double)cap ? (int64_t)r : cap;
+    // the block table's running width sums are 32-bit (a limit of the format)
+    if ((uint64_t)o->tiles * (uint64_t)cn > 0xffffffffull) return TAH_ERR_INVALID_ARG;
+    // per-sample weights and upgrade indexes are 32-bit on the device
+    if ((uint64_t)cap > 0xffffffffull) return TAH_ERR_UNSUPPORTED;
+    // every tile takes the same level when nothing or everything fits
+    o->glevel = (o->nl == 0 || o->R == 0) ? 0 : (o->R == cap ? o->nl : -1);
+    for (int j = 0; j < o->nl; ++j) {
+      // lambda_j = log2 of upgrade j's gain per bit, Delta(b) = (2^b - 1)^-2
+      const double l0 = ldexp(1.0, p->candidates[j]) - 1.0, l1 = ldexp(1.0, p->candidates[j + 1]) - 1.0;
+      const double gain = 1.0 / (l0 * l0) - 1.0 / (l1 * l1);
+      o->cost[j] = p->candidates[j + 1] - p->candidates[j];
+      o->lam[j] = (float)log2(gain / (double)o->cost[j]);
+    }
+    o->ngpasses = 0;
+    if (o->glevel < 0) {
+      // composite = (32-bit key, ib bits of the complemented upgrade index), top digit first
+      o->ib = bit_width((uint64_t)(o->N * o->nl - 1));
+      if (o->ib < 1) o->ib = 1;
+      for (int hi = 32 + o->ib; hi > 0; hi -= kDigitBits) {
+        const int lo = hi - kDigitBits > 0 ? hi - kDigitBits : 0;
+        o->gpasses[o->ngpasses++] = GPass{lo, hi - lo};
+      }
+    }
+  }
   o->tau = p->tau;
   o->budget = p->bit_budget;
   o->n_candidates = p->n_candidates;
   for (int i = 0; i < 4; ++i) o->candidates[i] = i < p->n_candidates ? p->candidates[i] : 0;
   o->nblocks = (o->tiles + 63) / 64;
 
-  const int64_t nhi = o->k * o->kA * o->nsamples;  // quantization tiles at b_hi
+  const int64_t map_bytes = (o->allocator == TAH_ALLOC_GREEDY ? 16 : 8) * o->nblocks;  // 1 or 2 bits per tile
   o->off_table = 256;
   o->off_bitmap = align256(o->off_table + 4 * o->nblocks);
-  o->off_side = align256(o->off_bitmap + 8 * o->nblocks);
+  o->off_side = align256(o->off_bitmap + map_bytes);
   o->off_scale = align256(o->off_side + o->tiles);
   o->off_zero = align256(o->off_scale + 2 * o->tiles);
   o->off_codes = align256(o->off_zero + 4 * o->tiles);
-  o->code_bytes = (o->tiles * G * b_lo + nhi * G * (b_hi - b_lo)) / 8;
+  if (o->allocator == TAH_ALLOC_TOP_P) {
+    const int64_t nhi = o->k * o->kA * o->nsamples;  // quantization tiles at b_hi
+    o->code_bytes = (o->tiles * G * o->b_lo + nhi * G * (o->b_hi - o->b_lo)) / 8;
+  } else {  // the most the code blocks can take: A/8 bytes per unit of width, c_1 N + R units per sample
+    o->code_bytes = o->nsamples * (A / 8) * ((int64_t)o->b_lo * o->N + o->R);
+  }
   o->total = align256(o->off_codes + o->code_bytes);
 
-  const bool mixed = o->k > 0;
+  const bool mixed = o->mode != 0;  // block table and width map built before the encoder
+  const bool sel = o->mode == 1 || o->glevel < 0;  // a select runs
   int64_t w = 0;
   o->ws_status = w;
   w += 256;
   o->ws_state = w;  // two selection states per sample (ping-pong across passes)
-  w = align256(w + 2 * (int64_t)sizeof(SampleState) * (mixed ? o->nsamples : 0));
+  static_assert(sizeof(SampleState) >= sizeof(GState), "one state size serves both selects");
+  w = align256(w + 2 * (int64_t)sizeof(SampleState) * (sel ? o->nsamples : 0));
   o->ws_hist = w;  // three rotating histograms per sample
-  w = align256(w + 3 * 4 * kBins * (mixed ? o->nsamples : 0));
+  w = align256(w + 3 * 4 * kBins * (sel ? o->nsamples : 0));
   o->ws_H = w;  // entropy of each allocation tile
   w = align256(w + 4 * o->atiles);
   o->ws_LS = w;  // per-quantization-tile sums (L, S) when an allocation tile spans several
@@ -107,20 +154,22 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   o->ws_table = w;
   w = align256(w + 4 * (mixed ? o->nblocks : 0));
   o->ws_bitmap = w;
-  w = align256(w + 8 * (mixed ? o->nblocks : 0));
+  w = align256(w + (mixed ? map_bytes : 0));
   // per sample: a count, a pad word, then the (key, index) pairs whose key
   // matches the threshold's prefix after the second entropy pass (ties at the
   // threshold are broken among them)
   o->ncand = o->N < kMaxCand ? o->N : kMaxCand;
   o->cand_stride = 2 + 2 * o->ncand;
   o->ws_cand = w;
-  w = align256(w + 4 * o->cand_stride * (mixed ? o->nsamples : 0));
+  w = align256(w + 4 * o->cand_stride * (o->mode == 1 ? o->nsamples : 0));
+  o->ws_wtotal = w;  // greedy: the sum of all code widths (the used part of the code section)
+  w = align256(w + (o->mode == 2 ? 4 : 0));
   o->ws_total = w;
 
   // radix-select passes: three digits of the 32-bit entropy key, then enough
   // digits of the tile index to order tied entropies
   o->npasses = 0;
-  if (mixed) {
+  if (o->mode == 1) {
     o->passes[o->npasses++] = SelectPass{0, 21, 11, 0};
     o->passes[o->npasses++] = SelectPass{0, 10, 11, 0};
     o->passes[o->npasses++] = SelectPass{0, 0, 10, 1};
@@ -153,7 +202,7 @@ void make_header(const Plan& pl, Header* h) {
   put(41, pl.candidates, 4);
   put(45, &bl, 1);
   put(46, &bh, 1);
-  put(48, &pl.k, 8);
+  put(48, pl.allocator == TAH_ALLOC_TOP_P ? &pl.k : &pl.R, 8);
   put(56, &pl.tiles, 8);
   put(64, &pl.off_table, 8);
   put(72, &pl.off_bitmap, 8);
@@ -163,6 +212,8 @@ void make_header(const Plan& pl, Header* h) {
   put(104, &pl.off_codes, 8);
   put(112, &pl.total, 8);
   put(120, &A, 4);
+  const uint8_t al = (uint8_t)pl.allocator;
+  put(124, &al, 1);
   memcpy(h->w, b, 128);
 }
 
@@ -171,7 +222,7 @@ void make_pads(const Plan& pl, PadRanges* pr) {
   const int64_t ends[7][2] = {
       {128, pl.off_table},
       {pl.off_table + 4 * pl.nblocks, pl.off_bitmap},
-      {pl.off_bitmap + 8 * pl.nblocks, pl.off_side},
+      {pl.off_bitmap + (pl.allocator == TAH_ALLOC_GREEDY ? 16 : 8) * pl.nblocks, pl.off_side},
       {pl.off_side + pl.tiles, pl.off_scale},
       {pl.off_scale + 2 * pl.tiles, pl.off_zero},
       {pl.off_zero + 4 * pl.tiles, pl.off_codes},
@@ -208,12 +259,17 @@ static tah_status_t run_encode(const void* x, tah_dtype_t x_dtype, int64_t token
   if (ws_cap < (size_t)pl.ws_total) return TAH_ERR_BUFFER_TOO_SMALL;
   pl.x_dtype = x_dtype;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  const bool mixed = pl.k > 0;
   uint8_t* w = static_cast<uint8_t*>(ws);
-  if (mixed && pl.tiles > 0) {
+  const int mode = pl.tiles > 0 ? pl.mode : 0;
+  if (mode == 1) {
     hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, true, st);
     if (e != hipSuccess) return hip_status(e);
     e = launch_select(pl, payload, ws, st);
+    if (e != hipSuccess) return hip_status(e);
+  } else if (mode == 2) {
+    hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, pl.glevel < 0, st);
+    if (e != hipSuccess) return hip_status(e);
+    e = launch_greedy(pl, payload, ws, st);
     if (e != hipSuccess) return hip_status(e);
   } else if (pl.kA > 1 && pl.tiles > 0) {
     // no selection, but the workspace still receives the allocation-tile
@@ -222,7 +278,7 @@ static tah_status_t run_encode(const void* x, tah_dtype_t x_dtype, int64_t token
     hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, false, st);
     if (e != hipSuccess) return hip_status(e);
   }
-  return hip_status(launch_encode(pl, x, payload, want_y ? y : nullptr, y_dtype, ws, st, mixed && pl.tiles > 0));
+  return hip_status(launch_encode(pl, x, payload, want_y ? y : nullptr, y_dtype, ws, st, mode));
 }
 
 }  // namespace tah

@@ -30,6 +30,7 @@ struct DecArgs {
   int64_t tiles, len;
   int64_t off_table, off_bitmap, off_side, off_scale, off_zero, off_codes;
   int32_t b_lo, b_hi, sz_lo, sz_hi;
+  uint32_t cands;  // candidate widths, one byte each (any-width layout)
   Header expect;
 };
 
@@ -69,13 +70,23 @@ __device__ __forceinline__ void load_dequant_b(int b, const uint8_t* src, float 
 }
 
 // A group's metadata: per lane (side byte, bf16 scale, zero-point) and per
-// group (block-table entry, width-map words).
+// group (block-table entry, the two words of the 1-bit width map); with the
+// 2-bit level map, bm0 is instead the word that holds the lane's own level.
 struct DecMeta {
   uint32_t side, scale, tab, bm0, bm1;
   float zero;
 };
 
-template <int NT>
+// Code width of a lane's tile under the 2-bit level map (a level past the
+// candidates, only in a corrupt payload, reads as c_1 so every access stays
+// inside the region buffer).
+__device__ __forceinline__ int level_width(const DecArgs& a, const DecMeta& m, int lane) {
+  const uint32_t lv = (m.bm0 >> (2 * (lane & 15))) & 3u;
+  const int w = (int)((a.cands >> (8 * lv)) & 255u);
+  return w != 0 ? w : a.b_lo;
+}
+
+template <int NT, bool MULTI>
 __device__ __forceinline__ void load_meta(const DecArgs& a, int64_t g, DecMeta& m) {
   const int64_t t0 = g * NT;
   const int64_t t = t0 + threadIdx.x;
@@ -84,21 +95,38 @@ __device__ __forceinline__ void load_meta(const DecArgs& a, int64_t g, DecMeta& 
   m.scale = reinterpret_cast<const uint16_t*>(a.payload + a.off_scale)[tc];
   m.zero = reinterpret_cast<const float*>(a.payload + a.off_zero)[tc];
   const int64_t blk = t0 >> 6;
+  const uint32_t* map = reinterpret_cast<const uint32_t*>(a.payload + a.off_bitmap);
   m.tab = reinterpret_cast<const uint32_t*>(a.payload + a.off_table)[blk];
-  m.bm0 = reinterpret_cast<const uint32_t*>(a.payload + a.off_bitmap)[2 * blk];
-  m.bm1 = reinterpret_cast<const uint32_t*>(a.payload + a.off_bitmap)[2 * blk + 1];
+  if constexpr (MULTI) {
+    m.bm0 = map[4 * blk + (threadIdx.x >> 4)];  // 16 tiles per word
+    m.bm1 = 0u;
+  } else {
+    m.bm0 = map[2 * blk];
+    m.bm1 = map[2 * blk + 1];
+  }
 }
 
 // The code region of a group: first byte and length (the group's blocks are
-// contiguous: b_lo blocks and b_hi blocks in tile order).
-template <int NT>
+// contiguous: b_lo blocks and b_hi blocks in tile order, or blocks of any
+// candidate width located by the width-sum table, G/8 bytes per unit).
+template <int NT, bool MULTI>
 __device__ __forceinline__ void region_of(const DecArgs& a, int64_t g, const DecMeta& m, int64_t& rs, int& rlen) {
   const int64_t t0 = g * NT;
   const int n = (int)((a.tiles - t0) < NT ? (a.tiles - t0) : NT);
-  const uint64_t bm = ((uint64_t)m.bm1 << 32) | m.bm0;
-  const uint64_t valid = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
-  rs = a.off_codes + t0 * a.sz_lo + (int64_t)m.tab * (a.sz_hi - a.sz_lo);
-  rlen = n * a.sz_lo + __popcll(bm & valid) * (a.sz_hi - a.sz_lo);
+  if constexpr (MULTI) {
+    const int lane = threadIdx.x;
+    int w = lane < n ? level_width(a, m, lane) : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) w += __shfl_xor(w, off, 64);
+    const int unit = a.sz_lo / a.b_lo;  // G/8
+    rs = a.off_codes + (int64_t)unit * (int64_t)m.tab;
+    rlen = unit * w;
+  } else {
+    const uint64_t bm = ((uint64_t)m.bm1 << 32) | m.bm0;
+    const uint64_t valid = n >= 64 ? ~0ull : ((1ull << n) - 1ull);
+    rs = a.off_codes + t0 * a.sz_lo + (int64_t)m.tab * (a.sz_hi - a.sz_lo);
+    rlen = n * a.sz_lo + __popcll(bm & valid) * (a.sz_hi - a.sz_lo);
+  }
 }
 
 // Region bytes of a group go through registers in 16-byte chunks: the region
@@ -130,8 +158,9 @@ __device__ __forceinline__ void load_region(const DecArgs& a, int64_t rs, int rl
 
 // MAXB: the widest code the payload can hold (4 or 8 bits), which sizes the
 // code region in LDS and in registers; fewer LDS bytes per workgroup let more
-// workgroups share a compute unit.
-template <int G, typename TOut, int MAXB>
+// workgroups share a compute unit. MULTI: the 2-bit level map of the greedy
+// allocator instead of the 1-bit width map.
+template <int G, typename TOut, int MAXB, bool MULTI>
 __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   constexpr int NT = 64;
   constexpr int V = G / 16;     // elements per lane in a 16-lane transform group
@@ -177,10 +206,10 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   RR rr;
   int64_t rs_c;
   int rlen_c;
-  load_meta<NT>(a, g, mc);
-  region_of<NT>(a, g, mc, rs_c, rlen_c);
+  load_meta<NT, MULTI>(a, g, mc);
+  region_of<NT, MULTI>(a, g, mc, rs_c, rlen_c);
   load_region<G, NT>(a, rs_c, rlen_c, rr);
-  if (g + step < ngroups) load_meta<NT>(a, g + step, mn);
+  if (g + step < ngroups) load_meta<NT, MULTI>(a, g + step, mn);
 
   int64_t prev_t0 = -1;
   int prev_n = 0;
@@ -195,9 +224,9 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     // the next group's region, and the metadata two groups ahead
     if (g + step < ngroups) {
       mc = mn;
-      region_of<NT>(a, g + step, mc, rs_c, rlen_c);
+      region_of<NT, MULTI>(a, g + step, mc, rs_c, rlen_c);
       load_region<G, NT>(a, rs_c, rlen_c, rr);
-      if (g + 2 * step < ngroups) load_meta<NT>(a, g + 2 * step, mn);
+      if (g + 2 * step < ngroups) load_meta<NT, MULTI>(a, g + 2 * step, mn);
     } else {
 #pragma unroll
       for (int i = 0; i < RR::kChunks; ++i) rr.c[i] = u32x4{0u, 0u, 0u, 0u};  // last group: the old contents are dead
@@ -210,11 +239,26 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
     const int hi = act ? (int)((bm >> lane) & 1u) : 0;
     const int flag = act ? (int)(m.side >> 7) : 0;
     const int piv = (int)(m.side & (G - 1));  // a corrupt pivot must not index outside the tile
-    const int b = hi ? a.b_hi : a.b_lo;
-    const int sz = hi ? a.sz_hi : a.sz_lo;
+    int b, sz, lane_off;
+    if constexpr (MULTI) {
+      const int unit = a.sz_lo / a.b_lo;  // G/8
+      b = act ? level_width(a, m, lane) : 0;
+      int incl = b;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      sz = unit * b;
+      lane_off = unit * (incl - b);
+    } else {
+      b = hi ? a.b_hi : a.b_lo;
+      sz = hi ? a.sz_hi : a.sz_lo;
+      lane_off = lane * a.sz_lo + (int)lanes_below(bm) * (a.sz_hi - a.sz_lo);
+    }
     float v[G];
     if (act) {
-      int off = (int)(rs & 15) + lane * a.sz_lo + (int)lanes_below(bm) * (a.sz_hi - a.sz_lo);
+      int off = (int)(rs & 15) + lane_off;
       const int cap = RR::kChunks * NT * 16 - sz;
       off = off < cap ? off : 0;  // stays inside the region buffer on a corrupt table
       const float s = __uint_as_float(m.scale << 16);
@@ -282,19 +326,20 @@ static int dec_cu_count() {
   return cus;
 }
 
-template <int G, typename TOut, int MAXB>
+template <int G, typename TOut, int MAXB, bool MULTI>
 static hipError_t launch_dec_b(const DecArgs& a, hipStream_t st) {
-  static const int per_cu = dec_wgs_per_cu(k_decode<G, TOut, MAXB>);
+  static const int per_cu = dec_wgs_per_cu(k_decode<G, TOut, MAXB, MULTI>);
   const int64_t ngroups = a.tiles > 0 ? (a.tiles + 63) / 64 : 1;
   const int64_t resident = (int64_t)per_cu * dec_cu_count();
   const int64_t nwg = ngroups < resident ? ngroups : resident;
-  hipLaunchKernelGGL((k_decode<G, TOut, MAXB>), dim3((unsigned)nwg), dim3(64), 0, st, a);
+  hipLaunchKernelGGL((k_decode<G, TOut, MAXB, MULTI>), dim3((unsigned)nwg), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
 template <int G, typename TOut>
-static hipError_t launch_dec_t(const DecArgs& a, hipStream_t st) {
-  return a.b_hi <= 4 ? launch_dec_b<G, TOut, 4>(a, st) : launch_dec_b<G, TOut, 8>(a, st);
+static hipError_t launch_dec_t(const DecArgs& a, bool multi, hipStream_t st) {
+  if (multi) return a.b_hi <= 4 ? launch_dec_b<G, TOut, 4, true>(a, st) : launch_dec_b<G, TOut, 8, true>(a, st);
+  return a.b_hi <= 4 ? launch_dec_b<G, TOut, 4, false>(a, st) : launch_dec_b<G, TOut, 8, false>(a, st);
 }
 
 hipError_t launch_decode(const Plan& pl, const void* payload, void* y, int y_dtype, void* ws, hipStream_t st) {
@@ -314,12 +359,14 @@ hipError_t launch_decode(const Plan& pl, const void* payload, void* y, int y_dty
   a.b_hi = pl.b_hi;
   a.sz_lo = pl.G * pl.b_lo / 8;
   a.sz_hi = pl.G * pl.b_hi / 8;
+  a.cands = 0;
+  for (int i = 0; i < pl.n_candidates; ++i) a.cands |= (uint32_t)pl.candidates[i] << (8 * i);
   make_header(pl, &a.expect);
-  const bool f32 = y_dtype == TAH_DTYPE_F32;
+  const bool f32 = y_dtype == TAH_DTYPE_F32, multi = pl.mode == 2;
   switch (pl.G) {
-    case 32: return f32 ? launch_dec_t<32, float>(a, st) : launch_dec_t<32, bf16_t>(a, st);
-    case 64: return f32 ? launch_dec_t<64, float>(a, st) : launch_dec_t<64, bf16_t>(a, st);
-    case 128: return f32 ? launch_dec_t<128, float>(a, st) : launch_dec_t<128, bf16_t>(a, st);
+    case 32: return f32 ? launch_dec_t<32, float>(a, multi, st) : launch_dec_t<32, bf16_t>(a, multi, st);
+    case 64: return f32 ? launch_dec_t<64, float>(a, multi, st) : launch_dec_t<64, bf16_t>(a, multi, st);
+    case 128: return f32 ? launch_dec_t<128, float>(a, multi, st) : launch_dec_t<128, bf16_t>(a, multi, st);
     default: return hipErrorInvalidValue;
   }
 }

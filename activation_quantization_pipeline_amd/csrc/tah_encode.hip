@@ -7,7 +7,8 @@
 //  2. phase A: lane i reads tile i from LDS and computes the outlier ratio of
 //              Eq. (3) (top-2 magnitudes, pivot d, flag) and, for a uniform
 //              allocation, the tile entropy of Eq. (1)-(2); with a mixed
-//              allocation the width bit comes from the selection pass instead.
+//              allocation the width comes from the selection pass instead
+//              (a bit of the width map, or a 2-bit level of the greedy one).
 //              It fixes the tile's code-block offset (§3.4 packing order);
 //  3. forward: a flagged tile gets the pivot swap P_d in its own LDS row and
 //              the Hadamard transform of Eq. (4) in the lane's registers;
@@ -33,6 +34,9 @@ struct EncArgs {
   int64_t tiles;
   int64_t off_side, off_scale, off_zero, off_codes;
   int32_t b_lo, b_hi, sz_lo, sz_hi;
+  uint32_t cands;           // candidate widths, one byte each (any-width layout)
+  const uint32_t* wtotal;   // any-width layout: the sum of all code widths
+  int64_t code_end;         // end of the code section
   float tau;
   Header hdr;
   PadRanges pads;
@@ -54,7 +58,8 @@ __device__ __forceinline__ void store_codes(const uint32_t (&mq)[G], uint8_t* ds
   constexpr int W = G * B / 32;
   uint32_t w[W];
   pack_codes<G, B>(mq, w);
-  // Every code block offset is a multiple of G*B/8 bytes past a 256-byte aligned base.
+  // Every code block offset is a multiple of G/8 bytes (one bit per code) past
+  // a 256-byte aligned base, whatever the widths of the blocks before it.
   if constexpr (G >= 128) {
 #pragma unroll
     for (int i = 0; i < W / 4; ++i)
@@ -188,7 +193,9 @@ __device__ __forceinline__ void step_of(float lo, float hv, int b, float& s, flo
 // fused rounding against 2^23); store code block, scale and zero-point. With
 // OUT the tile is replaced by its dequantized values (the receiver's step of
 // Algorithm 1, from the codes in registers).
-template <int G, int OUT>
+// GUARD: skip a code block that would end past the code section (the
+// any-width layout, whose offsets come from the allocator's tables).
+template <int G, int OUT, bool GUARD = false>
 __device__ __forceinline__ void quantize_tile(const EncArgs& a, float (&v)[G], int64_t t, int b, int64_t code_off) {
   float lo = v[0], hv = v[0];
 #pragma unroll
@@ -204,7 +211,7 @@ __device__ __forceinline__ void quantize_tile(const EncArgs& a, float (&v)[G], i
 #pragma unroll
   for (int k = 0; k < G; ++k) mq[k] = __float_as_uint(__builtin_fmaf(v[k] - lo, inv, 0x1p23f));
   if (a.payload) {
-    store_codes_b<G>(b, mq, a.payload + code_off);
+    if (!GUARD || code_off + (int64_t)(G / 8) * b <= a.code_end) store_codes_b<G>(b, mq, a.payload + code_off);
     reinterpret_cast<uint16_t*>(a.payload + a.off_scale)[t] = (uint16_t)(__float_as_uint(s) >> 16);
     reinterpret_cast<float*>(a.payload + a.off_zero)[t] = lo;
   }
@@ -215,6 +222,9 @@ __device__ __forceinline__ void quantize_tile(const EncArgs& a, float (&v)[G], i
 }
 
 // OUT: 0 = no reconstruction, 1 = fp32, 2 = bf16.
+// MODE: the width layout: 0 one width (the entropy is computed here), 1 two
+// widths from the 1-bit width map and the count table, 2 any candidate from
+// the 2-bit level map and the width-sum table.
 // A workgroup is one wavefront with LDS rows of its own, and it is persistent:
 // group g of 64 tiles goes to workgroup g mod gridDim.x. Groups of small tiles
 // are prefetched into registers while the current group is processed.
@@ -224,9 +234,10 @@ __device__ __forceinline__ void quantize_tile(const EncArgs& a, float (&v)[G], i
 // of its 64 tiles is flagged; measured on the 8192x8192 round trip this beats
 // handing the flagged tiles to 16-lane groups through LDS (barriers and
 // round trips per group) at every tau, from 0 (every tile) to 4.
-template <int G, typename TIn, int OUT, bool MIXED>
+template <int G, typename TIn, int OUT, int MODE>
 __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncArgs a) {
   constexpr int NT = 64;
+  constexpr bool MIXED = MODE != 0;
   using RI = TileRow<G, TIn>;
   using TOut = typename std::conditional<OUT == 1, float, bf16_t>::type;
   using RO = TileRow<G, TOut>;
@@ -247,6 +258,14 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
     if (lane < 32) reinterpret_cast<uint32_t*>(a.payload)[lane] = a.hdr.w[lane];
     for (int r = 0; r < a.pads.n; ++r)
       for (int i = lane; i < a.pads.len[r]; i += NT) a.payload[a.pads.off[r] + i] = 0;
+  }
+  if constexpr (MODE == 2) {
+    // the code section is sized for the whole budget: its unused tail is zero
+    if (a.payload) {
+      const int64_t used = a.off_codes + (int64_t)(G / 8) * (int64_t)a.wtotal[0];
+      for (int64_t i = used + (int64_t)blockIdx.x * NT + lane; i < a.code_end; i += (int64_t)gridDim.x * NT)
+        a.payload[i] = 0;
+    }
   }
 
   if constexpr (!MIXED) load_log2_tab(lt);  // read after the first barrier of the loop
@@ -290,7 +309,7 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
     // ---------------- phase A: lane owns tile t0 + lane ----------------
     const bool act = lane < n;
     const int64_t t = t0 + lane;
-    int flag = 0, piv = 0, hi = 0;
+    int flag = 0, piv = 0, hi = 0, bw = 0;
     float v[G];
     if (act) {
       float m1, m2, l1, S;
@@ -303,8 +322,11 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
         // Eq. (1)-(2)
         if constexpr (kFused) a.H[t] = entropy_from_sums(l1, S, lt);
         else a.H[t] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);
-      } else {
+      } else if constexpr (MODE == 1) {
         hi = (a.bitmap[t >> 5] >> (t & 31)) & 1u;
+      } else {
+        const uint32_t lv = (a.bitmap[t >> 4] >> (2 * (t & 15))) & 3u;
+        bw = (int)((a.cands >> (8 * lv)) & 255u);
       }
       // side byte: the flag, and the pivot of a transformed tile (0 for the others)
       if (a.payload) a.payload[a.off_side + t] = (uint8_t)(flag ? (0x80 | piv) : 0);
@@ -314,7 +336,17 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
     // the 64 tiles of a group are one run of the block table.
     const uint64_t hmask = ballot(act && hi);
     int64_t code_off = a.off_codes + t * a.sz_lo;
-    if constexpr (MIXED) {
+    if constexpr (MODE == 2) {
+      // G/8 bytes per unit of width: the table's sum before the group plus the
+      // widths of the lanes below
+      uint32_t incl = (uint32_t)bw;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      code_off = a.off_codes + (int64_t)(G / 8) * ((int64_t)a.table[t0 >> 6] + (int64_t)(incl - (uint32_t)bw));
+    } else if constexpr (MIXED) {
       const uint32_t hb = a.table[t0 >> 6] + lanes_below(hmask);
       code_off += (int64_t)hb * (a.sz_hi - a.sz_lo);
     } else {
@@ -328,7 +360,7 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
     }
 
     // ---------------- transformed tiles (§3.3) and quantization ----------------
-    const int b = hi ? a.b_hi : a.b_lo;
+    const int b = MODE == 2 ? bw : (hi ? a.b_hi : a.b_lo);
     if (act) {
       if (flag) {  // P_d in the lane's own row, then H of Eq. (4) in registers
         uint8_t* row = xs + lane * RI::kStride;
@@ -338,7 +370,7 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
         lds_read_tile<G, TIn>(row, v);
         fwht<G>(v);
       }
-      quantize_tile<G, OUT>(a, v, t, b, code_off);
+      quantize_tile<G, OUT, MODE == 2>(a, v, t, b, code_off);
       if constexpr (OUT != 0) {
         if (flag) {  // H^T = H, the 1/G
           fwht<G>(v);
@@ -386,31 +418,34 @@ static int cu_count() {
   return cus;
 }
 
-template <int G, typename TIn, int OUT, bool MIXED>
+template <int G, typename TIn, int OUT, int MODE>
 static hipError_t launch_one(const EncArgs& a, hipStream_t st) {
   constexpr int NT = 64;
-  static const int per_cu = wgs_per_cu(k_encode<G, TIn, OUT, MIXED>, NT);
+  static const int per_cu = wgs_per_cu(k_encode<G, TIn, OUT, MODE>, NT);
   const int64_t ngroups = a.tiles > 0 ? (a.tiles + NT - 1) / NT : 1;
   const int64_t resident = (int64_t)per_cu * cu_count();
   const int64_t nwg = ngroups < resident ? ngroups : resident;
-  hipLaunchKernelGGL((k_encode<G, TIn, OUT, MIXED>), dim3((unsigned)nwg), dim3(NT), 0, st, a);
+  hipLaunchKernelGGL((k_encode<G, TIn, OUT, MODE>), dim3((unsigned)nwg), dim3(NT), 0, st, a);
   return hipGetLastError();
 }
 
+template <int G, typename TIn, int MODE>
+static hipError_t dispatch_mode(const EncArgs& a, int out, hipStream_t st) {
+  if (out == 1) return launch_one<G, TIn, 1, MODE>(a, st);
+  if (out == 2) return launch_one<G, TIn, 2, MODE>(a, st);
+  return launch_one<G, TIn, 0, MODE>(a, st);
+}
+
 template <int G, typename TIn>
-static hipError_t dispatch_out(const EncArgs& a, int out, bool mixed, hipStream_t st) {
-  if (mixed) {
-    if (out == 1) return launch_one<G, TIn, 1, true>(a, st);
-    if (out == 2) return launch_one<G, TIn, 2, true>(a, st);
-    return launch_one<G, TIn, 0, true>(a, st);
-  }
-  if (out == 1) return launch_one<G, TIn, 1, false>(a, st);
-  if (out == 2) return launch_one<G, TIn, 2, false>(a, st);
-  return launch_one<G, TIn, 0, false>(a, st);
+static hipError_t dispatch_out(const EncArgs& a, int out, int mode, hipStream_t st) {
+  if (mode == 2) return dispatch_mode<G, TIn, 2>(a, out, st);
+  if (mode == 1) return dispatch_mode<G, TIn, 1>(a, out, st);
+  return dispatch_mode<G, TIn, 0>(a, out, st);
 }
 
 hipError_t launch_encode(const Plan& pl, const void* x, void* payload, void* y, int y_dtype, void* ws,
-                         hipStream_t st, bool mixed) {
+                         hipStream_t st, int mode) {
+  const bool mixed = mode != 0;
   EncArgs a;
   a.x = static_cast<const uint8_t*>(x);
   a.y = static_cast<uint8_t*>(y);
@@ -438,15 +473,19 @@ hipError_t launch_encode(const Plan& pl, const void* x, void* payload, void* y, 
   a.b_hi = pl.b_hi;
   a.sz_lo = pl.G * pl.b_lo / 8;
   a.sz_hi = pl.G * pl.b_hi / 8;
+  a.cands = 0;
+  for (int i = 0; i < pl.n_candidates; ++i) a.cands |= (uint32_t)pl.candidates[i] << (8 * i);
+  a.wtotal = reinterpret_cast<const uint32_t*>(w + pl.ws_wtotal);
+  a.code_end = pl.off_codes + pl.code_bytes;
   a.tau = pl.tau;
   make_header(pl, &a.hdr);
   make_pads(pl, &a.pads);
   const int out = y ? (y_dtype == TAH_DTYPE_F32 ? 1 : 2) : 0;
   const bool bf = pl.x_dtype == TAH_DTYPE_BF16;
   switch (pl.G) {
-    case 32: return bf ? dispatch_out<32, bf16_t>(a, out, mixed, st) : dispatch_out<32, float>(a, out, mixed, st);
-    case 64: return bf ? dispatch_out<64, bf16_t>(a, out, mixed, st) : dispatch_out<64, float>(a, out, mixed, st);
-    case 128: return bf ? dispatch_out<128, bf16_t>(a, out, mixed, st) : dispatch_out<128, float>(a, out, mixed, st);
+    case 32: return bf ? dispatch_out<32, bf16_t>(a, out, mode, st) : dispatch_out<32, float>(a, out, mode, st);
+    case 64: return bf ? dispatch_out<64, bf16_t>(a, out, mode, st) : dispatch_out<64, float>(a, out, mode, st);
+    case 128: return bf ? dispatch_out<128, bf16_t>(a, out, mode, st) : dispatch_out<128, float>(a, out, mode, st);
     default: return hipErrorInvalidValue;
   }
 }

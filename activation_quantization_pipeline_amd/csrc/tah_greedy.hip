@@ -1,0 +1,304 @@
+// Greedy bit allocation over every candidate width for gfx950 (the allocator
+// TAH_ALLOC_GREEDY of tah.h). The pages rank a sample's tiles by entropy and
+// give the top p% the higher of two widths (TAH-Quant §3.2); for more widths
+// this allocator takes upgrades c_j -> c_(j+1) in order of their gain per bit,
+// whose log2 is kappa = 2 H_u + lambda_j, while the sample's R bits last.
+//
+// The upgrades taken form a prefix of the order (kappa descending, tile index
+// ascending, j ascending), so the allocation is fixed by its first upgrade
+// that does not fit, e*. Each upgrade is one 64-bit composite: the 32-bit
+// order-preserving key of kappa above the complemented upgrade index
+// u * nl + j; composites are unique and a larger one comes first. e* is the
+// composite where the running cost first exceeds R, found by a radix select
+// whose histograms add each upgrade's cost instead of 1:
+//   k_ghist  - one launch per digit (11 bits, top digit first, up to 6). Each
+//              workgroup applies the previous digit (one wavefront scans that
+//              histogram of the sample, descending, and finds the bin where
+//              the running cost reaches r = remaining budget + 1), then adds
+//              the costs of the upgrades that match the prefix into a
+//              2048-bin LDS histogram and into the sample's global one.
+//              Histograms rotate over three buffers and states over two, so
+//              kernel boundaries are the only synchronisation;
+//   k_gfinal - applies the last digit: the composite of e* per sample;
+//   k_glevel - one lane per quantization tile: its level is the count of its
+//              allocation tile's upgrades whose composite is above e*'s; the
+//              2-bit level map and the sum of the widths per 64 tiles;
+//   k_table  - (tah_select.hip) exclusive scan of those sums: the block table,
+//              which locates every code block, and the total width (the used
+//              part of the code section).
+// When no upgrade or every upgrade fits (R = 0, one candidate, or R covering
+// all of them) the select is skipped and every tile takes the same level.
+#include "tah_device.hpp"
+#include "tah_internal.hpp"
+
+namespace tah {
+
+// fp32 -> uint32 with the same order (keys are finite).
+__device__ __forceinline__ uint32_t key_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+struct GArgs {
+  const float* H;  // entropy per allocation tile
+  int64_t N;       // allocation tiles per sample
+  int32_t nl, ib;  // upgrades per tile, index bits of the composite
+  float lam[3];    // lambda_j
+  int32_t cost[3]; // c_(j+1) - c_j
+};
+
+// Upgrade j of tile u of a sample: kappa = 2 H_u + lambda_j in fp32 (2 H_u is
+// exact, so a fused multiply-add rounds the same), above the complemented index.
+__device__ __forceinline__ uint64_t composite(const GArgs& g, float h, int64_t u, int j) {
+  const float kappa = 2.0f * h + g.lam[j];
+  const uint64_t imax = (1ull << g.ib) - 1ull;
+  const uint64_t idx = (uint64_t)u * (uint64_t)g.nl + (uint64_t)j;
+  return ((uint64_t)key_bits(kappa) << g.ib) | (imax - idx);
+}
+
+// One wavefront: finds the digit of the pass whose bin holds cost position r
+// (1-based) in descending order of the sample's histogram h, then narrows the
+// state to it. r never exceeds the histogram's total: the host runs the
+// select only when R is below the cost of all upgrades.
+__device__ __forceinline__ GState apply_gpass(GState S, const uint32_t* h, const GPass& ps) {
+  const int lane = threadIdx.x & 63;
+  constexpr int PER = kBins / 64;
+  uint32_t c[PER];
+  uint64_t sum = 0;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    c[i] = h[kBins - 1 - (lane * PER + i)];
+    sum += c[i];
+  }
+  uint64_t incl = sum;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const uint64_t o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  const uint64_t excl = incl - sum;
+  const bool here = (int64_t)excl < S.r && S.r <= (int64_t)incl;
+  const uint64_t hm = ballot(here);
+  if (hm == 0) return S;
+  const int src = __ffsll((unsigned long long)hm) - 1;
+  int ord = 0;
+  int64_t before = 0;
+  if (here) {
+    before = (int64_t)excl;
+    ord = lane * PER;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      if (before + (int64_t)c[i] >= S.r) {
+        ord = lane * PER + i;
+        break;
+      }
+      before += c[i];
+    }
+  }
+  ord = __shfl(ord, src, 64);
+  before = (int64_t)__shfl((long long)before, src, 64);
+  S.r -= before;
+  S.prefix |= (uint64_t)(kBins - 1 - ord) << ps.shift;
+  return S;
+}
+
+// ------------------------------------------------------------------ hist ----
+struct GHistArgs {
+  GArgs g;
+  const GState* st_prev;      // state before the previous pass (unused on pass 0)
+  GState* st_cur;             // state before this pass, written by each sample's first block
+  const uint32_t* hist_prev;  // previous pass's histograms
+  uint32_t* hist_cur;         // this pass's histograms (zero on entry)
+  uint32_t* hist_clear;       // the next pass's histograms, cleared here
+  int64_t chunks_per_sample, R;
+  GPass pass, prev;
+  int32_t has_prev, tb;  // tb: composite bits, 32 + ib
+};
+
+constexpr int kGThreads = 1024;
+constexpr int kGPerThread = 16;
+constexpr int kGChunk = kGThreads * kGPerThread;  // allocation tiles per workgroup
+
+__global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ GState ss;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t s = blockIdx.x / a.chunks_per_sample;
+  const int64_t c = blockIdx.x % a.chunks_per_sample;
+  const int64_t u0 = c * kGChunk;
+  {  // the next pass's histogram of this sample, cleared in slices by the sample's blocks
+    const int64_t per = (kBins + a.chunks_per_sample - 1) / a.chunks_per_sample;
+    const int64_t b0 = c * per, b1 = b0 + per < kBins ? b0 + per : kBins;
+    for (int64_t i = b0 + tid; i < b1; i += kGThreads) a.hist_clear[s * kBins + i] = 0u;
+  }
+  for (int i = tid; i < kBins; i += kGThreads) lh[i] = 0u;
+  if (tid < 64) {
+    GState S;
+    if (a.has_prev) {
+      S = apply_gpass(a.st_prev[s], a.hist_prev + s * kBins, a.prev);
+    } else {
+      S.prefix = 0ull;
+      S.r = a.R + 1;  // the first upgrade whose running cost exceeds R
+    }
+    if (tid == 0) {
+      ss = S;
+      if (c == 0) a.st_cur[s] = S;
+    }
+  }
+  __syncthreads();
+  const GState S = ss;
+  const int hs = a.pass.shift + a.pass.width;  // composite bits above the current digit
+  const uint64_t dmask = (1ull << a.pass.width) - 1ull;
+  const uint64_t want_hi = hs >= 64 ? 0ull : (S.prefix >> hs);
+  float hv[kGPerThread];  // all loads in flight before the first use
+#pragma unroll
+  for (int i = 0; i < kGPerThread; ++i) {
+    const int64_t u = u0 + i * kGThreads + tid;
+    hv[i] = u < a.g.N ? a.g.H[s * a.g.N + u] : 0.0f;
+  }
+  for (int j = 0; j < a.g.nl; ++j) {
+    const uint32_t cost = (uint32_t)a.g.cost[j];
+#pragma unroll
+    for (int i = 0; i < kGPerThread; ++i) {
+      const int64_t u = u0 + i * kGThreads + tid;
+      bool want = false;
+      uint32_t digit = 0;
+      if (u < a.g.N) {
+        const uint64_t C = composite(a.g, hv[i], u, j);
+        want = hs >= 64 || (C >> hs) == want_hi;
+        digit = (uint32_t)((C >> a.pass.shift) & dmask);
+      }
+      // lanes with the same digit as the first remaining lane add together
+      // (twice), the rest one by one
+#pragma unroll
+      for (int round = 0; round < 2; ++round) {
+        const uint64_t wm = ballot(want);
+        if (wm == 0) break;
+        const int leader = __ffsll((unsigned long long)wm) - 1;
+        const uint32_t d0 = (uint32_t)__shfl((int)digit, leader, 64);
+        const bool same = want && digit == d0;
+        const uint64_t sm = ballot(same);
+        if (lane == leader) atomicAdd(&lh[d0], (uint32_t)__popcll(sm) * cost);
+        want = want && !same;
+      }
+      if (want) atomicAdd(&lh[digit], cost);
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < kBins; i += kGThreads)
+    if (lh[i]) atomicAdd(&a.hist_cur[s * kBins + i], lh[i]);
+}
+
+// One wavefront per sample: the last digit, which completes e*'s composite.
+__global__ __launch_bounds__(64) void k_gfinal(const GState* st_prev, const uint32_t* hist_last, GState* st_out,
+                                               GPass last) {
+  const int64_t s = blockIdx.x;
+  const GState S = apply_gpass(st_prev[s], hist_last + s * kBins, last);
+  if (threadIdx.x == 0) st_out[s] = S;
+}
+
+// ------------------------------------------------------------------ levels ----
+struct LevelArgs {
+  GArgs g;
+  const GState* st;  // e* per sample (unused when glevel >= 0)
+  uint32_t* map;     // 2 bits per tile, 4 words per 64 tiles
+  uint32_t* wsum;    // per 64 tiles: the sum of their code widths
+  int64_t tiles, nblocks, kA;
+  int32_t glevel;    // >= 0: every tile takes this level
+  uint32_t cands;    // candidate widths, one byte each, c_1 lowest
+};
+
+__global__ __launch_bounds__(256) void k_glevel(LevelArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t t = (int64_t)blockIdx.x * 256 + tid;
+  int lv = 0, w = 0;
+  if (t < a.tiles) {
+    if (a.glevel >= 0) {
+      lv = a.glevel;
+    } else {
+      const int64_t ta = a.kA == 1 ? t : t / a.kA;  // allocation tile
+      const int64_t s = ta / a.g.N;
+      const int64_t u = ta - s * a.g.N;
+      const float h = a.g.H[ta];
+      const uint64_t P = a.st[s].prefix;
+      for (int j = 0; j < a.g.nl; ++j) lv += composite(a.g, h, u, j) > P ? 1 : 0;
+    }
+    w = (int)((a.cands >> (8 * lv)) & 255u);
+  }
+  uint32_t f = (uint32_t)lv << (2 * (lane & 15));
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) f |= (uint32_t)__shfl_xor((int)f, off, 64);
+  int sum = w;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) sum += __shfl_xor(sum, off, 64);
+  const int64_t blk = ((int64_t)blockIdx.x * 256 + (tid & ~63)) >> 6;
+  if (blk < a.nblocks) {
+    if ((lane & 15) == 0) a.map[4 * blk + (lane >> 4)] = f;
+    if (lane == 0) a.wsum[blk] = (uint32_t)sum;
+  }
+}
+
+hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st) {
+  uint8_t* w = static_cast<uint8_t*>(ws);
+  uint8_t* P = static_cast<uint8_t*>(payload);
+  GArgs g;
+  g.H = reinterpret_cast<const float*>(w + pl.ws_H);
+  g.N = pl.N;
+  g.nl = pl.nl;
+  g.ib = pl.ib;
+  for (int j = 0; j < 3; ++j) {
+    g.lam[j] = pl.lam[j];
+    g.cost[j] = pl.cost[j];
+  }
+  GState* states = reinterpret_cast<GState*>(w + pl.ws_state);
+  const int64_t ns = pl.nsamples;
+  GState* final_st = nullptr;
+  if (pl.glevel < 0) {
+    uint32_t* hists = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
+    const int64_t hsz = ns * kBins;
+    GHistArgs h;
+    h.g = g;
+    h.chunks_per_sample = (pl.N + kGChunk - 1) / kGChunk;
+    h.R = pl.R;
+    h.tb = 32 + pl.ib;
+    const int np = pl.ngpasses;
+    // pass p: state p in states[p % 2], histogram p in hists[p % 3] (zeroed
+    // by k_stats for p = 0)
+    for (int p = 0; p < np; ++p) {
+      h.pass = pl.gpasses[p];
+      h.has_prev = p > 0;
+      h.prev = p > 0 ? pl.gpasses[p - 1] : pl.gpasses[p];
+      h.st_prev = states + ((p + 1) % 2) * ns;
+      h.st_cur = states + (p % 2) * ns;
+      h.hist_prev = hists + ((p + 2) % 3) * hsz;
+      h.hist_cur = hists + (p % 3) * hsz;
+      h.hist_clear = hists + ((p + 1) % 3) * hsz;
+      hipLaunchKernelGGL(k_ghist, dim3((unsigned)(h.chunks_per_sample * ns)), dim3(kGThreads), 0, st, h);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
+    final_st = states + (np % 2) * ns;
+    hipLaunchKernelGGL(k_gfinal, dim3((unsigned)ns), dim3(64), 0, st, (const GState*)(states + ((np + 1) % 2) * ns),
+                       (const uint32_t*)(hists + ((np + 2) % 3) * hsz), final_st, pl.gpasses[np - 1]);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  LevelArgs L;
+  L.g = g;
+  L.st = final_st;
+  L.map = reinterpret_cast<uint32_t*>(P ? P + pl.off_bitmap : w + pl.ws_bitmap);
+  L.wsum = reinterpret_cast<uint32_t*>(w + pl.ws_blockcnt);
+  L.tiles = pl.tiles;
+  L.nblocks = pl.nblocks;
+  L.kA = pl.kA;
+  L.glevel = pl.glevel;
+  L.cands = 0;
+  for (int i = 0; i < pl.n_candidates; ++i) L.cands |= (uint32_t)pl.candidates[i] << (8 * i);
+  hipLaunchKernelGGL(k_glevel, dim3((unsigned)((pl.tiles + 255) / 256)), dim3(256), 0, st, L);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  uint32_t* table = reinterpret_cast<uint32_t*>(P ? P + pl.off_table : w + pl.ws_table);
+  return launch_table(L.wsum, table, reinterpret_cast<uint32_t*>(w + pl.ws_wtotal), pl.nblocks, st);
+}
+
+}  // namespace tah

@@ -27,12 +27,28 @@ struct SelectPass {
   int32_t last_h; // 1 on the last entropy pass
 };
 
+// One digit of the greedy allocator's select over 64-bit (key, index) composites.
+struct GPass {
+  int32_t shift, width;
+};
+
 struct Plan {
   int64_t tokens, hidden, S, nsamples, M, tiles, nblocks;
   int32_t G, log2G, b_lo, b_hi;
   // allocation tiles (§3.2): A = kA * G channels, atiles in all, N per sample
   int64_t A, kA, atiles, N;
   int64_t k;  // allocation tiles per sample with b_hi
+  // width layout of the encoder: 0 one width, 1 two widths (top-p% select),
+  // 2 any candidate per tile (greedy allocator, 2-bit level map)
+  int32_t allocator, mode;
+  // greedy allocator: R bits per sample above c_1; nl upgrades per tile with
+  // constants lam and costs cost; the select runs over composites of 32 key
+  // bits and ib index bits unless every tile takes the same level (glevel >= 0)
+  int64_t R;
+  int32_t nl, ib, glevel, ngpasses;
+  float lam[3];
+  int32_t cost[3];
+  GPass gpasses[kMaxPasses];
   int32_t x_dtype;
   float tau, budget;
   int32_t n_candidates;
@@ -40,10 +56,17 @@ struct Plan {
   // payload layout
   int64_t off_table, off_bitmap, off_side, off_scale, off_zero, off_codes, code_bytes, total;
   // workspace layout
-  int64_t ws_status, ws_state, ws_hist, ws_H, ws_LS, ws_blockcnt, ws_table, ws_bitmap, ws_cand, ws_total;
+  int64_t ws_status, ws_state, ws_hist, ws_H, ws_LS, ws_blockcnt, ws_table, ws_bitmap, ws_cand, ws_wtotal, ws_total;
   int64_t ncand, cand_stride;  // capacity of a sample's candidate list; its uint32 words
   int32_t npasses;
   SelectPass passes[kMaxPasses];
+};
+
+// Per-sample state of the greedy allocator's select: the composite prefix
+// found so far and the bit position (1-based, by weight) still to place in it.
+struct GState {
+  uint64_t prefix;
+  int64_t r;
 };
 
 // Per-sample selection state, device resident.
@@ -66,11 +89,17 @@ struct PadRanges {
 };
 
 // Launchers (return hipSuccess or the launch error).
+// mode: the width layout (Plan::mode), 0 when the tensor is empty
 hipError_t launch_encode(const Plan& pl, const void* x, void* payload, void* y, int y_dtype, void* ws,
-                         hipStream_t st, bool mixed);
+                         hipStream_t st, int mode);
 // Entropy of every allocation tile into h_out (pl.atiles values).
 hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, bool init_select, hipStream_t st);
 hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st);
+// Greedy allocator (tah_greedy.hip): levels, width sums, block table.
+hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st);
+// Exclusive scan of per-64-tile counts into the block table; total (may be
+// null) receives the sum of all counts.
+hipError_t launch_table(const uint32_t* cnt, uint32_t* table, uint32_t* total, int64_t nblocks, hipStream_t st);
 hipError_t launch_decode(const Plan& pl, const void* payload, void* y, int y_dtype, void* ws, hipStream_t st);
 
 // Backward compressor (tah_naive.hip).

@@ -127,7 +127,7 @@ hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, b
   a.ls = reinterpret_cast<float2*>(w + pl.ws_LS);
   a.hist = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
   a.tiles = pl.tiles;
-  a.hist_words = pl.k > 0 ? pl.nsamples * kBins : 0;
+  a.hist_words = init_select ? pl.nsamples * kBins : 0;
   a.init = init_select ? 1 : 0;
   const bool bf = pl.x_dtype == TAH_DTYPE_BF16, sums = pl.kA > 1;
   hipError_t e;
@@ -437,7 +437,9 @@ constexpr int kScanStep = kScanThreads * kScanPer;
 // Exclusive scan of the per-64-tile counts. Global memory is read and written
 // coalesced (through an LDS copy of the step); each thread scans kScanPer
 // consecutive counts, then the threads' totals are scanned across the block.
-__global__ __launch_bounds__(kScanThreads) void k_table(const uint32_t* cnt, uint32_t* table, int64_t nblocks) {
+// total (may be null) receives the sum of all counts.
+__global__ __launch_bounds__(kScanThreads) void k_table(const uint32_t* cnt, uint32_t* table, uint32_t* total,
+                                                        int64_t nblocks) {
   __shared__ uint32_t buf[kScanStep];
   __shared__ uint32_t wsum[kScanThreads / 64];
   __shared__ uint32_t carry_s;
@@ -485,6 +487,12 @@ __global__ __launch_bounds__(kScanThreads) void k_table(const uint32_t* cnt, uin
     }
     __syncthreads();
   }
+  if (total && tid == 0) *total = carry_s;
+}
+
+hipError_t launch_table(const uint32_t* cnt, uint32_t* table, uint32_t* total, int64_t nblocks, hipStream_t st) {
+  hipLaunchKernelGGL(k_table, dim3(1), dim3(kScanThreads), 0, st, cnt, table, total, nblocks);
+  return hipGetLastError();
 }
 
 hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st) {
@@ -550,8 +558,7 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   uint32_t* table = reinterpret_cast<uint32_t*>(P ? P + pl.off_table : w + pl.ws_table);
-  hipLaunchKernelGGL(k_table, dim3(1), dim3(kScanThreads), 0, st, (const uint32_t*)m.blockcnt, table, pl.nblocks);
-  return hipGetLastError();
+  return launch_table(m.blockcnt, table, nullptr, pl.nblocks, st);
 }
 
 }  // namespace tah

@@ -37,7 +37,7 @@
 extern "C" {
 #endif
 
-#define TAH_ABI_VERSION 2
+#define TAH_ABI_VERSION 3
 
 typedef enum { TAH_DTYPE_F32 = 0, TAH_DTYPE_BF16 = 1 } tah_dtype_t;
 
@@ -73,7 +73,24 @@ typedef enum {
  *     (Eq. 1-2 over all A channels) adds the per-quantization-tile sums
  *     L = sum |a| and S = sum |a| log2 |a| left to right; each quantization
  *     tile takes the width of its allocation tile.
+ *   allocator: TAH_ALLOC_TOP_P (0, the paper's rule above) or
+ *     TAH_ALLOC_GREEDY (1): every candidate width may occur in a sample. The
+ *     paper gives no rule for more than two widths; this one reads its entropy
+ *     ranking as a distortion budget. Tile u weighs 2^(2 H_u); upgrade j of a
+ *     tile (c_j -> c_(j+1), costing c_(j+1) - c_j bits) has the key
+ *       kappa = 2 H_u + lambda_j (fp32),
+ *       lambda_j = log2((Delta(c_j) - Delta(c_(j+1))) / (c_(j+1) - c_j)),
+ *       Delta(b) = (2^b - 1)^-2,
+ *     the log2 of its gain per bit; starting from c_1 everywhere, upgrades are
+ *     taken in the order kappa descending, then tile index, then j, while the
+ *     bits they add stay within R = floor((budget - c_1) * N) per sample; the
+ *     first that does not fit ends the allocation. With two candidates this
+ *     is the top-p% rule. Limits: tokens * hidden / tile * c_n below 2^32
+ *     (else TAH_ERR_INVALID_ARG) and (c_n - c_1) * N below 2^32 (else
+ *     TAH_ERR_UNSUPPORTED).
  */
+#define TAH_ALLOC_TOP_P 0
+#define TAH_ALLOC_GREEDY 1
 typedef struct {
   int32_t tile;
   int32_t tokens_per_sample;
@@ -82,6 +99,7 @@ typedef struct {
   uint8_t candidates[4];
   float tau;
   int32_t alloc_tile;
+  int32_t allocator;
 } tah_params_t;
 
 /* Fills the paper's defaults (§5.1): G = A = 64, 80% INT4 + 20% INT3
@@ -93,11 +111,16 @@ void tah_params_default(tah_params_t* p);
  * fixed-shape uint8 stream (§3.4): its size depends only on (tokens, hidden,
  * params), never on the values. Layout (little-endian, sections on 256-byte
  * boundaries): 128-byte header (magic "TAHQ", version 2, shape, params,
- * section offsets, allocation tile A as u32 at byte 120) | u32 count of b_hi
- * tiles before each run of 64 tiles | width map, one bit per quantization tile
- * (1 = b_hi; an allocation tile's bits are equal) | side byte per tile (bit 7: Hadamard applied,
+ * section offsets, allocation tile A as u32 at byte 120, allocator at byte
+ * 124) | block table, u32 per run of 64 tiles: the count of b_hi tiles before
+ * it (top-p%) or the sum of the code widths of the tiles before it (greedy) |
+ * width map, one bit per quantization tile (1 = b_hi; top-p%) or two bits,
+ * the candidate index, at bits 2(t%16) of word t/16 (greedy); an allocation
+ * tile's entries are equal | side byte per tile (bit 7: Hadamard applied,
  * bits 0-6: pivot index of a transformed tile, 0 otherwise) | bf16 scale per tile | fp32 zero-point per tile |
  * code blocks of G*b/8 bytes in tile order, codes least-significant-bit first.
+ * Under the greedy allocator the code section is sized for the whole budget
+ * and its unused tail is zero.
  */
 tah_status_t tah_payload_bytes(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* out);
 

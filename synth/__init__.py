@@ -184,7 +184,8 @@ NAIVE = {
 
 # Coverage variants: mixed allocations at other budgets, the tau values of
 # App. F (0, 2, 4, never), allocation tiles of several quantization tiles up to
-# whole tokens (Sec. 3.2: A = C is token-level allocation).
+# whole tokens (Sec. 3.2: A = C is token-level allocation), and the greedy
+# allocator over every candidate width.
 COVERAGE = {
     "x1a_c2_budget5": ("c2_4096x2048_bf16_g64", dict(bit_budget=5.0, candidates=(3, 4, 8))),
     "x1b_c2_budget2p5": ("c2_4096x2048_bf16_g64", dict(bit_budget=2.5, candidates=(2, 3, 4, 8))),
@@ -197,6 +198,10 @@ COVERAGE = {
     "x4a_c2_alloc256": ("c2_4096x2048_bf16_g64", dict(alloc_tile=256)),
     "x4b_c5_token_level": ("c5_8192x8192_bf16_g64", dict(bit_budget=3.8, candidates=(3, 4, 8), alloc_tile=8192)),
     "x4c_c4_token_level": ("c4_16384x5120_f32_g128", dict(alloc_tile=5120)),
+    # the greedy allocator over every candidate width (allocator 1)
+    "x5a_c2_greedy": ("c2_4096x2048_bf16_g64", dict(allocator=1)),
+    "x5b_c5_greedy": ("c5_8192x8192_bf16_g64", dict(bit_budget=3.8, candidates=(3, 4, 8), allocator=1)),
+    "x5c_c4_greedy_a640": ("c4_16384x5120_f32_g128", dict(alloc_tile=640, allocator=1)),
 }
 
 

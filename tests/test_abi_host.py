@@ -7,6 +7,7 @@ import math
 import os
 import re
 
+import numpy as np
 import pytest
 
 import activation_quantization_pipeline_amd as tah
@@ -29,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(tah.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert tah.abi_version() == 2
+    assert tah.abi_version() == 3
 
 
 def test_params_default_is_paper_default():
@@ -182,3 +183,32 @@ def test_binding_refuses_host_tensors_before_any_device_call():
     for i, call in enumerate(calls):
         with pytest.raises(tah.TahError):
             call()
+
+
+def test_greedy_allocator_sizes_and_errors(ref):
+    """The greedy allocator's payload and header layout agree with the oracle's
+    plan (sizes of every section, R), and its argument errors come back before
+    any device call."""
+    g = np.random.default_rng(4)
+    for trial in range(200):
+        G = int(g.choice([32, 64, 128]))
+        M = int(g.integers(1, 20))
+        tokens = int(g.integers(0, 300))
+        S = int(g.choice([0] + [d for d in range(1, max(tokens, 1) + 1) if tokens % d == 0][:6]))
+        kA = int(g.choice([k for k in range(1, M + 1) if M % k == 0]))
+        n = int(g.integers(1, 5))
+        cands = tuple(sorted(int(c) for c in g.choice(np.arange(1, 9), n, replace=False)))
+        budget = float(np.float32(g.uniform(cands[0], cands[-1] + 1)))
+        p = synth.Params(tile=G, tokens_per_sample=S, bit_budget=budget, candidates=cands, alloc_tile=G * kA,
+                         allocator=1)
+        pl = ref.plan(tokens, G * M, p)
+        assert tah.payload_bytes(tokens, G * M, p) == pl["total"], p
+        assert tah.workspace_bytes(tokens, G * M, p) >= 4 * pl["atiles"]
+    good = tah.TahParams(tile=64, bit_budget=3.5, candidates=(2, 3, 4, 8), allocator=tah.ALLOC_GREEDY)
+    assert _call_encode(tah.TahParams(**{**good.__dict__, "allocator": 2})) == 1
+    assert _call_encode(tah.TahParams(**{**good.__dict__, "allocator": -1})) == 1
+    assert _call_encode(tah.TahParams(**{**good.__dict__, "bit_budget": 1.5})) == 4
+    assert _call_encode(good, x=0) == 1  # valid parameters, then the null input pointer
+    # the block table's running width sums are 32-bit: 2^32 / 8 tiles at 8 bits do not fit
+    big = tah.TahParams(tile=64, bit_budget=8.0, candidates=(8,), allocator=tah.ALLOC_GREEDY)
+    assert _call_encode(big, tokens=1 << 23, hidden=64 * 64) == 1

@@ -1,0 +1,118 @@
+"""GPU-vs-oracle parity of the greedy allocator over every candidate width
+(allocator 1), through the C ABI: payload bytes bit for bit (level map,
+width-sum table, codes, the zeroed tail of the code section) and decoded
+values bit for bit, for encode, decode and both round trips.
+
+The full-size workloads with this allocator (4096 x 2048 over {2,3,4,8},
+8192 x 8192 over {3,4,8}, 16384 x 5120 fp32 with A = 640) run in
+test_parity_gpu.py's workload test; here: the degenerate budgets (nothing
+fits, everything fits, one candidate), ties of every key, ragged shapes,
+small samples, and seeded random configurations.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import activation_quantization_pipeline_amd as tah
+import oracle
+import synth
+from test_parity_gpu import assert_decoded_equal, random_config, run_case, say, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+P = tah.TahParams
+GREEDY = tah.ALLOC_GREEDY
+
+
+def levels_used(R, pl):
+    words = R[pl["off_bitmap"]:pl["off_bitmap"] + 16 * pl["nblocks"]].view(np.uint32)
+    t = np.arange(pl["tiles"])
+    return np.unique((words[t // 16] >> (2 * (t % 16)).astype(np.uint32)) & 3)
+
+
+@pytest.mark.parametrize("budget,cands,want", [
+    (2.0, (2, 3, 4, 8), {0}),          # R = 0: every tile at c_1, no select
+    (8.0, (2, 3, 4, 8), {3}),          # R covers every upgrade
+    (9.5, (3, 4, 8), {2}),             # budget above the widest candidate
+    (4.0, (4,), {0}),                  # one candidate
+    (2.01, (2, 8), {0, 1}),            # R below one upgrade's cost in most samples
+    (3.3, (2, 3, 4, 8), {0, 1, 2, 3}),
+])
+def test_degenerate_budgets(budget, cands, want):
+    x = synth.random_tensor(96, 512, synth.BF16, 3, n_out=3, mult=40)
+    p = P(tile=64, tokens_per_sample=32, bit_budget=budget, candidates=cands, tau=2.0, allocator=GREEDY)
+    R, _ = run_case(x, p, f"greedy budget {budget} cands {cands}")
+    pl = oracle.plan(96, 512, p)
+    assert set(levels_used(R, pl).tolist()) <= want | {0}
+    if len(want) == 1:
+        assert set(levels_used(R, pl).tolist()) == want
+
+
+@pytest.mark.parametrize("tile", [32, 64, 128])
+def test_every_key_ties(tile):
+    """A tensor of identical tiles: every entropy is equal, so every upgrade of
+    a level ties and the upgrade index alone orders them (the lower tile first)."""
+    row = synth.random_tensor(1, tile, synth.F32, 5, n_out=1, mult=10)
+    x = np.tile(row, (40, 7)).astype(np.float32)
+    for budget, cands in ((3.37, (2, 3, 4, 8)), (4.5, (3, 8)), (2.9, (1, 2, 3, 4))):
+        run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=budget, candidates=cands, tau=2.0, allocator=GREEDY),
+                 f"ties tile {tile} {cands} {budget}")
+    z = np.zeros((40, tile * 7), np.float32)  # all-zero tiles: H = 0 everywhere
+    run_case(z, P(tile=tile, tokens_per_sample=8, bit_budget=3.5, candidates=(2, 3, 4, 8), tau=2.0, allocator=GREEDY),
+             f"zeros tile {tile}")
+
+
+@pytest.mark.parametrize("tile", [32, 64, 128])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_ragged_shapes(tile, dtype):
+    for tokens, mult in ((1, 5), (3, 5), (7, 9), (65, 3), (300, 7)):
+        x = synth.random_tensor(tokens, tile * mult, dtype, tokens + mult, n_out=2, mult=25)
+        run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=3.4, candidates=(2, 3, 4, 8), tau=2.0,
+                      allocator=GREEDY), f"greedy ragged t{tokens} m{mult}")
+
+
+@pytest.mark.parametrize("S,A", [(1, 0), (3, 0), (16, 0), (16, 320), (4, 64)])
+def test_small_samples_and_allocation_tiles(S, A):
+    x = synth.random_tensor(48, 320, synth.BF16, S, n_out=3, mult=30)
+    run_case(x, P(tile=64, tokens_per_sample=S, bit_budget=3.5, candidates=(2, 3, 4, 8), tau=2.0, alloc_tile=A,
+                  allocator=GREEDY), f"greedy S={S} A={A}")
+    run_case(x, P(tile=32, tokens_per_sample=S, bit_budget=2.6, candidates=(1, 2, 5), tau=2.0, alloc_tile=A // 2,
+                  allocator=GREEDY), f"greedy S={S} A={A // 2} tile32")
+
+
+def test_empty_tensor():
+    p = P(tile=64, tokens_per_sample=0, bit_budget=3.5, candidates=(2, 3, 4, 8), tau=2.0, allocator=GREEDY)
+    x = np.zeros((0, 256), np.float32)
+    R = oracle.encode(x, p)
+    P_ = to_host(tah.encode(to_dev(x), p))
+    torch.cuda.synchronize()
+    assert np.array_equal(P_, R)
+
+
+@pytest.mark.parametrize("seed", range(60))
+def test_random_configurations(seed):
+    x, p = random_config(500 + seed)
+    p = dataclasses.replace(p, allocator=GREEDY)
+    R, y_ref = run_case(x, p, f"greedy random config {500 + seed}")
+    if x.dtype == np.uint16:
+        tokens, hidden = x.shape
+        y16, _ = tah.roundtrip(to_dev(x), p, torch.bfloat16)
+        assert_decoded_equal(to_host(y16), oracle.decode(R, tokens, hidden, p, oracle.BF16), R,
+                             oracle.plan(tokens, hidden, p), f"greedy random config {500 + seed} bf16 out")
+
+
+def test_header_mismatch_sets_status():
+    """A top-p% payload decoded as greedy (and the reverse) is rejected on the device."""
+    x = synth.random_tensor(64, 512, synth.BF16, 9, n_out=3, mult=40)
+    p0 = P(tile=64, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0)
+    p1 = dataclasses.replace(p0, allocator=GREEDY)
+    for a, b in ((p0, p1), (p1, p0)):
+        Pa = tah.encode(to_dev(x), a)
+        buf = torch.zeros(max(Pa.numel(), tah.payload_bytes(64, 512, b)), dtype=torch.uint8, device="cuda")
+        buf[:Pa.numel()] = Pa
+        ws = tah.alloc_workspace(64, 512, b)
+        tah.decode(buf, 64, 512, b, torch.float32, ws=ws)
+        assert tah.read_device_status(ws) == 5
