@@ -157,9 +157,11 @@ struct HistArgs {
   int32_t has_prev;
 };
 
-// Large workgroups: fewer of them add into the same global bins.
+// Large workgroups, 4 keys per thread: 256 of them for a million keys fill the
+// chip (16 keys per thread left three quarters of it idle), and few enough add
+// into the same global bins.
 constexpr int kHistThreads = 1024;
-constexpr int kHistPerThread = 16;
+constexpr int kHistPerThread = 4;
 constexpr int kHistChunk = kHistThreads * kHistPerThread;
 
 // Apply one pass to a sample's state: one wavefront scans the pass's histogram

@@ -37,6 +37,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, AMD published figure
 WORKLOAD = "c5_8192x8192_bf16_g64"
 MIXED = "x2_c5_budget3p8"
+GREEDY = "x5b_c5_greedy"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "k_encode_c5_roundtrip_traffic.json")
 CSRC = os.path.join(ROOT, "activation_quantization_pipeline_amd", "csrc")
 
@@ -245,6 +246,17 @@ def main():
             extras[f"mixed_80_20_{label}_roundtrip_gbps"] = round((2 * x_bytes + ca.payload_bytes) / (a_ms * 1e-3) / 1e9,
                                                                  1)
             del pa, wsa
+        # the greedy allocator over every candidate width ({3, 4, 8} at 3.8 bits: some tiles
+        # take 8 bits where the 80/20 rule gives 4)
+        wg = synth.workload(GREEDY)
+        cgd = tah.Codec(T, C, wg.params, torch.bfloat16, torch.bfloat16)
+        pgd = [torch.empty(cgd.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+        wsgd = torch.empty(cgd.workspace_bytes, dtype=torch.uint8, device=dev)
+        gd_ms, _, _, _ = time_launches(torch, lambda i: cgd.roundtrip(xs[i], pgd[i], ys[i], wsgd, stream_h), n_sets,
+                                       args.steps, args.warmup)
+        extras["greedy_3_4_8_roundtrip_gbps"] = round((2 * x_bytes + cgd.payload_bytes) / (gd_ms * 1e-3) / 1e9, 1)
+        extras["greedy_3_4_8_ms_per_step"] = round(gd_ms, 5)
+        del pgd, wsgd
         # the outlier thresholds of App. F on the headline configuration (tau = 2 is the headline)
         taus = {"2.0": round(value, 1)}
         for tau in (0.0, 4.0, math.inf):
