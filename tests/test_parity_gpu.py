@@ -472,7 +472,7 @@ def test_random_configurations(seed):
 
 
 @pytest.mark.parametrize("name", ["c3_16384x4096_bf16_g64", "c4_16384x5120_f32_g128", "c5_8192x8192_bf16_g64",
-                                  "x2_c5_budget3p8"])
+                                  "x2_c5_budget3p8", "x5b_c5_greedy"])
 def test_full_size_other_seed(name):
     """The large workloads at full size with another seed: payload and fused
     round trip (the benchmarked launch for c5) against the oracle."""
