@@ -104,13 +104,19 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
       o->lam[j] = (float)log2(gain / (double)o->cost[j]);
     }
     o->ngpasses = 0;
+    o->ngidx = 0;
     if (o->glevel < 0) {
-      // composite = (32-bit key, ib bits of the complemented upgrade index), top digit first
+      // composite = (32-bit key, ib bits of the complemented upgrade index):
+      // three grid-wide digits of the key (11/11/10 bits), then the index
+      // digits, top first, inside one workgroup per sample
       o->ib = bit_width((uint64_t)(o->N * o->nl - 1));
       if (o->ib < 1) o->ib = 1;
-      for (int hi = 32 + o->ib; hi > 0; hi -= kDigitBits) {
+      o->gpasses[o->ngpasses++] = GPass{o->ib + 21, 11};
+      o->gpasses[o->ngpasses++] = GPass{o->ib + 10, 11};
+      o->gpasses[o->ngpasses++] = GPass{o->ib, 10};
+      for (int hi = o->ib; hi > 0; hi -= kDigitBits) {
         const int lo = hi - kDigitBits > 0 ? hi - kDigitBits : 0;
-        o->gpasses[o->ngpasses++] = GPass{lo, hi - lo};
+        o->gidx[o->ngidx++] = GPass{lo, hi - lo};
       }
     }
   }
@@ -158,10 +164,13 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   // per sample: a count, a pad word, then the (key, index) pairs whose key
   // matches the threshold's prefix after the second entropy pass (ties at the
   // threshold are broken among them)
-  o->ncand = o->N < kMaxCand ? o->N : kMaxCand;
+  // (greedy: the (key, upgrade index) pairs matching the prefix after the
+  // second key digit)
+  const int64_t nkeys = o->mode == 2 ? o->N * o->nl : o->N;
+  o->ncand = nkeys < kMaxCand ? nkeys : kMaxCand;
   o->cand_stride = 2 + 2 * o->ncand;
   o->ws_cand = w;
-  w = align256(w + 4 * o->cand_stride * (o->mode == 1 ? o->nsamples : 0));
+  w = align256(w + 4 * o->cand_stride * (sel ? o->nsamples : 0));
   o->ws_wtotal = w;  // greedy: the sum of all code widths (the used part of the code section)
   w = align256(w + (o->mode == 2 ? 4 : 0));
   o->ws_total = w;

@@ -11,15 +11,18 @@
 // u * nl + j; composites are unique and a larger one comes first. e* is the
 // composite where the running cost first exceeds R, found by a radix select
 // whose histograms add each upgrade's cost instead of 1:
-//   k_ghist  - one launch per digit (11 bits, top digit first, up to 6). Each
+//   k_ghist  - one launch per digit of the 32-bit key (11/11/10 bits). Each
 //              workgroup applies the previous digit (one wavefront scans that
 //              histogram of the sample, descending, and finds the bin where
 //              the running cost reaches r = remaining budget + 1), then adds
 //              the costs of the upgrades that match the prefix into a
-//              2048-bin LDS histogram and into the sample's global one.
-//              Histograms rotate over three buffers and states over two, so
-//              kernel boundaries are the only synchronisation;
-//   k_gfinal - applies the last digit: the composite of e* per sample;
+//              2048-bin LDS histogram and into the sample's global one. The
+//              last digit also lists the (key, index) pairs that match the
+//              22-bit prefix. Histograms rotate over three buffers and states
+//              over two, so kernel boundaries are the only synchronisation;
+//   k_gresolve - one workgroup per sample applies the last key digit, then
+//              finds e*'s index among the upgrades with e*'s key by digit
+//              passes over that list, ascending, in LDS: e*'s composite;
 //   k_glevel - one lane per quantization tile: its level is the count of its
 //              allocation tile's upgrades whose composite is above e*'s; the
 //              2-bit level map and the sum of the widths per 64 tiles;
@@ -56,18 +59,20 @@ __device__ __forceinline__ uint64_t composite(const GArgs& g, float h, int64_t u
   return ((uint64_t)key_bits(kappa) << g.ib) | (imax - idx);
 }
 
-// One wavefront: finds the digit of the pass whose bin holds cost position r
-// (1-based) in descending order of the sample's histogram h, then narrows the
-// state to it. r never exceeds the histogram's total: the host runs the
-// select only when R is below the cost of all upgrades.
-__device__ __forceinline__ GState apply_gpass(GState S, const uint32_t* h, const GPass& ps) {
+// One wavefront: finds the bin of histogram h that holds cost position r
+// (1-based), bins taken in descending order (DESC, composite digits) or
+// ascending (index digits); returns its digit and the cost before it. r never
+// exceeds the histogram's total: the host runs the select only when R is
+// below the cost of all upgrades.
+template <bool DESC>
+__device__ __forceinline__ void find_bin(const uint32_t* h, int64_t r, uint32_t& digit, int64_t& before_out) {
   const int lane = threadIdx.x & 63;
   constexpr int PER = kBins / 64;
   uint32_t c[PER];
   uint64_t sum = 0;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
-    c[i] = h[kBins - 1 - (lane * PER + i)];
+    c[i] = h[DESC ? kBins - 1 - (lane * PER + i) : lane * PER + i];
     sum += c[i];
   }
   uint64_t incl = sum;
@@ -77,9 +82,13 @@ __device__ __forceinline__ GState apply_gpass(GState S, const uint32_t* h, const
     if (lane >= off) incl += o;
   }
   const uint64_t excl = incl - sum;
-  const bool here = (int64_t)excl < S.r && S.r <= (int64_t)incl;
+  const bool here = (int64_t)excl < r && r <= (int64_t)incl;
   const uint64_t hm = ballot(here);
-  if (hm == 0) return S;
+  if (hm == 0) {  // cannot happen for 1 <= r <= total
+    digit = 0u;
+    before_out = 0;
+    return;
+  }
   const int src = __ffsll((unsigned long long)hm) - 1;
   int ord = 0;
   int64_t before = 0;
@@ -88,7 +97,7 @@ __device__ __forceinline__ GState apply_gpass(GState S, const uint32_t* h, const
     ord = lane * PER;
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      if (before + (int64_t)c[i] >= S.r) {
+      if (before + (int64_t)c[i] >= r) {
         ord = lane * PER + i;
         break;
       }
@@ -96,9 +105,17 @@ __device__ __forceinline__ GState apply_gpass(GState S, const uint32_t* h, const
     }
   }
   ord = __shfl(ord, src, 64);
-  before = (int64_t)__shfl((long long)before, src, 64);
+  before_out = (int64_t)__shfl((long long)before, src, 64);
+  digit = (uint32_t)(DESC ? kBins - 1 - ord : ord);
+}
+
+// Narrows a sample's state to the bin of a composite digit.
+__device__ __forceinline__ GState apply_gpass(GState S, const uint32_t* h, const GPass& ps) {
+  uint32_t digit;
+  int64_t before;
+  find_bin<true>(h, S.r, digit, before);
   S.r -= before;
-  S.prefix |= (uint64_t)(kBins - 1 - ord) << ps.shift;
+  S.prefix |= (uint64_t)digit << ps.shift;
   return S;
 }
 
@@ -110,9 +127,10 @@ struct GHistArgs {
   const uint32_t* hist_prev;  // previous pass's histograms
   uint32_t* hist_cur;         // this pass's histograms (zero on entry)
   uint32_t* hist_clear;       // the next pass's histograms, cleared here
-  int64_t chunks_per_sample, R;
+  uint32_t* cand;  // per sample: count, pad, then up to ncand (key, index) pairs
+  int64_t chunks_per_sample, R, ncand, cand_stride;
   GPass pass, prev;
-  int32_t has_prev, tb;  // tb: composite bits, 32 + ib
+  int32_t has_prev, last_key;  // last_key: the last of the three key digits
 };
 
 // 4 tiles per thread: 256 workgroups for a million tiles fill the chip (16 per
@@ -125,6 +143,8 @@ constexpr int kGChunk = kGThreads * kGPerThread;  // allocation tiles per workgr
 __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
   __shared__ uint32_t lh[kBins];
   __shared__ GState ss;
+  __shared__ uint2 lc[kCandPerChunk];  // candidates of the last key digit
+  __shared__ uint32_t lcn, lbase;
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t s = blockIdx.x / a.chunks_per_sample;
   const int64_t c = blockIdx.x % a.chunks_per_sample;
@@ -135,6 +155,7 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
     for (int64_t i = b0 + tid; i < b1; i += kGThreads) a.hist_clear[s * kBins + i] = 0u;
   }
   for (int i = tid; i < kBins; i += kGThreads) lh[i] = 0u;
+  if (tid == 0) lcn = 0u;
   if (tid < 64) {
     GState S;
     if (a.has_prev) {
@@ -146,6 +167,7 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
     if (tid == 0) {
       ss = S;
       if (c == 0) a.st_cur[s] = S;
+      if (c == 0 && !a.has_prev) a.cand[s * a.cand_stride] = 0u;  // appended to by the last key digit
     }
   }
   __syncthreads();
@@ -166,10 +188,26 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
       const int64_t u = u0 + i * kGThreads + tid;
       bool want = false;
       uint32_t digit = 0;
+      uint64_t C = 0;
       if (u < a.g.N) {
-        const uint64_t C = composite(a.g, hv[i], u, j);
+        C = composite(a.g, hv[i], u, j);
         want = hs >= 64 || (C >> hs) == want_hi;
         digit = (uint32_t)((C >> a.pass.shift) & dmask);
+      }
+      if (a.last_key) {
+        // upgrades whose key matches the prefix, a superset of the ties at
+        // e*'s key, into this workgroup's LDS list (appended to the sample's
+        // list at the end): (key, index)
+        const uint64_t wm = ballot(want);
+        if (wm != 0) {
+          const int leader = __ffsll((unsigned long long)wm) - 1;
+          uint32_t base = 0;
+          if (lane == leader) base = atomicAdd(&lcn, (uint32_t)__popcll(wm));
+          base = (uint32_t)__shfl((int)base, leader, 64);
+          const uint32_t pos = base + lanes_below(wm);
+          if (want && pos < (uint32_t)kCandPerChunk)
+            lc[pos] = make_uint2((uint32_t)(C >> a.g.ib), (uint32_t)((uint64_t)u * (uint64_t)a.g.nl + (uint64_t)j));
+        }
       }
       // lanes with the same digit as the first remaining lane add together
       // (twice), the rest one by one
@@ -190,14 +228,106 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
   __syncthreads();
   for (int i = tid; i < kBins; i += kGThreads)
     if (lh[i]) atomicAdd(&a.hist_cur[s * kBins + i], lh[i]);
+  if (a.last_key) {
+    // one reservation in the sample's list per workgroup; a count above the
+    // list's capacity (or a workgroup past kCandPerChunk) marks it overflowed
+    const uint32_t n = lcn;
+    if (n != 0) {
+      uint32_t* cl = a.cand + s * a.cand_stride;
+      if (tid == 0) lbase = atomicAdd(cl, n > (uint32_t)kCandPerChunk ? (uint32_t)(a.ncand + 1) : n);
+      __syncthreads();
+      const uint32_t base = lbase;
+      for (uint32_t i = tid; i < n && i < (uint32_t)kCandPerChunk; i += kGThreads)
+        if ((int64_t)(base + i) < a.ncand) reinterpret_cast<uint2*>(cl + 2)[base + i] = lc[i];
+    }
+  }
 }
 
-// One wavefront per sample: the last digit, which completes e*'s composite.
-__global__ __launch_bounds__(64) void k_gfinal(const GState* st_prev, const uint32_t* hist_last, GState* st_out,
-                                               GPass last) {
+// One workgroup per sample: applies the last key digit, which fixes e*'s key
+// K and the cost position r still to place among the upgrades with key K;
+// then e*'s upgrade index (the lowest index first among equal keys) by
+// cost-weighted digit passes over an LDS histogram, ascending. The passes run
+// over the (key, index) pairs the last key digit listed (those matching the
+// 22-bit key prefix, usually a few thousand at most); only when that list
+// overflowed does this workgroup go through every upgrade of the sample.
+struct GResolveArgs {
+  GArgs g;
+  const GState* st_prev;
+  GState* st_out;
+  const uint32_t* hist_last;
+  const uint32_t* cand;
+  int64_t ncand, cand_stride;
+  GPass last;
+  int32_t nidx;
+  GPass idx[3];  // digits of the upgrade index, top first
+};
+
+constexpr int kGResolveThreads = 1024;
+
+__global__ __launch_bounds__(kGResolveThreads) void k_gresolve(GResolveArgs a) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ GState ss;
+  __shared__ uint32_t ipre_s;
+  __shared__ uint2 lk[kMaxCand];
+  const int tid = threadIdx.x;
   const int64_t s = blockIdx.x;
-  const GState S = apply_gpass(st_prev[s], hist_last + s * kBins, last);
-  if (threadIdx.x == 0) st_out[s] = S;
+  if (tid < 64) {
+    const GState S = apply_gpass(a.st_prev[s], a.hist_last + s * kBins, a.last);
+    if (tid == 0) {
+      ss = S;
+      ipre_s = 0u;
+    }
+  }
+  __syncthreads();
+  const GState S = ss;
+  const uint32_t K = (uint32_t)(S.prefix >> a.g.ib);
+  int64_t r = S.r;
+  const uint32_t* cl = a.cand + s * a.cand_stride;
+  const int64_t nc = cl[0];
+  const bool listed = nc <= a.ncand;  // else go through every upgrade of the sample
+  const int64_t n = listed ? nc : a.g.N * a.g.nl;
+  if (listed) {
+    for (int64_t i = tid; i < nc; i += kGResolveThreads) lk[i] = reinterpret_cast<const uint2*>(cl + 2)[i];
+  }
+  __syncthreads();
+  const float* h = a.g.H + s * a.g.N;
+  for (int p = 0; p < a.nidx; ++p) {
+    const GPass ps = a.idx[p];
+    for (int i = tid; i < kBins; i += kGResolveThreads) lh[i] = 0u;
+    __syncthreads();
+    const uint32_t ipre = ipre_s;
+    const int hs = ps.shift + ps.width;  // index bits above the current digit
+    const uint32_t dmask = (1u << ps.width) - 1u;
+    for (int64_t i = tid; i < n; i += kGResolveThreads) {
+      uint32_t key, idx;
+      if (listed) {
+        key = lk[i].x;
+        idx = lk[i].y;
+      } else {
+        const int64_t u = i / a.g.nl;
+        const int j = (int)(i - u * a.g.nl);
+        key = (uint32_t)(composite(a.g, h[u], u, j) >> a.g.ib);
+        idx = (uint32_t)i;
+      }
+      if (key == K && (hs >= 32 || (idx >> hs) == (ipre >> hs)))
+        atomicAdd(&lh[(idx >> ps.shift) & dmask], (uint32_t)a.g.cost[idx % (uint32_t)a.g.nl]);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t digit;
+      int64_t before;
+      find_bin<false>(lh, r, digit, before);
+      if (tid == 0) ipre_s = ipre | (digit << ps.shift);
+      r -= before;  // only wavefront 0's r is used
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    GState T;
+    T.prefix = ((uint64_t)K << a.g.ib) | (((1ull << a.g.ib) - 1ull) - (uint64_t)ipre_s);
+    T.r = r;
+    a.st_out[s] = T;
+  }
 }
 
 // ------------------------------------------------------------------ levels ----
@@ -261,14 +391,17 @@ hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st
     const int64_t hsz = ns * kBins;
     GHistArgs h;
     h.g = g;
+    h.cand = reinterpret_cast<uint32_t*>(w + pl.ws_cand);
     h.chunks_per_sample = (pl.N + kGChunk - 1) / kGChunk;
     h.R = pl.R;
-    h.tb = 32 + pl.ib;
+    h.ncand = pl.ncand;
+    h.cand_stride = pl.cand_stride;
     const int np = pl.ngpasses;
-    // pass p: state p in states[p % 2], histogram p in hists[p % 3] (zeroed
-    // by k_stats for p = 0)
+    // key digit p: state p in states[p % 2], histogram p in hists[p % 3]
+    // (zeroed by k_stats for p = 0)
     for (int p = 0; p < np; ++p) {
       h.pass = pl.gpasses[p];
+      h.last_key = p == np - 1;
       h.has_prev = p > 0;
       h.prev = p > 0 ? pl.gpasses[p - 1] : pl.gpasses[p];
       h.st_prev = states + ((p + 1) % 2) * ns;
@@ -281,8 +414,18 @@ hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st
       if (e != hipSuccess) return e;
     }
     final_st = states + (np % 2) * ns;
-    hipLaunchKernelGGL(k_gfinal, dim3((unsigned)ns), dim3(64), 0, st, (const GState*)(states + ((np + 1) % 2) * ns),
-                       (const uint32_t*)(hists + ((np + 2) % 3) * hsz), final_st, pl.gpasses[np - 1]);
+    GResolveArgs rs;
+    rs.g = g;
+    rs.st_prev = states + ((np + 1) % 2) * ns;
+    rs.st_out = final_st;
+    rs.hist_last = hists + ((np + 2) % 3) * hsz;
+    rs.cand = h.cand;
+    rs.ncand = pl.ncand;
+    rs.cand_stride = pl.cand_stride;
+    rs.last = pl.gpasses[np - 1];
+    rs.nidx = pl.ngidx;
+    for (int i = 0; i < 3; ++i) rs.idx[i] = pl.gidx[i];
+    hipLaunchKernelGGL(k_gresolve, dim3((unsigned)ns), dim3(kGResolveThreads), 0, st, rs);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -45,10 +45,11 @@ struct Plan {
   // constants lam and costs cost; the select runs over composites of 32 key
   // bits and ib index bits unless every tile takes the same level (glevel >= 0)
   int64_t R;
-  int32_t nl, ib, glevel, ngpasses;
+  int32_t nl, ib, glevel, ngpasses, ngidx;
   float lam[3];
   int32_t cost[3];
-  GPass gpasses[kMaxPasses];
+  GPass gpasses[kMaxPasses];  // the three digits of the 32-bit key
+  GPass gidx[3];              // the digits of the upgrade index (inside one workgroup per sample)
   int32_t x_dtype;
   float tau, budget;
   int32_t n_candidates;
