@@ -3,8 +3,10 @@ no allocation inside the library: every call is a sequence of kernel
 launches on the caller's stream), through the C ABI.
 
 A captured mixed-allocation round trip (entropy pass, three select passes,
-tie resolution, width map, block table, encoder: ten kernels) and a captured
-decode are replayed several times, with eager work on the same buffers
+tie resolution, width map, block table, encoder: ten kernels; with the greedy
+allocator, five cost-weighted select passes, the final digit, the level map,
+the block table and the encoder) and a captured decode are replayed several
+times, with eager work on the same buffers
 between the replays, and every replay must reproduce the eager results bit for
 bit.
 """
@@ -24,8 +26,11 @@ def say(*a):
     print(*a, flush=True)
 
 
-def test_captured_round_trip_and_decode_replay_like_eager():
-    name = "c2_4096x2048_bf16_g64"  # 80/20-style mixed allocation at budget 3.5 over {2,3,4,8}
+@pytest.mark.parametrize("name", [
+    "c2_4096x2048_bf16_g64",  # top-p mixed allocation at budget 3.5 over {2,3,4,8}
+    "x5a_c2_greedy",          # the greedy allocator: cost-weighted select passes, level map, width sums
+])
+def test_captured_round_trip_and_decode_replay_like_eager(name):
     w = synth.workload(name)
     p = w.params
     T, C = w.tokens, w.hidden

@@ -116,3 +116,18 @@ def test_header_mismatch_sets_status():
         ws = tah.alloc_workspace(64, 512, b)
         tah.decode(buf, 64, 512, b, torch.float32, ws=ws)
         assert tah.read_device_status(ws) == 5
+
+
+@pytest.mark.parametrize("tile,budget,cands", [(64, 3.3, (2, 3, 4, 8)), (32, 2.7, (1, 2, 4)), (128, 4.6, (3, 4, 8))])
+def test_ties_resolved_from_the_list(tile, budget, cands):
+    """Eight distinct rows repeated: 8 distinct entropies, each shared by many
+    tiles, so e*'s key is tied across tiles but few keys match its prefix: the
+    tie is broken from the listed (key, index) pairs, not by the whole-sample
+    scan."""
+    rows = synth.random_tensor(8, tile * 3, synth.F32, tile, n_out=1, mult=20)
+    order = np.random.default_rng(tile).integers(0, 8, size=200)
+    x = np.ascontiguousarray(rows[order]).astype(np.float32)
+    p = P(tile=tile, tokens_per_sample=0, bit_budget=budget, candidates=cands, tau=2.0, allocator=GREEDY)
+    R, _ = run_case(x, p, f"listed ties tile {tile}")
+    pl = oracle.plan(200, tile * 3, p)
+    assert len(levels_used(R, pl)) >= 2
