@@ -397,6 +397,25 @@ __device__ __forceinline__ void lds_write_part(uint8_t* row, int r, const float 
   }
 }
 
+// Streaming accesses with the nontemporal hint: the tensor read by the encoder
+// and the tensor written by the encoder and decoder are touched once per call.
+// Measured on the 8192 x 8192 bf16 round trip: 67.2 -> 61.0 us, decode
+// 39.0 -> 29.5 us. Not used for the statistics pass's reads (the encoder reads
+// the same tensor right after it, from the cache) nor for the payload.
+typedef uint32_t nt_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 load_stream(const uint4* p) {
+  const nt_u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_stream(uint4* p, const uint4 q) {
+  nt_u32x4 v;
+  v.x = q.x;
+  v.y = q.y;
+  v.z = q.z;
+  v.w = q.w;
+  __builtin_nontemporal_store(v, reinterpret_cast<nt_u32x4*>(p));
+}
+
 // A group of NT consecutive tiles held in registers on its way to LDS: thread
 // i owns the 16-byte chunks i, i + NT, i + 2 NT, ... of the group, so every
 // load instruction of the workgroup reads one contiguous, coalesced block.
@@ -413,7 +432,7 @@ __device__ __forceinline__ void group_load(const uint8_t* __restrict__ src, int 
   // past the end reloads the last one, which group_to_lds never stores.
   const int last = n_tiles * R::kChunks - 1;
 #pragma unroll
-  for (int i = 0; i < R::kChunks; ++i) r.c[i] = s[min((int)threadIdx.x + i * NT, last)];
+  for (int i = 0; i < R::kChunks; ++i) r.c[i] = load_stream(&s[min((int)threadIdx.x + i * NT, last)]);
 }
 
 // Makes the compiler wait for the loads of r here (an empty asm that reads them).
@@ -475,7 +494,7 @@ __device__ __forceinline__ void stage_out(const uint8_t* lds, uint8_t* __restric
   for (int i = 0; i < R::kChunks; ++i) buf[i] = *reinterpret_cast<const uint4*>(base + i * (NT / R::kChunks) * R::kStride);
 #pragma unroll
   for (int i = 0; i < R::kChunks; ++i) {
-    if (n_tiles == NT || (int)threadIdx.x + i * NT < nchunks) d[i * NT] = buf[i];
+    if (n_tiles == NT || (int)threadIdx.x + i * NT < nchunks) store_stream(&d[i * NT], buf[i]);
   }
 }
 
