@@ -11,7 +11,8 @@
 //              (a bit of the width map, or a 2-bit level of the greedy one).
 //              It fixes the tile's code-block offset (§3.4 packing order);
 //  3. forward: a flagged tile gets the pivot swap P_d in its own LDS row and
-//              the Hadamard transform of Eq. (4) in the lane's registers;
+//              the Hadamard transform of Eq. (4) in the lane's registers (in
+//              the encode-only kernel, by 16-lane groups through LDS slots);
 //  4. quantize: every lane quantizes its (transformed or not) tile
 //              asymmetrically (§3.3), packs the codes and stores code block,
 //              scale and zero-point; the fused variant dequantizes from the
@@ -229,11 +230,12 @@ __device__ __forceinline__ void quantize_tile(const EncArgs& a, float (&v)[G], i
 // group g of 64 tiles goes to workgroup g mod gridDim.x. Groups of small tiles
 // are prefetched into registers while the current group is processed.
 //
-// A flagged tile (Eq. 3) is transformed by its own lane with fwht<G>, the
-// stage order of the oracle. The wavefront runs the butterflies whenever one
-// of its 64 tiles is flagged; measured on the 8192x8192 round trip this beats
-// handing the flagged tiles to 16-lane groups through LDS (barriers and
-// round trips per group) at every tau, from 0 (every tile) to 4.
+// In the round trip a flagged tile (Eq. 3) is transformed by its own lane
+// with fwht<G>, the stage order of the oracle. The wavefront runs the
+// butterflies whenever one of its 64 tiles is flagged; measured on the
+// 8192x8192 round trip this beats handing the flagged tiles to 16-lane groups
+// through LDS (barriers and round trips per group), forward and inverse or
+// forward alone. The encode-only kernel does hand them over (see kCoopH).
 template <int G, typename TIn, int OUT, int MODE>
 __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncArgs a) {
   constexpr int NT = 64;
