@@ -90,7 +90,7 @@ __device__ __forceinline__ void naive_stage_in(const uint8_t* src, int64_t ne, u
     uint4 q = make_uint4(0u, 0u, 0u, 0u);
     const int64_t off = (int64_t)c * 16;
     if (off + 16 <= bytes) {
-      q = *reinterpret_cast<const uint4*>(src + off);
+      q = load_stream(reinterpret_cast<const uint4*>(src + off));  // streamed once: nontemporal
     } else if (c < nchunks) {
       uint32_t wv[4] = {0u, 0u, 0u, 0u};
       for (int64_t b = off; b < bytes; b += EB) {  // the tail chunk, element by element
@@ -115,7 +115,7 @@ __device__ __forceinline__ void naive_stage_out(const uint8_t* rows, uint8_t* ds
     const uint4 q = *reinterpret_cast<const uint4*>(rows + (c / kChunks) * kStride + (c % kChunks) * 16);
     const int64_t off = (int64_t)c * 16;
     if (off + 16 <= bytes) {
-      *reinterpret_cast<uint4*>(dst + off) = q;
+      store_stream(reinterpret_cast<uint4*>(dst + off), q);  // streamed once: nontemporal
     } else {
       const uint32_t wv[4] = {q.x, q.y, q.z, q.w};
       for (int64_t b = off; b < bytes; b += EB) {  // the tail chunk, element by element
