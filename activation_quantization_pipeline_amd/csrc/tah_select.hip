@@ -31,6 +31,8 @@
 //              selected tie; per-64-tile counts;
 //   k_table  - exclusive scan of those counts: b_hi tiles before each run of
 //              64 tiles, which locates every variable-width code block.
+// Samples of at most kSmallSelect keys skip k_hist and k_resolve: one
+// workgroup per sample (k_select_small) runs every digit pass in LDS.
 #include <type_traits>
 
 #include "tah_device.hpp"
@@ -401,6 +403,89 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
   if (tid == 0) a.st_out[s] = S;
 }
 
+// Small samples (N <= kSmallSelect keys): one workgroup per sample runs every
+// digit pass of the select, the three key digits and, when the threshold key
+// is shared by more tiles than remain to be selected, the tile-index digits,
+// over the sample's keys with an LDS histogram (lanes sharing a digit add
+// once), instead of one grid-wide launch per digit and k_resolve: the same
+// passes and apply_pass, so the same final state. The limit is one histogram
+// chunk, where the grid-wide passes also run one workgroup per sample; above
+// it they spread a sample over more workgroups, which pays for the launches
+// (at 32768 keys per sample and 4 samples this kernel took the 4096 x 2048
+// round trip from 47.8 to 78.2 us).
+constexpr int64_t kSmallSelect = kHistChunk;
+constexpr int kSmallThreads = 1024;
+
+struct SmallSelectArgs {
+  const float* H;
+  SampleState* st_out;
+  int64_t N, k;
+  int32_t npasses;
+  SelectPass passes[kMaxPasses];
+};
+
+__global__ __launch_bounds__(kSmallThreads) void k_select_small(SmallSelectArgs a) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ SampleState ss;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t s = blockIdx.x;
+  const float* h = a.H + s * a.N;
+  if (tid == 0) {
+    SampleState S;
+    S.key = 0u;
+    S.upos = 0u;
+    S.r = a.k;
+    S.tie_all = 0;
+    S.pad = 0;
+    ss = S;
+  }
+  for (int p = 0; p < a.npasses; ++p) {
+    const SelectPass ps = a.passes[p];
+    for (int i = tid; i < kBins; i += kSmallThreads) lh[i] = 0u;
+    __syncthreads();
+    const SampleState S = ss;
+    if (ps.kind == 1 && S.tie_all) break;  // every tile with the threshold key is selected
+    const int hs = ps.shift + ps.width;  // bits above the current digit
+    const uint32_t dmask = (1u << ps.width) - 1u;
+    for (int64_t i0 = 0; i0 < a.N; i0 += kSmallThreads) {  // uniform trip count: ballots need every lane
+      const int64_t i = i0 + tid;
+      bool want = false;
+      uint32_t digit = 0;
+      if (i < a.N) {
+        const uint32_t key = orderable(h[i]);
+        if (ps.kind == 0) {
+          want = hs >= 32 || (key >> hs) == (S.key >> hs);
+          digit = (key >> ps.shift) & dmask;
+        } else {
+          const uint32_t u = (uint32_t)i;
+          want = key == S.key && (hs >= 32 || (u >> hs) == (S.upos >> hs));
+          digit = (u >> ps.shift) & dmask;
+        }
+      }
+#pragma unroll
+      for (int round = 0; round < 2; ++round) {
+        const uint64_t wm = ballot(want);
+        if (wm == 0) break;
+        const int leader = __ffsll((unsigned long long)wm) - 1;
+        const uint32_t d0 = (uint32_t)__shfl((int)digit, leader, 64);
+        const bool same = want && digit == d0;
+        const uint64_t sm = ballot(same);
+        if (lane == leader) atomicAdd(&lh[d0], (uint32_t)__popcll(sm));
+        want = want && !same;
+      }
+      if (want) atomicAdd(&lh[digit], 1u);
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const SampleState T = apply_pass(S, lh, ps);
+      if (tid == 0) ss = T;
+    }
+    __syncthreads();
+  }
+  __syncthreads();
+  if (tid == 0) a.st_out[s] = ss;
+}
+
 // ------------------------------------------------------------------ mark ----
 struct MarkArgs {
   const float* H;  // per allocation tile
@@ -497,10 +582,41 @@ hipError_t launch_table(const uint32_t* cnt, uint32_t* table, uint32_t* total, i
   return hipGetLastError();
 }
 
+// Width map and per-64-tile counts from the final states, then the block table.
+static hipError_t mark_and_table(const Plan& pl, uint8_t* P, uint8_t* w, const SampleState* st_final, hipStream_t st) {
+  MarkArgs m;
+  m.H = reinterpret_cast<const float*>(w + pl.ws_H);
+  m.st = st_final;
+  m.bitmap = reinterpret_cast<uint32_t*>(P ? P + pl.off_bitmap : w + pl.ws_bitmap);
+  m.blockcnt = reinterpret_cast<uint32_t*>(w + pl.ws_blockcnt);
+  m.tiles = pl.tiles;
+  m.N = pl.N;
+  m.nblocks = pl.nblocks;
+  m.kA = pl.kA;
+  hipLaunchKernelGGL(k_mark, dim3((unsigned)((pl.tiles + 255) / 256)), dim3(256), 0, st, m);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  uint32_t* table = reinterpret_cast<uint32_t*>(P ? P + pl.off_table : w + pl.ws_table);
+  return launch_table(m.blockcnt, table, nullptr, pl.nblocks, st);
+}
+
 hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st) {
   uint8_t* w = static_cast<uint8_t*>(ws);
   uint8_t* P = static_cast<uint8_t*>(payload);
   SampleState* states = reinterpret_cast<SampleState*>(w + pl.ws_state);
+  if (pl.N <= kSmallSelect) {
+    SmallSelectArgs sa;
+    sa.H = reinterpret_cast<const float*>(w + pl.ws_H);
+    sa.st_out = states;
+    sa.N = pl.N;
+    sa.k = pl.k;
+    sa.npasses = pl.npasses;
+    for (int i = 0; i < kMaxPasses; ++i) sa.passes[i] = pl.passes[i];
+    hipLaunchKernelGGL(k_select_small, dim3((unsigned)pl.nsamples), dim3(kSmallThreads), 0, st, sa);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return mark_and_table(pl, P, w, states, st);
+  }
   uint32_t* hists = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
   const int64_t hsz = pl.nsamples * kBins;
   HistArgs h;
@@ -547,20 +663,7 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   hipLaunchKernelGGL(k_resolve, dim3((unsigned)pl.nsamples), dim3(kResolveThreads), 0, st, rs);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  MarkArgs m;
-  m.H = h.H;
-  m.st = rs.st_out;
-  m.bitmap = reinterpret_cast<uint32_t*>(P ? P + pl.off_bitmap : w + pl.ws_bitmap);
-  m.blockcnt = reinterpret_cast<uint32_t*>(w + pl.ws_blockcnt);
-  m.tiles = pl.tiles;
-  m.N = pl.N;
-  m.nblocks = pl.nblocks;
-  m.kA = pl.kA;
-  hipLaunchKernelGGL(k_mark, dim3((unsigned)((pl.tiles + 255) / 256)), dim3(256), 0, st, m);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  uint32_t* table = reinterpret_cast<uint32_t*>(P ? P + pl.off_table : w + pl.ws_table);
-  return launch_table(m.blockcnt, table, nullptr, pl.nblocks, st);
+  return mark_and_table(pl, P, w, rs.st_out, st);
 }
 
 }  // namespace tah

@@ -487,3 +487,37 @@ def test_full_size_other_seed(name):
     y, P = tah.roundtrip(to_dev(x), w.params, y_dt)
     assert_payload_equal(to_host(P), R, pl, f"{name} seed 1")
     assert_decoded_equal(to_host(y), y_ref, R, pl, f"{name} seed 1")
+
+
+@pytest.mark.parametrize("n_tied", [200, 6000])
+def test_threshold_inside_a_tie_in_a_large_sample(n_tied):
+    """One sample of 163840 tiles, above the size that one workgroup selects
+    alone, so the select runs grid-wide (40 histogram workgroups, then the tie
+    step): half the tiles flat (above), n_tied copies of one tile spread over
+    the sample, the rest spiky (below); k = 81920 lands inside the tied class.
+    With 200 tied tiles the tie is broken from the listed candidates; with
+    6000 the list overflows and the whole sample is scanned."""
+    rng = np.random.default_rng(31 + n_tied)
+    T, H, G = 2560, 4096, 64
+    n = T * H // G
+    n_flat = 81920 - n_tied // 2
+    kind = np.full(n, 2)
+    idx = rng.permutation(n)
+    kind[idx[:n_flat]] = 0
+    kind[idx[n_flat:n_flat + n_tied]] = 1
+    flat = rng.uniform(0.9, 1.1, (n, G)) * rng.choice([-1, 1], (n, G))
+    spiky = rng.standard_normal((n, G)) * 0.01
+    spiky[np.arange(n), rng.integers(G, size=n)] = 5.0
+    tied = np.where(np.arange(G) % 2 == 0, 1.0, 0.0) * np.linspace(0.5, 1.5, G)
+    tiles = np.where((kind == 0)[:, None], flat, np.where((kind == 1)[:, None], tied[None, :], spiky))
+    x = tiles.reshape(T, H).astype(np.float32)
+    p = P(tile=G, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0)
+    pl = oracle.plan(T, H, p)
+    assert pl["k"] == 81920 and pl["tiles_per_sample"] > 131072
+    R, _ = run_case(x, p, f"tie in a large sample, {n_tied} tied")
+    bm = R[pl["off_bitmap"]:pl["off_bitmap"] + 8 * pl["nblocks"]].view(np.uint64)
+    hi = np.unpackbits(bm.view(np.uint8), bitorder="little")[:n].astype(bool)
+    tied_idx = np.flatnonzero(kind == 1)
+    n_sel = 81920 - n_flat
+    assert hi[kind == 0].all() and not hi[kind == 2].any()
+    assert hi[tied_idx[:n_sel]].all() and not hi[tied_idx[n_sel:]].any()
