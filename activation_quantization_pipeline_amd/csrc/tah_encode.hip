@@ -51,7 +51,7 @@ constexpr int tiles_per_wg() {
 // Minimum waves per SIMD the register allocator must leave room for.
 template <int G, typename T, int OUT>
 constexpr int kMinWaves() {
-  return (G <= 64 && OUT != 0 && Elem<T>::kBytes == 2) ? 3 : (G <= 64 ? 2 : 1);
+  return (G <= 64 && Elem<T>::kBytes == 2) ? 3 : (G <= 64 ? 2 : 1);
 }
 
 template <int G, int B>
@@ -98,24 +98,17 @@ __device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
 // bf16 tiles: the magnitude bits and (G-1-k) share one 32-bit key (bf16
 // leaves the low 16 bits free), so max/median on unsigned keys give the top
 // two magnitudes, the lowest index among ties, and no float compares.
-// FUSED (bf16 only): the entropy's sum S = sum |a_k| log2 |a_k| (left to
-// right) is taken in the same pass, its table reads issued with the keys of
-// 8 elements and consumed while the next 8 are in flight. That hides the LDS
-// latency but keeps more registers live, so only the kernels with registers
-// to spare (encode without reconstruction) use it.
-template <int G, typename TIn, bool FUSED>
+template <int G, typename TIn>
 __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], float& m1, float& m2, int& d,
-                                           float& l1, float& S, const float* lt) {
+                                           float& l1) {
   if constexpr (Elem<TIn>::kBytes == 2) {
     const uint4* p = reinterpret_cast<const uint4*>(row);
     uint32_t k1 = 0u, k2 = 0u;
-    float s = 0.0f, acc = 0.0f;
-    float lgp[8];
+    float s = 0.0f;
 #pragma unroll
     for (int c = 0; c < G / 8; ++c) {
       const uint4 q = p[c];
       const uint32_t u[4] = {q.x, q.y, q.z, q.w};
-      float lgc[8];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int k = 8 * c + 2 * i;
@@ -129,10 +122,6 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
         const uint32_t kh = (u[i] & 0x7fff0000u) | (uint32_t)(G - 2 - k);
         v[k] = __uint_as_float(xl);
         v[k + 1] = __uint_as_float(xh);
-        if constexpr (FUSED) {
-          lgc[2 * i] = log2_node(v[k], lt);
-          lgc[2 * i + 1] = log2_node(v[k + 1], lt);
-        }
         s = s + fabsf(v[k]);
         k2 = umed3(k2, kl, k1);
         k1 = max(k1, kl);
@@ -140,24 +129,11 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
         k2 = umed3(k2, kh, k1);
         k1 = max(k1, kh);
       }
-      if constexpr (FUSED) {
-        if (c > 0) {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(fabsf(v[8 * (c - 1) + i]), lgp[i], acc);
-        }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) lgp[i] = lgc[i];
-      }
-    }
-    if constexpr (FUSED) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc = __builtin_fmaf(fabsf(v[G - 8 + i]), lgp[i], acc);
     }
     m1 = __uint_as_float(k1 & 0xffff0000u);
     m2 = __uint_as_float(k2 & 0xffff0000u);
     d = G - 1 - (int)(k1 & 0xffffu);
     l1 = s;
-    S = acc;
   } else {
     lds_read_tile<G, TIn>(row, v);
     float a1 = fabsf(v[0]), a2 = 0.0f, s = 0.0f + fabsf(v[0]);
@@ -175,7 +151,6 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
     m2 = a2;
     d = dd;
     l1 = s;
-    S = 0.0f;
   }
 }
 
@@ -243,7 +218,10 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
   using RI = TileRow<G, TIn>;
   using TOut = typename std::conditional<OUT == 1, float, bf16_t>::type;
   using RO = TileRow<G, TOut>;
-  constexpr bool kPrefetch = RI::kChunks <= 8;
+  // The next group is prefetched into registers in the round trip; the
+  // encode-only kernel leaves those 32 registers to its three waves per SIMD
+  // (41.4 us against 44.4 us at two waves with the prefetch).
+  constexpr bool kPrefetch = RI::kChunks <= 8 && OUT != 0;
   // Each LDS row is read and rewritten only by its own lane, so a rebuilt tile
   // goes back into its own row when rows have the same width; otherwise
   // rebuilt tiles get rows of their own.
@@ -326,16 +304,13 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
     int flag = 0, piv = 0, hi = 0, bw = 0;
     float v[G];
     if (act) {
-      float m1, m2, l1, S;
+      float m1, m2, l1;
       int d;
-      constexpr bool kFused = !MIXED && OUT == 0 && Elem<TIn>::kBytes == 2;
-      tile_stats<G, TIn, kFused>(xs + lane * RI::kStride, v, m1, m2, d, l1, S, lt);
+      tile_stats<G, TIn>(xs + lane * RI::kStride, v, m1, m2, d, l1);
       flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
       piv = d;
       if constexpr (!MIXED) {
-        // Eq. (1)-(2)
-        if constexpr (kFused) a.H[t] = entropy_from_sums(l1, S, lt);
-        else a.H[t] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);
+        a.H[t] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);  // Eq. (1)-(2)
       } else if constexpr (MODE == 1) {
         hi = (a.bitmap[t >> 5] >> (t & 31)) & 1u;
       } else {
