@@ -3,7 +3,8 @@
 // A workgroup is one wavefront; it takes groups of 64 consecutive tiles, one
 // tile per lane:
 //  1. stage:   the 64 tiles (contiguous in HBM) arrive with 16-byte coalesced
-//              loads (prefetched one group ahead) and go into padded LDS rows;
+//              loads (in the round trip prefetched one group ahead) and go into
+//              padded LDS rows;
 //  2. phase A: lane i reads tile i from LDS and computes the outlier ratio of
 //              Eq. (3) (top-2 magnitudes, pivot d, flag) and, for a uniform
 //              allocation, the tile entropy of Eq. (1)-(2); with a mixed
@@ -202,8 +203,9 @@ __device__ __forceinline__ void quantize_tile(const EncArgs& a, float (&v)[G], i
 // widths from the 1-bit width map and the count table, 2 any candidate from
 // the 2-bit level map and the width-sum table.
 // A workgroup is one wavefront with LDS rows of its own, and it is persistent:
-// group g of 64 tiles goes to workgroup g mod gridDim.x. Groups of small tiles
-// are prefetched into registers while the current group is processed.
+// group g of 64 tiles goes to workgroup g mod gridDim.x. In the round trip,
+// groups of small tiles are prefetched into registers while the current group
+// is processed.
 //
 // In the round trip a flagged tile (Eq. 3) is transformed by its own lane
 // with fwht<G>, the stage order of the oracle. The wavefront runs the
