@@ -134,7 +134,7 @@ def main():
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py: the TAH-Quant codec is a per-stage, single-GPU kernel; this build measures one GPU only "
+        print("bench.py: the TAH-Quant codec is a per-stage, single-GPU kernel; it measures one GPU only "
               "and does not run with --gpus > 1", file=sys.stderr)
         sys.exit(2)
 

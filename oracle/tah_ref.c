@@ -16,8 +16,8 @@
  * "Training Transformers with 4-bit Integers" (arXiv 2306.11987), and the
  * low-nibble-first code order follows that paper's INT4 packing appendix.
  *
- * Readings where the pages leave a step open are listed in the design doc; the ones
- * that change numbers are restated next to the code below.
+ * Where the pages leave a step open, the reading taken is stated next to the
+ * code that implements it below.
  *
  * Build: gcc -O2 -std=c11 -ffp-contract=off -fPIC -shared (no fast-math), so
  * every fp32 operation rounds exactly once, in the order written.

@@ -1,6 +1,6 @@
 """GPU-vs-oracle parity of the TAH-Quant HIP path, through the C ABI.
 
-Bar (BASELINE the benchmark spec): width bits, side bytes, scale bits, zero-points and
+Bar: width bits, side bytes, scale bits, zero-points and
 packed codes bit-exact; decoded fp32 within 1e-5 * tile scale. The fp32
 operation order is shared by specification, so every payload byte and every
 decoded value is expected to be identical; the tests require exactly that,
