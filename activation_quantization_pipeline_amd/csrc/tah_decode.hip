@@ -1,4 +1,4 @@
-// Decode kernel of the TAH-Quant codec for gfx950 (Algorithm 1, line 5: the
+// Decode kernel of the TAH-Quant codec for gfx950 (Algorithm 1, the receiver's step: the
 // receiving stage dequantizes). A workgroup is one wavefront and is
 // persistent: group g of 64 consecutive tiles (one per lane) goes to
 // workgroup g mod gridDim.x.

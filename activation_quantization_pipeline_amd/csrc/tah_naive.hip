@@ -1,5 +1,5 @@
 // Backward compressor of TAH-Quant pipeline training for gfx950: the activation
-// gradients sent back across the stage boundary (Algorithm 1, lines 6-7) go
+// gradients sent back across the stage boundary (Algorithm 1, the backward pass) go
 // through a simple b-bit fixed-point quantizer (§3.5), with the scaling of
 // Appendix H, Eq. (24): g_hat = Q(c g) / c.
 //   q = clamp(round_half_even(g * c_q), -2^(b-1), 2^(b-1) - 1),  c_q = c 2^(b-1)

@@ -283,7 +283,7 @@ def main():
             had[label] = round((x_bytes + 4 * T * C) / (h_mean * 1e-3) / 1e9, 1)
         extras["hadamard_alone_gbps"] = had
         del yh
-        # the backward path (Algorithm 1 lines 6-7): activation gradients of the same shape,
+        # the backward path (Algorithm 1, backward pass): activation gradients of the same shape,
         # fixed-point compressor at 8 bits with the scaling of Eq. (24), and TAH-Quant at 4 bits
         gname = "g1_8192x8192_bf16_grad"
         gw = synth.workload(gname)

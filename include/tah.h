@@ -5,8 +5,9 @@
  * activation tensor that one pipeline stage sends to the next:
  *   "TAH-Quant: Effective Activation Quantization in Pipeline Parallelism over
  *    Slow Network" (arXiv 2506.01352v2), Sections 3.1-3.5 and Algorithm 1.
- * The sender runs tah_encode (Algorithm 1, line 4), the receiver tah_decode
- * (line 5); tah_roundtrip does both in one pass over the tensor.
+ * The sender runs tah_encode (Algorithm 1, the sender's quantization step),
+ * the receiver tah_decode (its dequantization step); tah_roundtrip does both
+ * in one pass over the tensor.
  *
  * Tensor view: x and y are row-major [tokens, hidden], tokens = B * S
  * (micro-batch times sequence), hidden = C channels (§3.1). Each token's
@@ -142,7 +143,7 @@ tah_status_t tah_encode(const void* x, tah_dtype_t x_dtype, int64_t tokens, int6
 
 /*
  * Decode payload (payload_len bytes) into y [tokens, hidden] (y_dtype; bf16 is
- * rounded to nearest even) — Algorithm 1, line 5: unpack, dequantize, apply
+ * rounded to nearest even) — Algorithm 1, the receiver's step: unpack, dequantize, apply
  * H^T / G and undo the pivot swap on flagged tiles. The shape and params must
  * be those of the encode: the device checks the payload header against them
  * and, on a mismatch, writes TAH_ERR_BAD_PAYLOAD to the workspace status word
@@ -174,7 +175,7 @@ tah_status_t tah_workspace_entropy(int64_t tokens, int64_t hidden, const tah_par
 
 /*
  * Backward compressor for the activation gradients that the next stage sends
- * back (Algorithm 1, lines 6-7: a simple fixed-point compressor, §3.5), with
+ * back (Algorithm 1, the backward pass: a simple fixed-point compressor, §3.5), with
  * the scaling of Appendix H, Eq. (24): g_hat = Q(c g) / c. Q is b-bit signed
  * fixed point with b-1 fractional bits, round half to even, saturating:
  *   q = clamp(rne(g * c * 2^(b-1)), -2^(b-1), 2^(b-1) - 1),  g_hat = q / (c * 2^(b-1)).

@@ -10,7 +10,7 @@
  *   §3.3  Eq. (3) outlier ratio vs tau, pivot swap P_d, Eq. (4) tile-local
  *         Hadamard, asymmetric uniform quantizer, inverse by H^T;
  *   §3.4  mixed precisions + metadata packed into one fixed-size uint8 stream;
- *   Algorithm 1 (lines 4-5): sender quantizes, receiver dequantizes;
+ *   Algorithm 1: the sender quantizes, the receiver dequantizes;
  *   Appendix F: tau = 0 always transforms, tau = inf never does.
  * The Sylvester ordering of H_G follows the Hadamard quantizer section of
  * "Training Transformers with 4-bit Integers" (arXiv 2306.11987), and the
@@ -397,7 +397,7 @@ void tahref_quantize(const float* y, int G, int b, float* lo_out, float* s_out, 
 }
 
 /*
- * Receiver side (Algorithm 1 line 5; inverse of §3.3 by H^T):
+ * Receiver side (Algorithm 1, the receiver's step; inverse of §3.3 by H^T):
  *   yhat_k = fmaf(q_k, s, lo);
  *   flagged tile: z = H_G yhat, x'_k = z_k * (1/G) (exact), then undo the pivot swap;
  *   otherwise x = yhat.
@@ -611,7 +611,7 @@ int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden
 }
 
 /*
- * Encoder (Algorithm 1 line 4): entropy and widths (§3.2), then per tile the
+ * Encoder (Algorithm 1, the sender's step): entropy and widths (§3.2), then per tile the
  * outlier test, pivot swap and Hadamard (§3.3), quantization, and packing of
  * codes and metadata into one fixed-size byte stream (§3.4).
  *
@@ -699,7 +699,7 @@ int tahref_encode(const void* x, int x_dtype, int64_t tokens, int64_t hidden, co
 }
 
 /*
- * Decoder (Algorithm 1 line 5). The shape and parameters come from the caller
+ * Decoder (Algorithm 1, the receiver's step). The shape and parameters come from the caller
  * (pipeline stages know them statically); the header must agree with them.
  * Code blocks are located by a running sum over the width map in tile order;
  * the block table is checked against that sum, and so is the allocation: k
@@ -772,7 +772,7 @@ int tahref_decode(const uint8_t* P, size_t len, int64_t tokens, int64_t hidden, 
 }
 
 /* ------------------------------------------------------------------ */
-/* backward compressor Q_Naive (Algorithm 1 lines 6-7, App. H Eq. 24)  */
+/* backward compressor Q_Naive (Algorithm 1 backward, App. H Eq. 24) */
 /* ------------------------------------------------------------------ */
 
 static int naive_args_ok(int64_t n, int bits, float c) {

@@ -93,7 +93,7 @@ int tahref_tile_stats(const void* x, int x_dtype, int64_t tokens, int64_t hidden
 
 /*
  * Backward compressor Q_Naive for the activation gradients that travel back
- * across the stage boundary (Algorithm 1 lines 6-7; §3.5 calls it a simple
+ * across the stage boundary (Algorithm 1, backward pass; §3.5 calls it a simple
  * fixed-point compressor of 6-8 bits) with the scaling of Appendix H,
  * Eq. (24): g_hat = Q(c g) / c. Reading: Q is b-bit signed fixed point with
  * b-1 fractional bits (values k 2^-(b-1), k in [-2^(b-1), 2^(b-1)-1]),

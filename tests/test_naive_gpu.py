@@ -1,5 +1,5 @@
-"""GPU-vs-oracle parity of the backward compressor Q_Naive (Algorithm 1 lines
-6-7, Appendix H Eq. 24), through the C ABI.
+"""GPU-vs-oracle parity of the backward compressor Q_Naive (Algorithm 1,
+backward pass; Appendix H Eq. 24), through the C ABI.
 
 Codes are integers decided in fp32 by the same operations on both sides, so
 the payload must be byte-identical and the decoded values bit-identical.

@@ -472,7 +472,7 @@ def test_bf16_input_widens_exactly(ref):
 
 
 # ------------------------------------------------ backward compressor (Q_Naive) ----
-# Algorithm 1 lines 6-7 (fixed-point compressor of the activation gradients) and
+# Algorithm 1, backward pass (fixed-point compressor of the activation gradients) and
 # Appendix H Eq. (24) g_hat = Q(c g) / c; Q read as b-bit signed fixed point with
 # b-1 fractional bits, round half to even, saturating.
 
