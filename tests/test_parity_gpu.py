@@ -521,3 +521,37 @@ def test_threshold_inside_a_tie_in_a_large_sample(n_tied):
     n_sel = 81920 - n_flat
     assert hi[kind == 0].all() and not hi[kind == 2].any()
     assert hi[tied_idx[:n_sel]].all() and not hi[tied_idx[n_sel:]].any()
+
+
+def random_config_large(seed):
+    """A seeded random configuration of up to 3000 tokens and 64 tiles per
+    token: samples above the one-workgroup select's 4096 keys, several groups
+    per encoder workgroup; both allocators."""
+    r = np.random.default_rng(90000 + seed)
+    G = int(r.choice([32, 64, 128]))
+    M = int(r.integers(1, 65))
+    tokens = int(r.integers(1, 3001))
+    divisors = [d for d in range(1, tokens + 1) if tokens % d == 0]
+    S = int(r.choice([0] + divisors))
+    kA = int(r.choice([k for k in range(1, M + 1) if M % k == 0]))
+    n_c = int(r.integers(1, 5))
+    cands = tuple(sorted(int(c) for c in r.choice(np.arange(1, 9), size=n_c, replace=False)))
+    budget = float(np.float32(r.uniform(cands[0], cands[-1] + 0.5)))
+    tau = float(r.choice([0.0, 1.0, 2.0, 4.0, math.inf]))
+    dtype = synth.F32 if r.random() < 0.5 else synth.BF16
+    x = synth.random_tensor(tokens, G * M, dtype, 95000 + seed, scale=float(r.choice([1e-3, 1.0, 50.0])),
+                            n_out=int(r.integers(0, 4)), mult=float(r.choice([5.0, 40.0, 300.0])))
+    p = P(tile=G, tokens_per_sample=S, bit_budget=budget, candidates=cands, tau=tau, alloc_tile=G * kA,
+          allocator=seed % 2)
+    return x, p
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_random_larger_configurations(seed):
+    x, p = random_config_large(seed)
+    R, _ = run_case(x, p, f"larger random config {seed}")
+    if x.dtype == np.uint16:
+        tokens, hidden = x.shape
+        y16, _ = tah.roundtrip(to_dev(x), p, torch.bfloat16)
+        assert_decoded_equal(to_host(y16), oracle.decode(R, tokens, hidden, p, oracle.BF16), R,
+                             oracle.plan(tokens, hidden, p), f"larger random config {seed} bf16 out")
