@@ -127,8 +127,10 @@ tah_status_t tah_payload_bytes(int64_t tokens, int64_t hidden, const tah_params_
 
 /* Size in bytes of the device workspace the calls below need for this shape
  * (per-tile entropies, selection state and histograms, the tie candidates of
- * the selection, the device status word). Every call rewrites what it reads
- * there, so the contents between calls do not matter. */
+ * the selection, width map and block table when no payload is written, under
+ * the greedy allocator the used width total, the device status word). Every
+ * call rewrites what it reads there, so the contents between calls do not
+ * matter. */
 tah_status_t tah_workspace_bytes(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* out);
 
 /*
