@@ -30,7 +30,9 @@
 //              which locates every code block, and the total width (the used
 //              part of the code section).
 // When no upgrade or every upgrade fits (R = 0, one candidate, or R covering
-// all of them) the select is skipped and every tile takes the same level.
+// all of them) the select is skipped and every tile takes the same level; a
+// sample of at most kGSmall upgrades is selected by one workgroup
+// (k_gselect_small) in one launch.
 #include "tah_device.hpp"
 #include "tah_internal.hpp"
 
@@ -330,6 +332,112 @@ __global__ __launch_bounds__(kGResolveThreads) void k_gresolve(GResolveArgs a) {
   }
 }
 
+// Samples of at most kGSmall upgrades: one workgroup per sample runs the three
+// key digits and the index digits of the select in LDS (the same composites,
+// costs and find_bin as k_ghist and k_gresolve) in one launch. Up to this size
+// the grid-wide digits would run one workgroup per sample as well.
+constexpr int64_t kGSmall = kGChunk;
+
+struct GSmallArgs {
+  GArgs g;
+  GState* st_out;
+  int64_t R;
+  GPass key[3];
+  int32_t nidx;
+  GPass idx[3];
+};
+
+__global__ __launch_bounds__(kGThreads) void k_gselect_small(GSmallArgs a) {
+  __shared__ uint32_t lh[kBins];
+  __shared__ GState ss;
+  __shared__ uint32_t ipre_s;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int64_t s = blockIdx.x;
+  const float* h = a.g.H + s * a.g.N;
+  if (tid == 0) {
+    GState S;
+    S.prefix = 0ull;
+    S.r = a.R + 1;  // the first upgrade whose running cost exceeds R
+    ss = S;
+    ipre_s = 0u;
+  }
+  // key digits: descending composites, each upgrade adds its cost
+  for (int p = 0; p < 3; ++p) {
+    const GPass ps = a.key[p];
+    for (int i = tid; i < kBins; i += kGThreads) lh[i] = 0u;
+    __syncthreads();
+    const GState S = ss;
+    const int hs = ps.shift + ps.width;
+    const uint64_t dmask = (1ull << ps.width) - 1ull;
+    const uint64_t want_hi = hs >= 64 ? 0ull : (S.prefix >> hs);
+    for (int j = 0; j < a.g.nl; ++j) {
+      const uint32_t cost = (uint32_t)a.g.cost[j];
+      for (int64_t u0 = 0; u0 < a.g.N; u0 += kGThreads) {  // uniform trip count: ballots need every lane
+        const int64_t u = u0 + tid;
+        bool want = false;
+        uint32_t digit = 0;
+        if (u < a.g.N) {
+          const uint64_t C = composite(a.g, h[u], u, j);
+          want = hs >= 64 || (C >> hs) == want_hi;
+          digit = (uint32_t)((C >> ps.shift) & dmask);
+        }
+#pragma unroll
+        for (int round = 0; round < 2; ++round) {
+          const uint64_t wm = ballot(want);
+          if (wm == 0) break;
+          const int leader = __ffsll((unsigned long long)wm) - 1;
+          const uint32_t d0 = (uint32_t)__shfl((int)digit, leader, 64);
+          const bool same = want && digit == d0;
+          const uint64_t sm = ballot(same);
+          if (lane == leader) atomicAdd(&lh[d0], (uint32_t)__popcll(sm) * cost);
+          want = want && !same;
+        }
+        if (want) atomicAdd(&lh[digit], cost);
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      const GState T = apply_gpass(S, lh, ps);
+      if (tid == 0) ss = T;
+    }
+    __syncthreads();
+  }
+  // index digits among the upgrades with e*'s key, ascending
+  const uint32_t K = (uint32_t)(ss.prefix >> a.g.ib);
+  int64_t r = ss.r;
+  for (int p = 0; p < a.nidx; ++p) {
+    const GPass ps = a.idx[p];
+    for (int i = tid; i < kBins; i += kGThreads) lh[i] = 0u;
+    __syncthreads();
+    const uint32_t ipre = ipre_s;
+    const int hs = ps.shift + ps.width;
+    const uint32_t dmask = (1u << ps.width) - 1u;
+    for (int j = 0; j < a.g.nl; ++j) {
+      for (int64_t u = tid; u < a.g.N; u += kGThreads) {
+        const uint32_t key = (uint32_t)(composite(a.g, h[u], u, j) >> a.g.ib);
+        const uint32_t idx = (uint32_t)(u * a.g.nl + j);
+        if (key == K && (hs >= 32 || (idx >> hs) == (ipre >> hs)))
+          atomicAdd(&lh[(idx >> ps.shift) & dmask], (uint32_t)a.g.cost[j]);
+      }
+    }
+    __syncthreads();
+    if (tid < 64) {
+      uint32_t digit;
+      int64_t before;
+      find_bin<false>(lh, r, digit, before);
+      if (tid == 0) ipre_s = ipre | (digit << ps.shift);
+      r -= before;  // only wavefront 0's r is used
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    GState T;
+    T.prefix = ((uint64_t)K << a.g.ib) | (((1ull << a.g.ib) - 1ull) - (uint64_t)ipre_s);
+    T.r = r;
+    a.st_out[s] = T;
+  }
+}
+
 // ------------------------------------------------------------------ levels ----
 struct LevelArgs {
   GArgs g;
@@ -386,7 +494,21 @@ hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st
   GState* states = reinterpret_cast<GState*>(w + pl.ws_state);
   const int64_t ns = pl.nsamples;
   GState* final_st = nullptr;
-  if (pl.glevel < 0) {
+  if (pl.glevel < 0 && pl.N * pl.nl <= kGSmall) {
+    GSmallArgs sa;
+    sa.g = g;
+    sa.st_out = states;
+    sa.R = pl.R;
+    for (int i = 0; i < 3; ++i) {
+      sa.key[i] = pl.gpasses[i];
+      sa.idx[i] = pl.gidx[i];
+    }
+    sa.nidx = pl.ngidx;
+    hipLaunchKernelGGL(k_gselect_small, dim3((unsigned)ns), dim3(kGThreads), 0, st, sa);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    final_st = states;
+  } else if (pl.glevel < 0) {
     uint32_t* hists = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
     const int64_t hsz = ns * kBins;
     GHistArgs h;

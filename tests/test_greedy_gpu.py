@@ -63,6 +63,12 @@ def test_every_key_ties(tile):
     z = np.zeros((40, tile * 7), np.float32)  # all-zero tiles: H = 0 everywhere
     run_case(z, P(tile=tile, tokens_per_sample=8, bit_budget=3.5, candidates=(2, 3, 4, 8), tau=2.0, allocator=GREEDY),
              f"zeros tile {tile}")
+    # a sample of 4096 tiles (12288 upgrades): the select runs grid-wide, every
+    # upgrade of a level shares one key, the tie list overflows and the tie
+    # step goes through the whole sample
+    zb = np.zeros((64, tile * 64), np.float32)
+    run_case(zb, P(tile=tile, tokens_per_sample=0, bit_budget=3.37, candidates=(2, 3, 4, 8), tau=2.0,
+                   allocator=GREEDY), f"zeros tile {tile}, one large sample")
 
 
 @pytest.mark.parametrize("tile", [32, 64, 128])
@@ -118,16 +124,18 @@ def test_header_mismatch_sets_status():
         assert tah.read_device_status(ws) == 5
 
 
+@pytest.mark.parametrize("tokens", [200, 2000])
 @pytest.mark.parametrize("tile,budget,cands", [(64, 3.3, (2, 3, 4, 8)), (32, 2.7, (1, 2, 4)), (128, 4.6, (3, 4, 8))])
-def test_ties_resolved_from_the_list(tile, budget, cands):
+def test_ties_resolved_from_the_list(tile, budget, cands, tokens):
     """Eight distinct rows repeated: 8 distinct entropies, each shared by many
-    tiles, so e*'s key is tied across tiles but few keys match its prefix: the
-    tie is broken from the listed (key, index) pairs, not by the whole-sample
-    scan."""
+    tiles, so e*'s key is tied across tiles but few keys match its prefix. With
+    200 tokens the sample is small enough for the one-workgroup select; with
+    2000 the select runs grid-wide and the tie is broken from the listed
+    (key, index) pairs, not by the whole-sample scan."""
     rows = synth.random_tensor(8, tile * 3, synth.F32, tile, n_out=1, mult=20)
-    order = np.random.default_rng(tile).integers(0, 8, size=200)
+    order = np.random.default_rng(tile).integers(0, 8, size=tokens)
     x = np.ascontiguousarray(rows[order]).astype(np.float32)
     p = P(tile=tile, tokens_per_sample=0, bit_budget=budget, candidates=cands, tau=2.0, allocator=GREEDY)
-    R, _ = run_case(x, p, f"listed ties tile {tile}")
-    pl = oracle.plan(200, tile * 3, p)
+    R, _ = run_case(x, p, f"listed ties tile {tile}, {tokens} tokens")
+    pl = oracle.plan(tokens, tile * 3, p)
     assert len(levels_used(R, pl)) >= 2
