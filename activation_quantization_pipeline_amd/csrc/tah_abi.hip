@@ -2,6 +2,8 @@
 // plan (width pair and k of §3.2, payload layout of §3.4, workspace layout) and
 // the launch sequence. Validation happens before anything is enqueued.
 #include <math.h>
+#include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include "tah_internal.hpp"
@@ -14,6 +16,37 @@ static int ilog2(int v) {
   int l = 0;
   while ((1 << l) < v) ++l;
   return l;
+}
+
+// The bit budget as the decimal it stands for: the pages give the split as a
+// percentage (80% INT4 / 20% INT3, TAH-Quant §3.2 and §5.1), a budget of 3.8
+// bits that fp32 holds as 3.79999995, which would make floor(p N) one short
+// whenever 0.8 N is an integer. The budget is read as the decimal with the
+// fewest fractional digits that rounds to the given fp32 value (the nearest
+// one, ties to even): num / den, den = 10^digits. B * 10^digits is exact in
+// double (24 + 21 significant bits), so rint rounds the exact product.
+static void budget_as_decimal(float B, int64_t* num, int64_t* den) {
+  double scale = 1.0;
+  for (int digits = 0; digits <= 9; ++digits, scale *= 10.0) {
+    const double m = rint((double)B * scale);
+    char s[48];
+    snprintf(s, sizeof s, "%.0fe-%d", m, digits);
+    if (strtof(s, nullptr) == B) {
+      *num = (int64_t)m;
+      *den = (int64_t)scale;
+      return;
+    }
+  }
+  *num = (int64_t)rint((double)B * 1e9);
+  *den = 1000000000;
+}
+
+// floor((B - base) N / step) for the decimal budget B >= base, in integers.
+static int64_t budget_floor(float B, int base, int64_t N, int step) {
+  int64_t num = 0, den = 1;
+  budget_as_decimal(B, &num, &den);
+  const __int128 above = (__int128)num - (__int128)base * den;
+  return (int64_t)(above * (__int128)N / ((__int128)step * den));
 }
 
 static int bit_width(uint64_t v) {
@@ -74,9 +107,8 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   if (p->allocator == TAH_ALLOC_TOP_P) {
     o->b_lo = b_lo;
     o->b_hi = b_hi;
-    o->k = (b_hi == b_lo || o->N == 0)
-               ? 0
-               : (int64_t)floor(((double)p->bit_budget - (double)b_lo) * (double)o->N / (double)(b_hi - b_lo));
+    // k = floor(p N), p = (B - b_lo) / (b_hi - b_lo) of the decimal budget B
+    o->k = (b_hi == b_lo || o->N == 0) ? 0 : budget_floor(p->bit_budget, b_lo, o->N, b_hi - b_lo);
     o->mode = o->k > 0 ? 1 : 0;
   } else {
     // greedy: any candidate per allocation tile; R = floor((B - c_1) N) bits a
@@ -88,8 +120,9 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
     o->mode = 2;
     o->nl = p->n_candidates - 1;
     const int64_t cap = (int64_t)(cn - c1) * o->N;
-    const double r = floor(((double)p->bit_budget - (double)c1) * (double)o->N);
-    o->R = r < (double)cap ? (int64_t)r : cap;
+    // from B = c_n on every upgrade fits; below it the decimal budget decides
+    o->R = p->bit_budget >= (float)cn ? cap : budget_floor(p->bit_budget, c1, o->N, 1);
+    if (o->R > cap) o->R = cap;
     // the block table's running width sums are 32-bit (a limit of the format)
     if ((uint64_t)o->tiles * (uint64_t)cn > 0xffffffffull) return TAH_ERR_INVALID_ARG;
     // per-sample weights and upgrade indexes are 32-bit on the device

@@ -25,6 +25,7 @@
 #include "tah_ref.h"
 
 #include <math.h>
+#include <stdio.h>
 #include <stdlib.h>
 #include <string.h>
 
@@ -80,6 +81,48 @@ static int ilog2(int v) {
   int l = 0;
   while ((1 << l) < v) ++l;
   return l;
+}
+
+/*
+ * The budget as the decimal it stands for. The pages state the split as a
+ * percentage (80% INT4 / 20% INT3, §3.2 and §5.1), i.e. a budget of 3.8 bits,
+ * which fp32 cannot hold: 3.8f is 3.7999999523..., and floor(0.79999995 N)
+ * would give 0.8 N - 1 whenever 0.8 N is an integer. Reading: the budget is
+ * the shortest decimal that rounds to the given fp32 value (fewest fractional
+ * digits, the nearest such decimal), B = num / den with den = 10^digits.
+ * Only budgets below 8 (the widest candidate) ever need it, so at most eight
+ * fractional digits and num, den < 2^30.
+ */
+static void budget_decimal(float B, int64_t* num, int64_t* den) {
+  char buf[64];
+  for (int digits = 0; digits <= 9; ++digits) {
+    snprintf(buf, sizeof buf, "%.*f", digits, (double)B); /* correctly rounded to `digits` places */
+    if (strtof(buf, NULL) != B) continue;
+    int64_t n = 0, d = 1;
+    int frac = 0;
+    for (const char* c = buf; *c; ++c) {
+      if (*c == '.') {
+        frac = 1;
+        continue;
+      }
+      n = n * 10 + (*c - '0');
+      if (frac) d *= 10;
+    }
+    *num = n;
+    *den = d;
+    return;
+  }
+  /* unreachable for finite B in [1, 8]: nine digits always round-trip */
+  *num = (int64_t)floor((double)B * 1e9);
+  *den = 1000000000;
+}
+
+/* floor((B - base) * N / step) for the decimal budget B, base <= B, exactly. */
+static int64_t budget_floor(float B, int base, int64_t N, int step) {
+  int64_t num, den;
+  budget_decimal(B, &num, &den);
+  const __int128 excess = (__int128)num - (__int128)base * den; /* (B - base) * den >= 0 */
+  return (int64_t)((excess * N) / ((__int128)step * den));
 }
 
 /* ------------------------------------------------------------------ */
@@ -148,13 +191,11 @@ int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tah
   if (p->allocator == 0) {
     o->b_lo = b_lo;
     o->b_hi = b_hi;
-    if (b_hi == b_lo || o->atiles_per_sample == 0) {
+    /* k = floor(p N) with p = (B - b_lo) / (b_hi - b_lo) and B the decimal budget */
+    if (b_hi == b_lo || o->atiles_per_sample == 0)
       o->k = 0;
-    } else {
-      double kk = floor(((double)p->bit_budget - (double)b_lo) * (double)o->atiles_per_sample /
-                        (double)(b_hi - b_lo));
-      o->k = (int64_t)kk;
-    }
+    else
+      o->k = budget_floor(p->bit_budget, b_lo, o->atiles_per_sample, b_hi - b_lo);
   } else {
     /* greedy (tahref_allocate_greedy): every candidate may occur; b_lo and b_hi
      * record the narrowest and the widest, and a sample may spend R bits above
@@ -165,9 +206,10 @@ int tahref_plan_make(int64_t tokens, int64_t hidden, const tahref_params* p, tah
     o->b_hi = cn;
     o->k = 0;
     const int64_t N = o->atiles_per_sample;
-    const double r = floor(((double)p->bit_budget - (double)c1) * (double)N);
     const int64_t cap = (int64_t)(cn - c1) * N;
-    o->R = r < (double)cap ? (int64_t)r : cap;
+    /* R = floor((B - c_1) N) with B the decimal budget; from B = c_n on, everything fits */
+    o->R = p->bit_budget >= (float)cn ? cap : budget_floor(p->bit_budget, c1, N, 1);
+    if (o->R > cap) o->R = cap;
     /* the block table holds the running sum of code widths in 32 bits */
     if ((uint64_t)o->tiles * (uint64_t)cn > 0xffffffffull) return TAHREF_ERR_INVALID_ARG;
   }

@@ -50,6 +50,20 @@ def test_sizes_match_oracle_layout(ref):
         assert tah.payload_bytes(50, 1536, p) == ref.plan(50, 1536, p)["total"], A
 
 
+def test_decimal_budget_sizes_match_oracle(ref):
+    # k (top-p) and R (greedy) follow the budget read as a decimal: 3.8 bits over
+    # N = 5 tiles is 4 tiles at 4 bits, which the code section's size shows
+    for N in (5, 80, 10240):
+        for budget, cands in [(3.8, (3, 4)), (3.3, (3, 4, 8)), (2.6, (2, 3)), (3.1415927, (3, 4))]:
+            for alloc in (0, 1):
+                p = synth.Params(tile=64, tokens_per_sample=0, bit_budget=budget, candidates=cands, allocator=alloc)
+                assert tah.payload_bytes(N, 64, p) == ref.plan(N, 64, p)["total"], (N, budget, alloc)
+    p = synth.Params(tile=64, tokens_per_sample=0, bit_budget=3.8, candidates=(3, 4))
+    pl = ref.plan(80, 64, p)
+    assert pl["code_bytes"] == 80 * 24 + 64 * 8
+    assert tah.payload_bytes(80, 64, p) == pl["off_codes"] + ((80 * 24 + 64 * 8 + 255) // 256) * 256
+
+
 def test_status_strings():
     for c in range(7):
         assert tah.status_string(c)

@@ -368,6 +368,27 @@ def test_width_pair_and_k(ref, N, budget, cands, blo, bhi, k):
         assert total + (bhi - blo) > budget * N
 
 
+@pytest.mark.parametrize("N", [5, 10, 80, 10240, 1048575])
+def test_k_of_decimal_budgets(ref, N):
+    # The pages' default is 80% INT4 / 20% INT3 (Sec. 3.2, Sec. 5.1): k = 0.8 N
+    # exactly when 0.8 N is an integer, although 3.8 in fp32 is 3.79999995.
+    # The budget is the shortest decimal that rounds to the fp32 value.
+    for budget, cands, frac in [(3.8, (3, 4), (4, 5)), (3.3, (3, 4), (3, 10)), (3.7, (3, 4, 8), (7, 10)),
+                                (2.6, (2, 3), (3, 5)), (4.2, (2, 4, 8), (1, 20)), (3.5, (3, 4), (1, 2))]:
+        assert float(np.float32(budget)) != budget or budget == 3.5
+        p = synth.Params(tile=64, tokens_per_sample=0, bit_budget=budget, candidates=cands, tau=2.0)
+        pl = ref.plan(N, 64, p)
+        assert pl["k"] == N * frac[0] // frac[1], (budget, N)
+        # the greedy allocator's bits above c_1: R = floor((B - c_1) N) with the same decimal B
+        g = synth.Params(**{**p.__dict__, "allocator": 1})
+        c1, cn = cands[0], cands[-1]
+        want = min((N * round((budget - c1) * 10)) // 10, (cn - c1) * N)
+        assert ref.plan(N, 64, g)["R"] == want, (budget, N)
+    # a budget with more digits: 3.1415927 (fp32 of pi - 0.0000001) keeps all its digits
+    p = synth.Params(tile=64, tokens_per_sample=0, bit_budget=float(np.float32(3.1415927)), candidates=(3, 4))
+    assert ref.plan(N, 64, p)["k"] == (N * 1415927) // 10000000
+
+
 def test_budget_errors(ref):
     with pytest.raises(ref.OracleError) as e:
         ref.plan(4, 64, synth.Params(tile=64, bit_budget=2.5, candidates=(3, 4)))
