@@ -9,11 +9,16 @@ three buffer sets rotate so no step reads what the previous step left in the
 256 MB Infinity Cache.
 
 value = algorithmic bytes per step (activations read + payload written +
-activations written) / time per step, in GB/s.
+activations written) / wall time per step, in GB/s; the activation rate
+|X| / t is reported beside it (extras.activation_gbps_roundtrip).
 
-Prints one JSON line. Extra legs: encode-only and decode-only rates, the same
-shape with a mixed 80% INT4 / 20% INT3 allocation (the paper's default,
-general two-pass path), the backward path on activation gradients of the same
+Prints one JSON line. Extra legs: the fused round trip of every workload
+shape (c1-c4 beside the headline c5, each with its fraction of the HBM peak),
+the headline shape on the general path (entropy pass, per-sample select,
+width map and block table, then the encoder: a budget of 3.000001 bits makes
+k = 1, so every kernel of the mixed path runs), encode-only and decode-only
+rates, the same shape with a mixed 80% INT4 / 20% INT3 allocation (the
+paper's default), the backward path on activation gradients of the same
 shape (the 8-bit fixed-point compressor with the scaling of Eq. 24, encode and
 decode, and the TAH-Quant codec at 4 bits), the tile-local Hadamard alone
 (the butterfly against the dense product on the matrix cores), a 512 MB device
@@ -81,6 +86,44 @@ def measured_valu():
     return {"lane_ops_per_element": sq["valu_lane_ops_per_element"], "busy_frac": sq["valu_busy_frac"]} if sq else None
 
 
+def host_cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def environment(torch) -> dict:
+    """GPU, ROCm and host figures recorded with the line."""
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    try:
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    except OSError:
+        pass
+    return {
+        "gpu": props.name,
+        "gpu_arch": getattr(props, "gcnArchName", None),
+        "compute_units": props.multi_processor_count,
+        "gpu_memory_gib": round(props.total_memory / 2**30, 1),
+        "rocm": rocm,
+        "torch_hip": torch.version.hip,
+        "host_cpu": host_cpu_model(),
+        "host_nproc": os.cpu_count(),
+        "host_cpus_usable": len(os.sched_getaffinity(0)),
+    }
+
+
+def allocation_label(p) -> str:
+    """The width pair of the budget (the two candidates around it) as a label."""
+    lo = max(c for c in p.candidates if c <= p.bit_budget)
+    hi = [c for c in p.candidates if c > p.bit_budget]
+    return f"uniform {lo}-bit" if not hi or p.bit_budget == lo else f"top-p {lo}/{hi[0]}-bit"
+
+
 def to_dev(x, torch):
     import numpy as np
 
@@ -123,6 +166,39 @@ def time_launches(torch, launch, n_sets, steps, warmup):
     return wall / steps * 1e3, mean, statistics.median(per), min(per)
 
 
+def roundtrip_leg_fn(torch, tah, synth, dev, stream_h, n_sets, args):
+    """A timer of the fused round trip of one workload shape."""
+
+    def roundtrip_leg(name, params=None, seed=0, x_sets=None):
+        """Fused round trip of one workload shape (payload written, output in the
+        input's dtype, three rotating buffer sets): time per launch from the
+        events around all launches, GB/s of algorithmic bytes and their fraction
+        of the HBM peak."""
+        wl = synth.workload(name)
+        prm = params or wl.params
+        tdt = torch.bfloat16 if wl.dtype == synth.BF16 else torch.float32
+        if x_sets is None:
+            xh = synth.generate(name, seed)
+            x_sets = [to_dev(xh, torch) for _ in range(n_sets)]
+        cl = tah.Codec(wl.tokens, wl.hidden, prm, tdt, tdt)
+        yl = [torch.empty((wl.tokens, wl.hidden), dtype=tdt, device=dev) for _ in range(n_sets)]
+        pl_ = [torch.empty(cl.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
+        wsl = torch.empty(cl.workspace_bytes, dtype=torch.uint8, device=dev)
+        xb = x_sets[0].numel() * x_sets[0].element_size()
+        nbytes = 2 * xb + cl.payload_bytes
+        l_ms, l_mean, _, _ = time_launches(torch, lambda i: cl.roundtrip(x_sets[i], pl_[i], yl[i], wsl, stream_h),
+                                           n_sets, args.steps, args.warmup)
+        del yl, pl_, wsl
+        gbps = nbytes / (l_mean * 1e-3) / 1e9
+        return {"shape": f"{wl.tokens}x{wl.hidden} {'bf16' if wl.dtype == synth.BF16 else 'fp32'} tile {prm.tile}",
+                "budget": prm.bit_budget, "candidates": list(prm.candidates), "allocation": allocation_label(prm),
+                "us_per_launch": round(l_mean * 1e3, 2), "us_wall_per_step": round(l_ms * 1e3, 2),
+                "algorithmic_bytes": nbytes, "gbps": round(gbps, 1), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+                "activation_gbps": round(xb / (l_mean * 1e-3) / 1e9, 1)}
+
+    return roundtrip_leg
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -131,6 +207,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle leg")
     ap.add_argument("--no-extras", action="store_true", help="time only the headline round trip")
     ap.add_argument("--copy-only", action="store_true", help="only a 512 MB device copy (counter calibration)")
+    ap.add_argument("--workload", default=None,
+                    help="only the fused round trip of this workload (a name from synth), for kernel traces")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -154,12 +232,17 @@ def main():
         print(json.dumps({"copy_bytes": 512 << 20, "copy_ms": med, "copy_gbps": 2 * (512 << 20) / (med * 1e-3) / 1e9}))
         return
 
+    n_sets = 3
+    if args.workload:
+        leg = roundtrip_leg_fn(torch, tah, synth, dev, stream_h, n_sets, args)(args.workload)
+        print(json.dumps({"workload": args.workload, **leg}))
+        return
+
     w = synth.workload(WORKLOAD)
     p = w.params
     T, C = w.tokens, w.hidden
     x_host = synth.generate(WORKLOAD, 0)
     codec = tah.Codec(T, C, p, torch.bfloat16, torch.bfloat16)
-    n_sets = 3
     xs = [to_dev(x_host, torch) for _ in range(n_sets)]
     ys = [torch.empty((T, C), dtype=torch.bfloat16, device=dev) for _ in range(n_sets)]
     ps = [torch.empty(codec.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
@@ -197,6 +280,7 @@ def main():
             "tau": p.tau,
             "payload_bytes": codec.payload_bytes,
             "bytes_per_step": bytes_step,
+            "value_is": "algorithmic bytes per second: activations read + payload written + activations written",
             "hbm_fraction": round(value / HBM_PEAK_GBPS, 4),
         },
         "roofline": {
@@ -215,8 +299,24 @@ def main():
         },
     }
 
+    out["environment"] = environment(torch)
+
+    roundtrip_leg = roundtrip_leg_fn(torch, tah, synth, dev, stream_h, n_sets, args)
+
     if not args.no_extras:
         extras = {}
+        # the fused round trip of every workload shape (c5 is the headline, timed above)
+        legs = {}
+        for name in ("c1_256x512_f32_g32", "c2_4096x2048_bf16_g64", "c3_16384x4096_bf16_g64",
+                     "c4_16384x5120_f32_g128"):
+            legs[name] = roundtrip_leg(name)
+        legs[WORKLOAD] = roundtrip_leg(WORKLOAD, x_sets=xs)
+        extras["workloads_roundtrip"] = legs
+        # the headline shape on the general path: entropy pass, select, width map
+        # and block table, encoder; a budget of 3.000001 bits gives k = 1 of the
+        # 1,048,576 tiles, the smallest allocation that runs every kernel of it
+        extras["general_path_c5_k1"] = roundtrip_leg(
+            WORKLOAD, params=dataclasses.replace(p, bit_budget=3.000001), x_sets=xs)
         # encode only and decode only on the same tensor
         _, e_mean, _, _ = time_launches(torch, lambda i: codec.encode(xs[i], ps[i], ws, stream_h), n_sets,
                                         args.steps, args.warmup)
@@ -334,6 +434,8 @@ def main():
             "unit": "GB/s",
             "cores": 1,
             "kind": "oracle",
+            "host_cpu": host_cpu_model(),
+            "host_nproc": os.cpu_count(),
             "sample": f"the full 8192x8192 tensor of this workload, oracle encode then decode to bf16, "
                       f"single thread, median of {len(runs)} runs ({t_cpu:.2f} s each, {sum(runs):.1f} s in all)",
         }

@@ -64,6 +64,24 @@ def test_decimal_budget_sizes_match_oracle(ref):
     assert tah.payload_bytes(80, 64, p) == pl["off_codes"] + ((80 * 24 + 64 * 8 + 255) // 256) * 256
 
 
+def test_budget_reading_agrees_with_oracle_on_random_budgets(ref):
+    # 32 samples of 64-bit-wide tiles: one more upgraded tile per sample adds
+    # 32 x 8 bytes, so any difference in k between the library's planner and the
+    # oracle's moves the payload size by a whole 256-byte step
+    r = np.random.default_rng(77)
+    for _ in range(1500):
+        S, M = int(r.integers(1, 40)), int(r.integers(1, 9))
+        lo = int(r.integers(1, 8))
+        digits = int(r.integers(1, 9))
+        budget = float(np.float32(round(lo + r.random(), digits)))
+        if budget >= lo + 1:
+            continue
+        p = synth.Params(tile=64, tokens_per_sample=S, bit_budget=budget, candidates=(lo, lo + 1))
+        assert tah.payload_bytes(32 * S, 64 * M, p) == ref.plan(32 * S, 64 * M, p)["total"], (budget, S, M)
+        g = synth.Params(**{**p.__dict__, "candidates": (lo, lo + 1, 8) if lo + 1 < 8 else (lo, 8), "allocator": 1})
+        assert tah.payload_bytes(32 * S, 64 * M, g) == ref.plan(32 * S, 64 * M, g)["total"], (budget, S, M)
+
+
 def test_status_strings():
     for c in range(7):
         assert tah.status_string(c)
