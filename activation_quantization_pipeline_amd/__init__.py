@@ -31,6 +31,7 @@ STATUS_NAMES = {
     4: "TAH_ERR_BUDGET_INFEASIBLE",
     5: "TAH_ERR_BAD_PAYLOAD",
     6: "TAH_ERR_HIP",
+    7: "TAH_ERR_SCRATCH_LIMIT",
 }
 
 # Every symbol include/tah.h declares.
@@ -41,6 +42,7 @@ EXPORTS = (
     "tah_encode",
     "tah_decode",
     "tah_roundtrip",
+    "tah_roundtrip_noalloc",
     "tah_tile_entropy",
     "tah_workspace_entropy",
     "tah_naive_payload_bytes",
@@ -106,7 +108,8 @@ def _cparams(p) -> _CParams:
 
 
 _lib = None
-ABI_VERSION = 3  # TAH_ABI_VERSION of include/tah.h
+ABI_VERSION = 4  # TAH_ABI_VERSION of include/tah.h
+NOALLOC_SCRATCH_BYTES = 32 << 20  # TAH_NOALLOC_SCRATCH_BYTES of include/tah.h
 ALLOC_TOP_P, ALLOC_GREEDY = 0, 1  # TAH_ALLOC_* of include/tah.h
 
 
@@ -130,6 +133,8 @@ def lib() -> ctypes.CDLL:
         L.tah_decode.restype = ctypes.c_int
         L.tah_roundtrip.argtypes = [vp, ctypes.c_int, i64, i64, P(_CParams), vp, sz, vp, ctypes.c_int, vp, sz, vp]
         L.tah_roundtrip.restype = ctypes.c_int
+        L.tah_roundtrip_noalloc.argtypes = [vp, ctypes.c_int, i64, i64, P(_CParams), vp, sz, vp, ctypes.c_int, vp]
+        L.tah_roundtrip_noalloc.restype = ctypes.c_int
         L.tah_tile_entropy.argtypes = [vp, ctypes.c_int, i64, i64, P(_CParams), vp, vp, sz, vp]
         L.tah_tile_entropy.restype = ctypes.c_int
         L.tah_naive_payload_bytes.argtypes = [i64, ctypes.c_int, P(sz)]
@@ -315,6 +320,21 @@ def roundtrip(x: torch.Tensor, p, y_dtype: torch.dtype | None = None, payload: t
                                  _stream(stream, dev))
     _check(rc, "tah_roundtrip")
     return y, payload
+
+
+def roundtrip_noalloc(x: torch.Tensor, p, payload: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """tah_roundtrip_noalloc: tah_roundtrip with the library's own scratch in place
+    of a workspace; the caller passes the payload (or None) and y it writes."""
+    tokens, hidden = _shape(x)
+    dev = _dev(x, "x")
+    _need(y, tokens * hidden, "y")
+    cp = _cparams(p)
+    with torch.cuda.device(dev):
+        rc = lib().tah_roundtrip_noalloc(_ptr(x, dev, "x"), _dtype_code(x.dtype), tokens, hidden, ctypes.byref(cp),
+                                         _ptr(payload, dev, "payload"),
+                                         _nbytes(payload) if payload is not None else 0, _ptr(y, dev, "y"),
+                                         _dtype_code(y.dtype), _stream(stream, dev))
+    _check(rc, "tah_roundtrip_noalloc")
 
 
 def tile_entropy(x: torch.Tensor, p, h: torch.Tensor | None = None, ws: torch.Tensor | None = None,

@@ -6,6 +6,9 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+#include <mutex>
+
 #include "tah_internal.hpp"
 
 namespace tah {
@@ -285,20 +288,22 @@ static bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 static bool gpu_tile_ok(int G) { return G == 32 || G == 64 || G == 128; }
 
-static tah_status_t run_encode(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden,
-                               const tah_params_t* p, void* payload, size_t payload_cap, void* y,
-                               tah_dtype_t y_dtype, bool want_y, void* ws, size_t ws_cap, void* stream) {
-  Plan pl;
-  tah_status_t rc = make_plan(tokens, hidden, p, &pl);
-  if (rc != TAH_OK) return rc;
+// Checks of an encode or round trip that do not involve the workspace.
+static tah_status_t check_encode(const Plan& pl, const void* x, tah_dtype_t x_dtype, const void* payload,
+                                 size_t payload_cap, const void* y, tah_dtype_t y_dtype, bool want_y) {
   if (x_dtype != TAH_DTYPE_F32 && x_dtype != TAH_DTYPE_BF16) return TAH_ERR_INVALID_ARG;
   if (want_y && y_dtype != TAH_DTYPE_F32 && y_dtype != TAH_DTYPE_BF16) return TAH_ERR_INVALID_ARG;
   if (!gpu_tile_ok(pl.G)) return TAH_ERR_UNSUPPORTED;
-  if (!ws || !aligned16(ws) || (payload && !aligned16(payload))) return TAH_ERR_INVALID_ARG;
+  if (payload && !aligned16(payload)) return TAH_ERR_INVALID_ARG;
   if (!want_y && !payload) return TAH_ERR_INVALID_ARG;
   if (pl.tiles > 0 && (!x || !aligned16(x) || (want_y && (!y || !aligned16(y))))) return TAH_ERR_INVALID_ARG;
   if (payload && payload_cap < (size_t)pl.total) return TAH_ERR_BUFFER_TOO_SMALL;
-  if (ws_cap < (size_t)pl.ws_total) return TAH_ERR_BUFFER_TOO_SMALL;
+  return TAH_OK;
+}
+
+// The launch sequence of an encode or round trip on a checked plan.
+static tah_status_t launch_encode_path(Plan& pl, const void* x, tah_dtype_t x_dtype, void* payload, void* y,
+                                       tah_dtype_t y_dtype, bool want_y, void* ws, void* stream) {
   pl.x_dtype = x_dtype;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* w = static_cast<uint8_t*>(ws);
@@ -321,6 +326,53 @@ static tah_status_t run_encode(const void* x, tah_dtype_t x_dtype, int64_t token
     if (e != hipSuccess) return hip_status(e);
   }
   return hip_status(launch_encode(pl, x, payload, want_y ? y : nullptr, y_dtype, ws, st, mode));
+}
+
+static tah_status_t run_encode(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden,
+                               const tah_params_t* p, void* payload, size_t payload_cap, void* y,
+                               tah_dtype_t y_dtype, bool want_y, void* ws, size_t ws_cap, void* stream) {
+  Plan pl;
+  tah_status_t rc = make_plan(tokens, hidden, p, &pl);
+  if (rc != TAH_OK) return rc;
+  rc = check_encode(pl, x, x_dtype, payload, payload_cap, y, y_dtype, want_y);
+  if (rc != TAH_OK) return rc;
+  if (!ws || !aligned16(ws)) return TAH_ERR_INVALID_ARG;
+  if (ws_cap < (size_t)pl.ws_total) return TAH_ERR_BUFFER_TOO_SMALL;
+  return launch_encode_path(pl, x, x_dtype, payload, y, y_dtype, want_y, ws, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free round trip (tah_roundtrip_noalloc): device
+// memory at file scope, TAH_NOALLOC_SCRATCH_BYTES on every GPU the library
+// runs on, held until the process ends. It plays the part of the caller's
+// workspace in the other calls. In host code the name `scratch` is a host-side
+// stand-in, never a device address: kernels only ever receive the address that
+// hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) uint8_t scratch[TAH_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_addr[kMaxDevices];
+}  // namespace
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (each GPU holds its own copy).
+static tah_status_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return TAH_ERR_HIP;
+  if (dev >= kMaxDevices) return TAH_ERR_UNSUPPORTED;
+  void* p = g_scratch_addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_addr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return TAH_ERR_HIP;
+      g_scratch_addr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return TAH_OK;
 }
 
 }  // namespace tah
@@ -379,6 +431,21 @@ tah_status_t tah_roundtrip(const void* x, tah_dtype_t x_dtype, int64_t tokens, i
                            void* payload, size_t payload_cap, void* y, tah_dtype_t y_dtype, void* ws, size_t ws_cap,
                            void* stream) {
   return run_encode(x, x_dtype, tokens, hidden, p, payload, payload_cap, y, y_dtype, true, ws, ws_cap, stream);
+}
+
+tah_status_t tah_roundtrip_noalloc(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden,
+                                   const tah_params_t* p, void* payload, size_t payload_cap, void* y,
+                                   tah_dtype_t y_dtype, void* stream) {
+  Plan pl;
+  tah_status_t rc = make_plan(tokens, hidden, p, &pl);
+  if (rc != TAH_OK) return rc;
+  rc = check_encode(pl, x, x_dtype, payload, payload_cap, y, y_dtype, true);
+  if (rc != TAH_OK) return rc;
+  if ((uint64_t)pl.ws_total > (uint64_t)TAH_NOALLOC_SCRATCH_BYTES) return TAH_ERR_SCRATCH_LIMIT;
+  void* ws = nullptr;
+  rc = scratch_on_current_device(&ws);
+  if (rc != TAH_OK) return rc;
+  return launch_encode_path(pl, x, x_dtype, payload, y, y_dtype, true, ws, stream);
 }
 
 tah_status_t tah_decode(const void* payload, size_t payload_len, int64_t tokens, int64_t hidden, const tah_params_t* p,
@@ -467,6 +534,7 @@ const char* tah_status_string(tah_status_t s) {
     case TAH_ERR_BUDGET_INFEASIBLE: return "bit budget below the smallest candidate width";
     case TAH_ERR_BAD_PAYLOAD: return "payload header does not match shape/params";
     case TAH_ERR_HIP: return "HIP runtime error";
+    case TAH_ERR_SCRATCH_LIMIT: return "shape needs more scratch than the allocation-free round trip holds";
   }
   return "unknown status";
 }

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TAH_ABI_VERSION 3
+#define TAH_ABI_VERSION 4
 
 typedef enum { TAH_DTYPE_F32 = 0, TAH_DTYPE_BF16 = 1 } tah_dtype_t;
 
@@ -49,7 +49,8 @@ typedef enum {
   TAH_ERR_BUFFER_TOO_SMALL = 3,  /* payload_cap / ws_cap / payload_len below the required size */
   TAH_ERR_BUDGET_INFEASIBLE = 4, /* bit_budget below the smallest candidate width */
   TAH_ERR_BAD_PAYLOAD = 5,       /* payload header disagrees with shape/params (device status word) */
-  TAH_ERR_HIP = 6                /* a HIP runtime call or kernel launch failed */
+  TAH_ERR_HIP = 6,               /* a HIP runtime call or kernel launch failed */
+  TAH_ERR_SCRATCH_LIMIT = 7      /* tah_roundtrip_noalloc: the shape needs more than TAH_NOALLOC_SCRATCH_BYTES */
 } tah_status_t;
 
 /*
@@ -64,7 +65,10 @@ typedef enum {
  *     the k = floor((budget - b_lo) * N / (b_hi - b_lo)) highest-entropy
  *     allocation tiles of a sample (N = S * hidden / A of them) get b_hi, the
  *     rest b_lo (§3.2, INT4 for the top p%, INT3 for the rest). Equal entropies
- *     rank the lower allocation-tile index first.
+ *     rank the lower allocation-tile index first. The budget is read as the
+ *     decimal it stands for: the shortest decimal that rounds to the given
+ *     fp32 value (3.8f, held as 3.79999995, is 3.8, so 80% of N tiles get b_hi
+ *     whenever 0.8 N is an integer); k is computed from it exactly.
  *   n_candidates, candidates: 1..4 widths, strictly increasing, each 1..8.
  *   tau: outlier threshold of Eq. (3) (§3.3, default 2.0); 0 transforms every
  *     non-zero tile, +INFINITY none (Appendix F). Must be >= 0 and not NaN.
@@ -124,6 +128,30 @@ void tah_params_default(tah_params_t* p);
  * and its unused tail is zero.
  */
 tah_status_t tah_payload_bytes(int64_t tokens, int64_t hidden, const tah_params_t* p, size_t* out);
+
+/*
+ * tah_roundtrip without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same kernels and the same results as tah_roundtrip
+ * (every argument has the same meaning), with the library's own scratch in
+ * place of ws. That scratch is a file-scope device array of
+ * TAH_NOALLOC_SCRATCH_BYTES on each GPU the library runs on, created with the
+ * library's code object and held until the process ends; its address on a
+ * device is looked up once, at the first call with that device current. No
+ * call allocates or frees anything.
+ *   - A shape whose workspace (tah_workspace_bytes) exceeds
+ *     TAH_NOALLOC_SCRATCH_BYTES returns TAH_ERR_SCRATCH_LIMIT and enqueues
+ *     nothing (32 MiB holds about six million tiles of any allocation, e.g.
+ *     every 8192 x 8192 and 16384 x 5120 setting).
+ *   - Every call on one GPU shares that GPU's scratch, and each call rewrites
+ *     what it reads there before reading it (nothing needs to start at zero).
+ *     Calls that overlap on one GPU (concurrent streams, or threads) race on
+ *     it and give undefined results: serialize them.
+ */
+#define TAH_NOALLOC_SCRATCH_BYTES (32u << 20)
+tah_status_t tah_roundtrip_noalloc(const void* x, tah_dtype_t x_dtype, int64_t tokens, int64_t hidden,
+                                   const tah_params_t* p, void* payload, size_t payload_cap, void* y,
+                                   tah_dtype_t y_dtype, void* stream);
 
 /* Size in bytes of the device workspace the calls below need for this shape
  * (per-tile entropies, selection state and histograms, the tie candidates of

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(tah.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
-    assert tah.abi_version() == 3
+    assert tah.abi_version() == 4
 
 
 def test_params_default_is_paper_default():
@@ -82,8 +82,29 @@ def test_budget_reading_agrees_with_oracle_on_random_budgets(ref):
         assert tah.payload_bytes(32 * S, 64 * M, g) == ref.plan(32 * S, 64 * M, g)["total"], (budget, S, M)
 
 
+def test_noalloc_round_trip_rejects_shapes_beyond_its_scratch():
+    # checked on the host before any device call: no GPU is needed to see it
+    L = tah.lib()
+    v = ctypes.c_void_p
+    p = tah.TahParams(tile=64, bit_budget=3.8, candidates=(3, 4))
+    cp = tah._cparams(p)
+    big = (65536, 8192)
+    assert tah.workspace_bytes(*big, p) > tah.NOALLOC_SCRATCH_BYTES
+    need = tah.payload_bytes(*big, p)
+    assert L.tah_roundtrip_noalloc(v(16), 1, *big, ctypes.byref(cp), v(16), need, v(16), 1, v(0)) == 7
+    assert "scratch" in tah.status_string(7)
+    # the other argument errors come first, as in tah_roundtrip
+    assert L.tah_roundtrip_noalloc(v(0), 1, *big, ctypes.byref(cp), v(16), need, v(16), 1, v(0)) == 1
+    assert L.tah_roundtrip_noalloc(v(16), 1, *big, ctypes.byref(cp), v(16), need - 1, v(16), 1, v(0)) == 3
+    assert L.tah_roundtrip_noalloc(v(16), 1, 4, 100, ctypes.byref(cp), v(16), 1 << 20, v(16), 1, v(0)) == 1
+    # the workloads all fit
+    for name in list(synth.WORKLOADS) + list(synth.COVERAGE):
+        w = synth.workload(name)
+        assert tah.workspace_bytes(w.tokens, w.hidden, w.params) <= tah.NOALLOC_SCRATCH_BYTES, name
+
+
 def test_status_strings():
-    for c in range(7):
+    for c in range(8):
         assert tah.status_string(c)
 
 
