@@ -31,8 +31,10 @@
 //              selected tie; per-64-tile counts;
 //   k_table  - exclusive scan of those counts: b_hi tiles before each run of
 //              64 tiles, which locates every variable-width code block.
-// Samples of at most kSmallSelect keys skip k_hist and k_resolve: one
-// workgroup per sample (k_select_small) runs every digit pass in LDS.
+// Samples of at most kLdsSelect keys skip k_hist and k_resolve: one
+// workgroup per sample (k_select_lds) holds the keys in LDS, runs every digit
+// pass there and, when samples cover whole runs of 64 tiles, writes the width
+// map and block table itself.
 #include <type_traits>
 
 #include "tah_device.hpp"
@@ -291,7 +293,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
         const int leader = __ffsll((unsigned long long)wm) - 1;
         uint32_t base = 0;
         if (lane == leader) base = atomicAdd(&lcn, (uint32_t)__popcll(wm));
-        base = (uint32_t)__shfl((int)base, leader, 64);
+        base = (uint32_t)__builtin_amdgcn_readlane((int)base, leader);
         const uint32_t pos = base + lanes_below(wm);
         if (want && pos < (uint32_t)kCandPerChunk) lc[pos] = make_uint2(orderable(hv[i]), (uint32_t)u);
       }
@@ -303,7 +305,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
       const uint64_t wm = ballot(want);
       if (wm == 0) break;
       const int leader = __ffsll((unsigned long long)wm) - 1;
-      const uint32_t d0 = (uint32_t)__shfl((int)digit, leader, 64);
+      const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)digit, leader);
       const bool same = want && digit == d0;
       const uint64_t sm = ballot(same);
       if (lane == leader) atomicAdd(&lh[d0], (uint32_t)__popcll(sm));
@@ -406,33 +408,57 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
   if (tid == 0) a.st_out[s] = S;
 }
 
-// Small samples (N <= kSmallSelect keys): one workgroup per sample runs every
-// digit pass of the select, the three key digits and, when the threshold key
-// is shared by more tiles than remain to be selected, the tile-index digits,
-// over the sample's keys with an LDS histogram (lanes sharing a digit add
-// once), instead of one grid-wide launch per digit and k_resolve: the same
-// passes and apply_pass, so the same final state. The limit is one histogram
-// chunk, where the grid-wide passes also run one workgroup per sample; above
-// it they spread a sample over more workgroups, which pays for the launches
-// (at 32768 keys per sample and 4 samples this kernel took the 4096 x 2048
-// round trip from 47.8 to 78.2 us).
-constexpr int64_t kSmallSelect = kHistChunk;
-constexpr int kSmallThreads = 1024;
+// Samples of at most kLdsSelect keys: one workgroup per sample holds the
+// sample's order-preserving keys in LDS (dynamic shared memory, 4 bytes per
+// key) and runs every digit pass of the select there, the three key digits and, when the
+// threshold key is shared by more tiles than remain to be selected, the
+// tile-index digits: the same passes and apply_pass as the grid-wide form, so
+// the same final state, from one read of the keys and one launch instead of
+// one launch per digit, k_resolve, k_mark and k_table. The limit is one
+// histogram chunk of the grid-wide passes, which would run one workgroup per
+// sample as well: with 32768-key samples a workgroup per sample is
+// latency-bound (32 dependent rounds per thread and pass) and the 4096 x 2048
+// round trip took 76.1 us against 47.7 us grid-wide, with the keys in LDS as
+// when they were re-read from global memory in every pass (78.2 us).
+// When a sample covers whole runs of 64 quantization tiles, the same
+// workgroup then writes the sample's width-map words and block-table entries:
+// every sample has k upgraded allocation tiles, so the block table at the
+// sample's first run is s * k * kA, and the runs inside the sample add their
+// own counts. Otherwise it writes the final state for k_mark.
+constexpr int64_t kLdsSelect = 4096;
+constexpr int64_t kLdsMarkRuns = 4096;
+constexpr int kLdsThreads = 1024;
 
-struct SmallSelectArgs {
+struct LdsSelectArgs {
   const float* H;
   SampleState* st_out;
-  int64_t N, k;
+  uint32_t* bitmap;  // width map (payload or workspace), fused marking only
+  uint32_t* table;   // block table (payload or workspace), fused marking only
+  int64_t N, k, kA;
+  int32_t fused;
   int32_t npasses;
   SelectPass passes[kMaxPasses];
 };
 
-__global__ __launch_bounds__(kSmallThreads) void k_select_small(SmallSelectArgs a) {
+__global__ __launch_bounds__(kLdsThreads) void k_select_lds(LdsSelectArgs a) {
+  extern __shared__ uint32_t keys[];  // the sample's N keys
   __shared__ uint32_t lh[kBins];
   __shared__ SampleState ss;
-  const int tid = threadIdx.x, lane = tid & 63;
+  __shared__ uint32_t wsum[kLdsThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t s = blockIdx.x;
-  const float* h = a.H + s * a.N;
+  {
+    const float* h = a.H + s * a.N;
+    int64_t i = tid;
+    for (; i + 3 * kLdsThreads < a.N; i += 4 * kLdsThreads) {  // four loads in flight per thread
+      const float h0 = h[i], h1 = h[i + kLdsThreads], h2 = h[i + 2 * kLdsThreads], h3 = h[i + 3 * kLdsThreads];
+      keys[i] = orderable(h0);
+      keys[i + kLdsThreads] = orderable(h1);
+      keys[i + 2 * kLdsThreads] = orderable(h2);
+      keys[i + 3 * kLdsThreads] = orderable(h3);
+    }
+    for (; i < a.N; i += kLdsThreads) keys[i] = orderable(h[i]);
+  }
   if (tid == 0) {
     SampleState S;
     S.key = 0u;
@@ -444,18 +470,18 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(SmallSelectArgs 
   }
   for (int p = 0; p < a.npasses; ++p) {
     const SelectPass ps = a.passes[p];
-    for (int i = tid; i < kBins; i += kSmallThreads) lh[i] = 0u;
+    for (int i = tid; i < kBins; i += kLdsThreads) lh[i] = 0u;
     __syncthreads();
     const SampleState S = ss;
     if (ps.kind == 1 && S.tie_all) break;  // every tile with the threshold key is selected
     const int hs = ps.shift + ps.width;  // bits above the current digit
     const uint32_t dmask = (1u << ps.width) - 1u;
-    for (int64_t i0 = 0; i0 < a.N; i0 += kSmallThreads) {  // uniform trip count: ballots need every lane
+    for (int64_t i0 = 0; i0 < a.N; i0 += kLdsThreads) {  // uniform trip count: ballots need every lane
       const int64_t i = i0 + tid;
       bool want = false;
       uint32_t digit = 0;
       if (i < a.N) {
-        const uint32_t key = orderable(h[i]);
+        const uint32_t key = keys[i];
         if (ps.kind == 0) {
           want = hs >= 32 || (key >> hs) == (S.key >> hs);
           digit = (key >> ps.shift) & dmask;
@@ -465,12 +491,14 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(SmallSelectArgs 
           digit = (u >> ps.shift) & dmask;
         }
       }
+      // lanes with the same digit as the first remaining lane add together
+      // (twice: entropy keys cluster), the rest one by one
 #pragma unroll
       for (int round = 0; round < 2; ++round) {
         const uint64_t wm = ballot(want);
         if (wm == 0) break;
         const int leader = __ffsll((unsigned long long)wm) - 1;
-        const uint32_t d0 = (uint32_t)__shfl((int)digit, leader, 64);
+        const uint32_t d0 = (uint32_t)__builtin_amdgcn_readlane((int)digit, leader);
         const bool same = want && digit == d0;
         const uint64_t sm = ballot(same);
         if (lane == leader) atomicAdd(&lh[d0], (uint32_t)__popcll(sm));
@@ -486,7 +514,43 @@ __global__ __launch_bounds__(kSmallThreads) void k_select_small(SmallSelectArgs 
     __syncthreads();
   }
   __syncthreads();
-  if (tid == 0) a.st_out[s] = ss;
+  const SampleState S = ss;
+  if (!a.fused) {
+    if (tid == 0) a.st_out[s] = S;
+    return;
+  }
+  // width map and block table of the sample's runs of 64 quantization tiles;
+  // lh holds each run's count, chunk by chunk
+  const int64_t nb = a.N * a.kA / 64;  // runs in the sample
+  const int64_t b0 = s * nb;           // the sample's first run in the tensor
+  uint32_t carry = (uint32_t)s * (uint32_t)a.k * (uint32_t)a.kA;
+  for (int64_t c0 = 0; c0 < nb; c0 += kLdsThreads) {
+    const int64_t cn = nb - c0 < kLdsThreads ? nb - c0 : kLdsThreads;
+    for (int64_t b = c0 + wave; b < c0 + cn; b += kLdsThreads / 64) {
+      const int64_t u = (b * 64 + lane) / a.kA;  // the lane's allocation tile
+      const uint32_t key = keys[u];
+      const bool sel = key > S.key || (key == S.key && (uint32_t)u <= S.upos);
+      const uint64_t m = ballot(sel);
+      if (lane < 2) a.bitmap[2 * (b0 + b) + lane] = (uint32_t)(m >> (32 * lane));
+      if (lane == 0) lh[b - c0] = (uint32_t)__popcll(m);
+    }
+    __syncthreads();
+    // exclusive scan of the chunk's counts
+    const uint32_t v = tid < cn ? lh[tid] : 0u;
+    uint32_t incl = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t before = carry;
+    for (int w = 0; w < wave; ++w) before += wsum[w];
+    if (tid < cn) a.table[b0 + c0 + tid] = before + incl - v;
+    for (int w = 0; w < kLdsThreads / 64; ++w) carry += wsum[w];
+    __syncthreads();  // lh and wsum are reused by the next chunk
+  }
 }
 
 // ------------------------------------------------------------------ mark ----
@@ -607,17 +671,27 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   uint8_t* w = static_cast<uint8_t*>(ws);
   uint8_t* P = static_cast<uint8_t*>(payload);
   SampleState* states = reinterpret_cast<SampleState*>(w + pl.ws_state);
-  if (pl.N <= kSmallSelect) {
-    SmallSelectArgs sa;
+  if (pl.N <= kLdsSelect) {
+    LdsSelectArgs sa;
     sa.H = reinterpret_cast<const float*>(w + pl.ws_H);
     sa.st_out = states;
+    sa.bitmap = reinterpret_cast<uint32_t*>(P ? P + pl.off_bitmap : w + pl.ws_bitmap);
+    sa.table = reinterpret_cast<uint32_t*>(P ? P + pl.off_table : w + pl.ws_table);
     sa.N = pl.N;
     sa.k = pl.k;
+    sa.kA = pl.kA;
+    // samples of whole runs of 64 tiles, few enough runs for one workgroup
+    // (token-level allocation of a large tensor marks grid-wide)
+    sa.fused = ((pl.N * pl.kA) % 64 == 0 && pl.N * pl.kA / 64 <= kLdsMarkRuns) ? 1 : 0;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_select_lds),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)(4 * kLdsSelect));
+    if (attr != hipSuccess) return attr;
     sa.npasses = pl.npasses;
     for (int i = 0; i < kMaxPasses; ++i) sa.passes[i] = pl.passes[i];
-    hipLaunchKernelGGL(k_select_small, dim3((unsigned)pl.nsamples), dim3(kSmallThreads), 0, st, sa);
+    hipLaunchKernelGGL(k_select_lds, dim3((unsigned)pl.nsamples), dim3(kLdsThreads), (size_t)(4 * pl.N), st, sa);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || sa.fused) return e;
     return mark_and_table(pl, P, w, states, st);
   }
   uint32_t* hists = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
