@@ -423,6 +423,330 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
   }
 }
 
+// ---------------------------------------------------------------------------
+// Tiles of 128 channels. One lane per tile needs the whole tile in registers
+// (128 values), and staging a whole 64-tile group through LDS takes 33 KB of
+// fp32 rows: one wavefront per SIMD. This kernel stages the group in two
+// rounds of 32 tiles (17 KB), computes the statistics from registers, and
+// forms, packs and dequantizes the codes word by word instead of holding all
+// 128 codes, so two wavefronts fit on a SIMD.
+
+// Phase-A statistics of a tile held in registers (Eq. 3 and Eq. 1), the
+// order of tile_stats: m1, d (first index of m1), m2 (max over k != d), l1
+// left to right. NODE: widened bf16 values, whose low 16 bits are zero, so the
+// magnitude and (G-1-k) share one key as in tile_stats.
+template <int G, bool NODE>
+__device__ __forceinline__ void tile_stats_regs(const float (&v)[G], float& m1, float& m2, int& d, float& l1) {
+  if constexpr (NODE) {
+    uint32_t k1 = 0u, k2 = 0u;
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const uint32_t key = (__float_as_uint(v[k]) & 0x7fff0000u) | (uint32_t)(G - 1 - k);
+      s = s + fabsf(v[k]);
+      k2 = umed3(k2, key, k1);
+      k1 = max(k1, key);
+    }
+    m1 = __uint_as_float(k1 & 0xffff0000u);
+    m2 = __uint_as_float(k2 & 0xffff0000u);
+    d = G - 1 - (int)(k1 & 0xffffu);
+    l1 = s;
+  } else {
+    float a1 = fabsf(v[0]), a2 = 0.0f, s = 0.0f + fabsf(v[0]);
+    int dd = 0;
+#pragma unroll
+    for (int k = 1; k < G; ++k) {
+      const float av = fabsf(v[k]);
+      s = s + av;
+      const bool c = av > a1;
+      a2 = __builtin_amdgcn_fmed3f(a2, av, a1);
+      a1 = fmaxf(a1, av);
+      dd = c ? k : dd;
+    }
+    m1 = a1;
+    m2 = a2;
+    d = dd;
+    l1 = s;
+  }
+}
+
+// Codes of width B of a tile in registers, packed word by word as pack_codes
+// does (code k at stream bits [kB, kB + B), LSB first), each code dequantized
+// into v (OUT) as soon as its last bit is in a word; stores the code block at
+// dst (GUARD: unless it would end past the code section). The same code
+// values, words and dequantized values as quantize_tile.
+template <int G, int B, int OUT, bool GUARD>
+__device__ __forceinline__ void quant_pack(const EncArgs& a, float (&v)[G], float lo, float s, float inv,
+                                           int64_t code_off) {
+  constexpr int W = G * B / 32;
+  uint32_t w[W];
+  uint32_t carry = 0u;  // a code that began in the previous word
+#pragma unroll
+  for (int i = 0; i < W; ++i) {
+    const int lo_bit = 32 * i;
+    const int k0 = lo_bit / B;
+    const int k1 = (lo_bit + 31) / B;
+    uint32_t acc = 0u;
+#pragma unroll
+    for (int k = k0; k <= k1; ++k) {
+      const int n = (k < k1) ? B : (lo_bit + 32 - k1 * B);
+      const uint32_t q = (k * B < lo_bit) ? carry : __float_as_uint(__builtin_fmaf(v[k] - lo, inv, 0x1p23f));
+      acc = __builtin_amdgcn_alignbit(q, acc, (uint32_t)n);
+      if ((k + 1) * B <= lo_bit + 32) {
+        if constexpr (OUT != 0) v[k] = __builtin_fmaf(__uint_as_float(q) - 0x1p23f, s, lo);
+      } else {
+        carry = q;
+      }
+    }
+    w[i] = acc;
+  }
+  if (a.payload && (!GUARD || code_off + (int64_t)(G / 8) * B <= a.code_end)) {
+    static_assert(W % 4 == 0, "whole 16-byte stores");
+    uint4* dst = reinterpret_cast<uint4*>(a.payload + code_off);
+#pragma unroll
+    for (int i = 0; i < W / 4; ++i) dst[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  }
+}
+
+template <int G, int OUT, bool GUARD>
+__device__ __forceinline__ void quantize_stream(const EncArgs& a, float (&v)[G], int64_t t, int b, int64_t code_off) {
+  float lo = v[0], hv = v[0];
+#pragma unroll
+  for (int k = 1; k < G; ++k) {
+    lo = fminf(lo, v[k]);
+    hv = fmaxf(hv, v[k]);
+  }
+  lo = lo + 0.0f;
+  hv = hv + 0.0f;
+  float s, inv;
+  step_of(lo, hv, b, s, inv);
+  switch (b) {
+    case 1: quant_pack<G, 1, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
+    case 2: quant_pack<G, 2, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
+    case 3: quant_pack<G, 3, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
+    case 4: quant_pack<G, 4, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
+    case 5: quant_pack<G, 5, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
+    case 6: quant_pack<G, 6, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
+    case 7: quant_pack<G, 7, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
+    default: quant_pack<G, 8, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
+  }
+  if (a.payload) {
+    reinterpret_cast<uint16_t*>(a.payload + a.off_scale)[t] = (uint16_t)(__float_as_uint(s) >> 16);
+    reinterpret_cast<float*>(a.payload + a.off_zero)[t] = lo;
+  }
+}
+
+// n (<= 32) contiguous tiles of BYTES bytes between global memory and LDS rows
+// of STRIDE bytes, 16 bytes per lane and step, streamed (touched once per call),
+// eight steps in flight (the 128-value tiles of half the lanes stay in
+// registers meanwhile).
+template <int BYTES, int STRIDE>
+__device__ __forceinline__ void rows_in(const uint8_t* __restrict__ src, uint8_t* lds, int n) {
+  constexpr int CH = BYTES / 16, PER = 32 * CH / 64, BATCH = PER < 8 ? PER : 8;
+  const uint4* s = reinterpret_cast<const uint4*>(src);
+  const int nch = n * CH;
+  // addresses formed here at each call: hoisted out of the group loop, the
+  // 32 of them would not fit beside the tiles
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+#pragma unroll
+  for (int i0 = 0; i0 < PER; i0 += BATCH) {
+    uint4 buf[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {  // the batch's loads in flight before its first LDS write
+      const int c = tid + 64 * (i0 + i);
+      buf[i] = load_stream(&s[c < nch ? c : nch - 1]);
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int c = tid + 64 * (i0 + i);
+      if (c < nch) *reinterpret_cast<uint4*>(lds + (c / CH) * STRIDE + (c % CH) * 16) = buf[i];
+    }
+  }
+}
+template <int BYTES, int STRIDE>
+__device__ __forceinline__ void rows_out(const uint8_t* lds, uint8_t* __restrict__ dst, int n) {
+  constexpr int CH = BYTES / 16, PER = 32 * CH / 64, BATCH = PER < 8 ? PER : 8;
+  uint4* d = reinterpret_cast<uint4*>(dst);
+  const int nch = n * CH;
+  int tid = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid));
+#pragma unroll
+  for (int i0 = 0; i0 < PER; i0 += BATCH) {
+    uint4 buf[BATCH];
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int c = tid + 64 * (i0 + i);
+      const int cc = c < nch ? c : 0;
+      buf[i] = *reinterpret_cast<const uint4*>(lds + (cc / CH) * STRIDE + (cc % CH) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < BATCH; ++i) {
+      const int c = tid + 64 * (i0 + i);
+      if (c < nch) store_stream(&d[c], buf[i]);
+    }
+  }
+}
+
+// tile_entropy with the sum formed in chunks of CH elements: an empty asm on
+// the running sum between chunks keeps the scheduler from issuing the table
+// reads of the whole tile ahead of the sums (128 fp32 values and their
+// interpolation slopes would not fit next to the tile). Same fp32 order.
+template <int G, bool NODE, int CH>
+__device__ __forceinline__ float tile_entropy_chunked(const float (&v)[G], float l1, const float* lt) {
+  float S = 0.0f;
+#pragma unroll
+  for (int k0 = 0; k0 < G; k0 += CH) {
+#pragma unroll
+    for (int k = k0; k < k0 + CH; ++k) {
+      // log2_full reads only the exponent and mantissa bits: the same on v as
+      // on |v|, which then stays a source modifier of the fma
+      const float lg = NODE ? log2_node(v[k], lt) : log2_full(v[k], lt);
+      S = __builtin_fmaf(fabsf(v[k]), lg, S);
+    }
+    asm volatile("" : "+v"(S));
+  }
+  return l1 > 0.0f ? log2_full(l1, lt) - S / l1 : 0.0f;
+}
+
+template <typename TIn, int OUT, int MODE>
+__global__ __launch_bounds__(64, 2) void k_encode128(EncArgs a) {
+  constexpr int G = 128, NT = 64, RT = 32;  // tiles per group, tiles per LDS round
+  constexpr bool MIXED = MODE != 0;
+  constexpr bool NODE = Elem<TIn>::kBytes == 2;
+  using RI = TileRow<G, TIn>;
+  using TOut = typename std::conditional<OUT == 1, float, bf16_t>::type;
+  using RO = TileRow<G, TOut>;
+  constexpr int kStride = TileRow<G, float>::kStride;  // fp32 rows (the pivot swap goes through them)
+  __shared__ __attribute__((aligned(16))) uint8_t st[RT * kStride];
+  __shared__ __attribute__((aligned(16))) float lt[256];  // log2 tables of the entropy
+  const int lane = threadIdx.x;
+  const int half = lane >> 5;
+  uint8_t* row = st + (lane & 31) * kStride;  // this lane's row in its round
+
+  if (blockIdx.x == 0 && a.payload) {
+    if (lane < 32) reinterpret_cast<uint32_t*>(a.payload)[lane] = a.hdr.w[lane];
+    for (int r = 0; r < a.pads.n; ++r)
+      for (int i = lane; i < a.pads.len[r]; i += NT) a.payload[a.pads.off[r] + i] = 0;
+  }
+  if constexpr (MODE == 2) {
+    if (a.payload) {
+      const int64_t used = a.off_codes + (int64_t)(G / 8) * (int64_t)a.wtotal[0];
+      for (int64_t i = used + (int64_t)blockIdx.x * NT + lane; i < a.code_end; i += (int64_t)gridDim.x * NT)
+        a.payload[i] = 0;
+    }
+  }
+  if constexpr (!MIXED) load_log2_tab(lt);  // read after the first barrier of the loop
+
+  const int64_t ngroups = (a.tiles + NT - 1) / NT;
+  for (int64_t g = blockIdx.x; g < ngroups; g += gridDim.x) {
+    const int64_t t0 = g * NT;
+    const int n = (int)min<int64_t>(NT, a.tiles - t0);
+    const bool act = lane < n;
+    const int64_t t = t0 + lane;
+    float v[G];
+    // ---- in: two rounds of 32 tiles through LDS
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int nr = min(max(n - r * RT, 0), RT);
+      if (nr > 0) {
+        __syncthreads();  // the rows are free
+        rows_in<RI::kBytes, kStride>(a.x + (t0 + r * RT) * RI::kBytes, st, nr);
+        __syncthreads();
+        if (half == r && act) lds_read_tile<G, TIn>(row, v);
+      }
+    }
+
+    // ---- phase A: lane owns tile t0 + lane
+    int flag = 0, piv = 0, hi = 0, bw = 0;
+    if (act) {
+      float m1, m2, l1;
+      int d;
+      tile_stats_regs<G, NODE>(v, m1, m2, d, l1);
+      flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
+      piv = d;
+      if constexpr (!MIXED) {
+        a.H[t] = tile_entropy_chunked<G, NODE, 16>(v, l1, lt);  // Eq. (1)-(2)
+      } else if constexpr (MODE == 1) {
+        hi = (a.bitmap[t >> 5] >> (t & 31)) & 1u;
+      } else {
+        const uint32_t lv = (a.bitmap[t >> 4] >> (2 * (t & 15))) & 3u;
+        bw = (int)((a.cands >> (8 * lv)) & 255u);
+      }
+      if (a.payload) a.payload[a.off_side + t] = (uint8_t)(flag ? (0x80 | piv) : 0);
+    }
+    const uint64_t hmask = ballot(act && hi);
+    int64_t code_off = a.off_codes + t * a.sz_lo;
+    if constexpr (MODE == 2) {
+      uint32_t incl = (uint32_t)bw;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const uint32_t o = (uint32_t)__shfl_up((int)incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      code_off = a.off_codes + (int64_t)(G / 8) * ((int64_t)a.table[t0 >> 6] + (int64_t)(incl - (uint32_t)bw));
+    } else if constexpr (MIXED) {
+      const uint32_t hb = a.table[t0 >> 6] + lanes_below(hmask);
+      code_off += (int64_t)hb * (a.sz_hi - a.sz_lo);
+    } else {
+      if (lane == 0 && a.bitmap) {
+        const int64_t blk = t0 >> 6;
+        a.bitmap[2 * blk] = 0u;
+        a.bitmap[2 * blk + 1] = 0u;
+        a.table[blk] = 0u;
+      }
+    }
+    const int b = MODE == 2 ? bw : (hi ? a.b_hi : a.b_lo);
+
+    // ---- forward: P_d through the lane's fp32 row (a register array takes no
+    // per-lane index), then H of Eq. (4) in registers
+    const uint64_t fmask = ballot(act && flag);
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      if ((uint32_t)(fmask >> (32 * r)) != 0u) {
+        __syncthreads();
+        if (half == r && act && flag) {
+          lds_write_tile<G, float>(row, v);
+          const uint32_t x0 = lds_elem_bits<float>(row, 0), xd = lds_elem_bits<float>(row, piv);
+          lds_elem_set<float>(row, 0, xd);
+          lds_elem_set<float>(row, piv, x0);
+          lds_read_tile<G, float>(row, v);
+        }
+      }
+    }
+    if (act && flag) fwht<G>(v);
+
+    // ---- quantize, pack, dequantize
+    if (act) quantize_stream<G, OUT, MODE == 2>(a, v, t, b, code_off);
+
+    // ---- inverse and out: two rounds of 32 rebuilt tiles through LDS
+    if constexpr (OUT != 0) {
+      if (act && flag) {  // H^T = H, the 1/G
+        fwht<G>(v);
+#pragma unroll
+        for (int k = 0; k < G; ++k) v[k] = v[k] * (1.0f / G);
+      }
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int nr = min(max(n - r * RT, 0), RT);
+        if (nr > 0) {
+          __syncthreads();
+          if (half == r && act) {
+            lds_write_tile<G, TOut>(row, v);
+            if (flag) {  // element d takes y_0, element 0 takes y_d
+              const uint32_t y0 = lds_elem_bits<TOut>(row, 0), yd = lds_elem_bits<TOut>(row, piv);
+              lds_elem_set<TOut>(row, piv, y0);
+              lds_elem_set<TOut>(row, 0, yd);
+            }
+          }
+          __syncthreads();
+          rows_out<RO::kBytes, kStride>(st, a.y + (t0 + r * RT) * RO::kBytes, nr);
+        }
+      }
+    }
+  }
+}
+
 // Resident workgroups per CU of a kernel, from the runtime's occupancy query.
 template <typename K>
 static int wgs_per_cu(K kernel, int threads) {
@@ -443,8 +767,20 @@ static int cu_count() {
   return cus;
 }
 
+template <typename TIn, int OUT, int MODE>
+static hipError_t launch_128(const EncArgs& a, hipStream_t st) {
+  constexpr int NT = 64;
+  static const int per_cu = wgs_per_cu(k_encode128<TIn, OUT, MODE>, NT);
+  const int64_t ngroups = a.tiles > 0 ? (a.tiles + NT - 1) / NT : 1;
+  const int64_t resident = (int64_t)per_cu * cu_count();
+  const int64_t nwg = ngroups < resident ? ngroups : resident;
+  hipLaunchKernelGGL((k_encode128<TIn, OUT, MODE>), dim3((unsigned)nwg), dim3(NT), 0, st, a);
+  return hipGetLastError();
+}
+
 template <int G, typename TIn, int OUT, int MODE>
 static hipError_t launch_one(const EncArgs& a, hipStream_t st) {
+  if constexpr (G == 128) return launch_128<TIn, OUT, MODE>(a, st);
   constexpr int NT = 64;
   static const int per_cu = wgs_per_cu(k_encode<G, TIn, OUT, MODE>, NT);
   const int64_t ngroups = a.tiles > 0 ? (a.tiles + NT - 1) / NT : 1;

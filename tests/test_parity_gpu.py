@@ -471,22 +471,25 @@ def test_random_configurations(seed):
                              oracle.plan(tokens, hidden, p), f"random config {seed} bf16 out")
 
 
-@pytest.mark.parametrize("name", ["c3_16384x4096_bf16_g64", "c4_16384x5120_f32_g128", "c5_8192x8192_bf16_g64",
-                                  "x2_c5_budget3p8", "x5b_c5_greedy"])
-def test_full_size_other_seed(name):
-    """The large workloads at full size with another seed: payload and fused
+FULL_SIZE_SEEDS = [(n, sd) for n in ("c3_16384x4096_bf16_g64", "c4_16384x5120_f32_g128", "c5_8192x8192_bf16_g64")
+                   for sd in (1, 2, 3, 4)] + [("x2_c5_budget3p8", 1), ("x5b_c5_greedy", 1)]
+
+
+@pytest.mark.parametrize("name,seed", FULL_SIZE_SEEDS)
+def test_full_size_other_seed(name, seed):
+    """The large workloads at full size with other seeds: payload and fused
     round trip (the benchmarked launch for c5) against the oracle."""
     w = synth.workload(name)
-    x = synth.generate(name, 1)
-    say(f"[seed1] {name}: oracle")
+    x = synth.generate(name, seed)
+    say(f"[seed{seed}] {name}: oracle")
     R = oracle.encode(x, w.params)
     pl = oracle.plan(w.tokens, w.hidden, w.params)
     y_dt, o_dt = (torch.bfloat16, oracle.BF16) if w.dtype == synth.BF16 else (torch.float32, oracle.F32)
     y_ref = oracle.decode(R, w.tokens, w.hidden, w.params, o_dt)
-    say(f"[seed1] {name}: GPU round trip")
+    say(f"[seed{seed}] {name}: GPU round trip")
     y, P = tah.roundtrip(to_dev(x), w.params, y_dt)
-    assert_payload_equal(to_host(P), R, pl, f"{name} seed 1")
-    assert_decoded_equal(to_host(y), y_ref, R, pl, f"{name} seed 1")
+    assert_payload_equal(to_host(P), R, pl, f"{name} seed {seed}")
+    assert_decoded_equal(to_host(y), y_ref, R, pl, f"{name} seed {seed}")
 
 
 @pytest.mark.parametrize("n_tied", [200, 6000])
