@@ -186,8 +186,10 @@ def roundtrip_leg_fn(torch, tah, synth, dev, stream_h, n_sets, args):
         wsl = torch.empty(cl.workspace_bytes, dtype=torch.uint8, device=dev)
         xb = x_sets[0].numel() * x_sets[0].element_size()
         nbytes = 2 * xb + cl.payload_bytes
+        # extra legs: at least 50 untimed and 100 timed launches (a freshly allocated
+        # buffer set of up to 2 GB runs its first launches slower)
         l_ms, l_mean, _, _ = time_launches(torch, lambda i: cl.roundtrip(x_sets[i], pl_[i], yl[i], wsl, stream_h),
-                                           n_sets, args.steps, args.warmup)
+                                           n_sets, max(args.steps, 100), max(args.warmup, 50))
         del yl, pl_, wsl
         gbps = nbytes / (l_mean * 1e-3) / 1e9
         return {"shape": f"{wl.tokens}x{wl.hidden} {'bf16' if wl.dtype == synth.BF16 else 'fp32'} tile {prm.tile}",
