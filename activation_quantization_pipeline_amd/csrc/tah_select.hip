@@ -215,9 +215,10 @@ __device__ __forceinline__ SampleState apply_pass(SampleState S, const uint32_t*
     }
     digit = (uint32_t)(ps.kind == 0 ? (kBins - 1 - ord) : ord);
   }
-  digit = (uint32_t)__shfl((int)digit, src, 64);
-  cnt = (uint32_t)__shfl((int)cnt, src, 64);
-  before = (int64_t)__shfl((long long)before, src, 64);
+  digit = (uint32_t)__builtin_amdgcn_readlane((int)digit, src);
+  cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
+  before = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(before >> 32), src) << 32) |
+                     (uint32_t)__builtin_amdgcn_readlane((int)before, src));
   S.r -= before;
   if (ps.kind == 0) {
     S.key |= digit << ps.shift;
@@ -240,6 +241,13 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
   const int64_t s = blockIdx.x / a.chunks_per_sample;
   const int64_t c = blockIdx.x % a.chunks_per_sample;
   const int64_t u0 = c * kHistChunk;
+  // the keys first: their loads are in flight while the previous pass is applied
+  float hv[kHistPerThread];
+#pragma unroll
+  for (int i = 0; i < kHistPerThread; ++i) {
+    const int64_t u = u0 + i * kHistThreads + tid;
+    hv[i] = u < a.N ? a.H[s * a.N + u] : 0.0f;
+  }
   // the next pass's histogram of this sample, cleared in slices by the sample's blocks
   {
     const int64_t per = (kBins + a.chunks_per_sample - 1) / a.chunks_per_sample;
@@ -269,12 +277,6 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
   const SampleState S = ss;
   const int hs = a.pass.shift + a.pass.width;  // bits above the current digit
   const uint32_t dmask = (1u << a.pass.width) - 1u;
-  float hv[kHistPerThread];  // all loads in flight before the first use
-#pragma unroll
-  for (int i = 0; i < kHistPerThread; ++i) {
-    const int64_t u = u0 + i * kHistThreads + tid;
-    hv[i] = u < a.N ? a.H[s * a.N + u] : 0.0f;
-  }
 #pragma unroll
   for (int i = 0; i < kHistPerThread; ++i) {
     const int64_t u = u0 + i * kHistThreads + tid;
