@@ -209,6 +209,8 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   w = align256(w + 4 * o->cand_stride * (sel ? o->nsamples : 0));
   o->ws_wtotal = w;  // greedy: the sum of all code widths (the used part of the code section)
   w = align256(w + (o->mode == 2 ? 4 : 0));
+  o->ws_side = w;  // mixed layouts without a payload: the side bytes of the statistics pass
+  w = align256(w + (mixed ? o->tiles : 0));
   o->ws_total = w;
 
   // radix-select passes: three digits of the 32-bit entropy key, then enough
@@ -308,13 +310,15 @@ static tah_status_t launch_encode_path(Plan& pl, const void* x, tah_dtype_t x_dt
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* w = static_cast<uint8_t*>(ws);
   const int mode = pl.tiles > 0 ? pl.mode : 0;
+  // mixed layouts: the statistics pass also writes the side bytes (Eq. 3)
+  uint8_t* side = payload ? static_cast<uint8_t*>(payload) + pl.off_side : w + pl.ws_side;
   if (mode == 1) {
-    hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, true, st);
+    hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, true, side, st);
     if (e != hipSuccess) return hip_status(e);
     e = launch_select(pl, payload, ws, st);
     if (e != hipSuccess) return hip_status(e);
   } else if (mode == 2) {
-    hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, pl.glevel < 0, st);
+    hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, pl.glevel < 0, side, st);
     if (e != hipSuccess) return hip_status(e);
     e = launch_greedy(pl, payload, ws, st);
     if (e != hipSuccess) return hip_status(e);
@@ -322,7 +326,7 @@ static tah_status_t launch_encode_path(Plan& pl, const void* x, tah_dtype_t x_dt
     // no selection, but the workspace still receives the allocation-tile
     // entropies; the encoder's own per-quantization-tile entropies then go to
     // the (by then consumed) partial-sum area
-    hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, false, st);
+    hipError_t e = launch_stats(pl, x, reinterpret_cast<float*>(w + pl.ws_H), ws, false, nullptr, st);
     if (e != hipSuccess) return hip_status(e);
   }
   return hip_status(launch_encode(pl, x, payload, want_y ? y : nullptr, y_dtype, ws, st, mode));
@@ -474,7 +478,7 @@ tah_status_t tah_tile_entropy(const void* x, tah_dtype_t x_dtype, int64_t tokens
   if (ws_cap < (size_t)pl.ws_total) return TAH_ERR_BUFFER_TOO_SMALL;
   if (pl.tiles == 0) return TAH_OK;
   pl.x_dtype = x_dtype;
-  return hip_status(launch_stats(pl, x, h, ws, false, static_cast<hipStream_t>(stream)));
+  return hip_status(launch_stats(pl, x, h, ws, false, nullptr, static_cast<hipStream_t>(stream)));
 }
 
 static bool naive_ok(int64_t n, int bits, float c) {

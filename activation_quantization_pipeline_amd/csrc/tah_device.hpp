@@ -237,6 +237,50 @@ __device__ __forceinline__ void fwht16(float (&y)[V], int r) {
   }
 }
 
+__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
+  return max(min(a, b), min(max(a, b), c));
+}
+
+// Statistics of a tile held in registers (Eq. 3 and Eq. 1): m1 = max |a_k|,
+// d = the first index holding it, m2 = max |a_k| over k != d, l1 = sum |a_k|
+// left to right from 0. NODE: widened bf16 values, whose low 16 bits are zero,
+// so the magnitude bits and (G-1-k) share one 32-bit key and unsigned max /
+// median give the top two magnitudes and the lowest index among ties.
+template <int G, bool NODE>
+__device__ __forceinline__ void tile_stats_regs(const float (&v)[G], float& m1, float& m2, int& d, float& l1) {
+  if constexpr (NODE) {
+    uint32_t k1 = 0u, k2 = 0u;
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < G; ++k) {
+      const uint32_t key = (__float_as_uint(v[k]) & 0x7fff0000u) | (uint32_t)(G - 1 - k);
+      s = s + fabsf(v[k]);
+      k2 = umed3(k2, key, k1);
+      k1 = max(k1, key);
+    }
+    m1 = __uint_as_float(k1 & 0xffff0000u);
+    m2 = __uint_as_float(k2 & 0xffff0000u);
+    d = G - 1 - (int)(k1 & 0xffffu);
+    l1 = s;
+  } else {
+    float a1 = fabsf(v[0]), a2 = 0.0f, s = 0.0f + fabsf(v[0]);
+    int dd = 0;
+#pragma unroll
+    for (int k = 1; k < G; ++k) {
+      const float av = fabsf(v[k]);
+      s = s + av;
+      const bool c = av > a1;
+      a2 = __builtin_amdgcn_fmed3f(a2, av, a1);
+      a1 = fmaxf(a1, av);
+      dd = c ? k : dd;
+    }
+    m1 = a1;
+    m2 = a2;
+    d = dd;
+    l1 = s;
+  }
+}
+
 // Number of lanes below this one whose bit is set in mask.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));

@@ -33,6 +33,7 @@ struct EncArgs {
   uint32_t* table;   // block table (payload or workspace)
   uint32_t* bitmap;  // width map (payload or workspace)
   float* H;          // per-tile entropies (workspace)
+  const uint8_t* side_in;  // mixed layouts: the side bytes the statistics pass wrote
   int64_t tiles;
   int64_t off_side, off_scale, off_zero, off_codes;
   int32_t b_lo, b_hi, sz_lo, sz_hi;
@@ -89,9 +90,6 @@ __device__ __forceinline__ void store_codes_b(int b, const uint32_t (&mq)[G], ui
   }
 }
 
-__device__ __forceinline__ uint32_t umed3(uint32_t a, uint32_t b, uint32_t c) {
-  return max(min(a, b), min(max(a, b), c));
-}
 
 // Phase-A statistics of one tile read from LDS (Eq. 3 and Eq. 1):
 // m1 = max |a_k|, d = first index holding m1, m2 = max |a_k| over k != d,
@@ -306,21 +304,28 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
     int flag = 0, piv = 0, hi = 0, bw = 0;
     float v[G];
     if (act) {
-      float m1, m2, l1;
-      int d;
-      tile_stats<G, TIn>(xs + lane * RI::kStride, v, m1, m2, d, l1);
-      flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
-      piv = d;
       if constexpr (!MIXED) {
+        float m1, m2, l1;
+        int d;
+        tile_stats<G, TIn>(xs + lane * RI::kStride, v, m1, m2, d, l1);
+        flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
+        piv = d;
         a.H[t] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);  // Eq. (1)-(2)
-      } else if constexpr (MODE == 1) {
-        hi = (a.bitmap[t >> 5] >> (t & 31)) & 1u;
+        // side byte: the flag, and the pivot of a transformed tile (0 for the others)
+        if (a.payload) a.payload[a.off_side + t] = (uint8_t)(flag ? (0x80 | piv) : 0);
       } else {
-        const uint32_t lv = (a.bitmap[t >> 4] >> (2 * (t & 15))) & 3u;
-        bw = (int)((a.cands >> (8 * lv)) & 255u);
+        // the statistics pass already took Eq. (3) and wrote the side byte
+        const uint32_t sb = a.side_in[t];
+        flag = (int)(sb >> 7);
+        piv = (int)(sb & 127u);
+        lds_read_tile<G, TIn>(xs + lane * RI::kStride, v);
+        if constexpr (MODE == 1) {
+          hi = (a.bitmap[t >> 5] >> (t & 31)) & 1u;
+        } else {
+          const uint32_t lv = (a.bitmap[t >> 4] >> (2 * (t & 15))) & 3u;
+          bw = (int)((a.cands >> (8 * lv)) & 255u);
+        }
       }
-      // side byte: the flag, and the pivot of a transformed tile (0 for the others)
-      if (a.payload) a.payload[a.off_side + t] = (uint8_t)(flag ? (0x80 | piv) : 0);
     }
 
     // Code-block offsets: tile t starts at t*sz_lo + (b_hi tiles before t)*(sz_hi - sz_lo);
@@ -430,45 +435,6 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
 // rounds of 32 tiles (17 KB), computes the statistics from registers, and
 // forms, packs and dequantizes the codes word by word instead of holding all
 // 128 codes, so two wavefronts fit on a SIMD.
-
-// Phase-A statistics of a tile held in registers (Eq. 3 and Eq. 1), the
-// order of tile_stats: m1, d (first index of m1), m2 (max over k != d), l1
-// left to right. NODE: widened bf16 values, whose low 16 bits are zero, so the
-// magnitude and (G-1-k) share one key as in tile_stats.
-template <int G, bool NODE>
-__device__ __forceinline__ void tile_stats_regs(const float (&v)[G], float& m1, float& m2, int& d, float& l1) {
-  if constexpr (NODE) {
-    uint32_t k1 = 0u, k2 = 0u;
-    float s = 0.0f;
-#pragma unroll
-    for (int k = 0; k < G; ++k) {
-      const uint32_t key = (__float_as_uint(v[k]) & 0x7fff0000u) | (uint32_t)(G - 1 - k);
-      s = s + fabsf(v[k]);
-      k2 = umed3(k2, key, k1);
-      k1 = max(k1, key);
-    }
-    m1 = __uint_as_float(k1 & 0xffff0000u);
-    m2 = __uint_as_float(k2 & 0xffff0000u);
-    d = G - 1 - (int)(k1 & 0xffffu);
-    l1 = s;
-  } else {
-    float a1 = fabsf(v[0]), a2 = 0.0f, s = 0.0f + fabsf(v[0]);
-    int dd = 0;
-#pragma unroll
-    for (int k = 1; k < G; ++k) {
-      const float av = fabsf(v[k]);
-      s = s + av;
-      const bool c = av > a1;
-      a2 = __builtin_amdgcn_fmed3f(a2, av, a1);
-      a1 = fmaxf(a1, av);
-      dd = c ? k : dd;
-    }
-    m1 = a1;
-    m2 = a2;
-    d = dd;
-    l1 = s;
-  }
-}
 
 // Codes of width B of a tile in registers, packed word by word as pack_codes
 // does (code k at stream bits [kB, kB + B), LSB first), each code dequantized
@@ -660,20 +626,26 @@ __global__ __launch_bounds__(64, 2) void k_encode128(EncArgs a) {
     // ---- phase A: lane owns tile t0 + lane
     int flag = 0, piv = 0, hi = 0, bw = 0;
     if (act) {
-      float m1, m2, l1;
-      int d;
-      tile_stats_regs<G, NODE>(v, m1, m2, d, l1);
-      flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
-      piv = d;
       if constexpr (!MIXED) {
+        float m1, m2, l1;
+        int d;
+        tile_stats_regs<G, NODE>(v, m1, m2, d, l1);
+        flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
+        piv = d;
         a.H[t] = tile_entropy_chunked<G, NODE, 16>(v, l1, lt);  // Eq. (1)-(2)
-      } else if constexpr (MODE == 1) {
-        hi = (a.bitmap[t >> 5] >> (t & 31)) & 1u;
+        if (a.payload) a.payload[a.off_side + t] = (uint8_t)(flag ? (0x80 | piv) : 0);
       } else {
-        const uint32_t lv = (a.bitmap[t >> 4] >> (2 * (t & 15))) & 3u;
-        bw = (int)((a.cands >> (8 * lv)) & 255u);
+        // the statistics pass already took Eq. (3) and wrote the side byte
+        const uint32_t sb = a.side_in[t];
+        flag = (int)(sb >> 7);
+        piv = (int)(sb & 127u);
+        if constexpr (MODE == 1) {
+          hi = (a.bitmap[t >> 5] >> (t & 31)) & 1u;
+        } else {
+          const uint32_t lv = (a.bitmap[t >> 4] >> (2 * (t & 15))) & 3u;
+          bw = (int)((a.cands >> (8 * lv)) & 255u);
+        }
       }
-      if (a.payload) a.payload[a.off_side + t] = (uint8_t)(flag ? (0x80 | piv) : 0);
     }
     const uint64_t hmask = ballot(act && hi);
     int64_t code_off = a.off_codes + t * a.sz_lo;
@@ -825,6 +797,7 @@ hipError_t launch_encode(const Plan& pl, const void* x, void* payload, void* y, 
   // the uniform-width kernel writes quantization-tile entropies: the entropy
   // area when allocation tiles are quantization tiles, else the sum area
   a.H = reinterpret_cast<float*>(w + (pl.kA > 1 ? pl.ws_LS : pl.ws_H));
+  a.side_in = payload ? a.payload + pl.off_side : w + pl.ws_side;
   a.tiles = pl.tiles;
   a.off_side = pl.off_side;
   a.off_scale = pl.off_scale;

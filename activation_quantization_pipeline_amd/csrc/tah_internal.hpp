@@ -57,7 +57,8 @@ struct Plan {
   // payload layout
   int64_t off_table, off_bitmap, off_side, off_scale, off_zero, off_codes, code_bytes, total;
   // workspace layout
-  int64_t ws_status, ws_state, ws_hist, ws_H, ws_LS, ws_blockcnt, ws_table, ws_bitmap, ws_cand, ws_wtotal, ws_total;
+  int64_t ws_status, ws_state, ws_hist, ws_H, ws_LS, ws_blockcnt, ws_table, ws_bitmap, ws_cand, ws_wtotal, ws_side,
+      ws_total;
   int64_t ncand, cand_stride;  // capacity of a sample's candidate list; its uint32 words
   int32_t npasses;
   SelectPass passes[kMaxPasses];
@@ -93,8 +94,10 @@ struct PadRanges {
 // mode: the width layout (Plan::mode), 0 when the tensor is empty
 hipError_t launch_encode(const Plan& pl, const void* x, void* payload, void* y, int y_dtype, void* ws,
                          hipStream_t st, int mode);
-// Entropy of every allocation tile into h_out (pl.atiles values).
-hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, bool init_select, hipStream_t st);
+// Entropy of every allocation tile into h_out (pl.atiles values); side (may
+// be null) receives every quantization tile's side byte (Eq. 3).
+hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, bool init_select, uint8_t* side,
+                        hipStream_t st);
 hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st);
 // Greedy allocator (tah_greedy.hip): levels, width sums, block table.
 hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st);

@@ -54,6 +54,8 @@ struct StatsArgs {
   float* h;     // entropy per tile (allocation tile = quantization tile)
   float2* ls;   // (L, S) per tile (allocation tile of several quantization tiles)
   uint32_t* hist;
+  uint8_t* side;  // Eq. (3) per tile as the payload's side byte (mixed layouts), or null
+  float tau;
   int64_t tiles, hist_words;
   int32_t init;
 };
@@ -63,7 +65,10 @@ constexpr int stats_tiles_per_wg() {
   return TileRow<G, TIn>::kBytes <= 128 ? 256 : (TileRow<G, TIn>::kBytes <= 256 ? 128 : 64);
 }
 
-template <int G, typename TIn, bool SUMS>
+// SIDE: also the outlier test of Eq. (3), m1 > tau (m2 + rho), and the side
+// byte (bit 7 the flag, bits 0-6 the pivot of a transformed tile), which the
+// mixed-width encoder then reads instead of finding the top two magnitudes.
+template <int G, typename TIn, bool SUMS, bool SIDE>
 __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsArgs a) {
   constexpr int NT = stats_tiles_per_wg<G, TIn>();
   using RI = TileRow<G, TIn>;
@@ -84,8 +89,16 @@ __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsA
     float v[G];
     lds_read_tile<G, TIn>(xs + tid * RI::kStride, v);
     float l1 = 0.0f;
+    if constexpr (SIDE) {
+      float m1, m2;
+      int d;
+      tile_stats_regs<G, Elem<TIn>::kBytes == 2>(v, m1, m2, d, l1);
+      const bool flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
+      a.side[t0 + tid] = (uint8_t)(flag ? (0x80 | d) : 0);
+    } else {
 #pragma unroll
-    for (int k = 0; k < G; ++k) l1 = l1 + fabsf(v[k]);
+      for (int k = 0; k < G; ++k) l1 = l1 + fabsf(v[k]);
+    }
     if constexpr (SUMS)
       a.ls[t0 + tid] = make_float2(l1, tile_logsum<G, Elem<TIn>::kBytes == 2>(v, lt));
     else
@@ -119,18 +132,22 @@ template <int G, typename TIn>
 static hipError_t launch_stats_t(const StatsArgs& a, bool sums, hipStream_t st) {
   constexpr int NT = stats_tiles_per_wg<G, TIn>();
   const int64_t nwg = a.tiles > 0 ? (a.tiles + NT - 1) / NT : 1;
-  if (sums)
-    hipLaunchKernelGGL((k_stats<G, TIn, true>), dim3((unsigned)nwg), dim3(NT), 0, st, a);
-  else
-    hipLaunchKernelGGL((k_stats<G, TIn, false>), dim3((unsigned)nwg), dim3(NT), 0, st, a);
+  const dim3 grid((unsigned)nwg), block(NT);
+  if (sums && a.side) hipLaunchKernelGGL((k_stats<G, TIn, true, true>), grid, block, 0, st, a);
+  else if (sums) hipLaunchKernelGGL((k_stats<G, TIn, true, false>), grid, block, 0, st, a);
+  else if (a.side) hipLaunchKernelGGL((k_stats<G, TIn, false, true>), grid, block, 0, st, a);
+  else hipLaunchKernelGGL((k_stats<G, TIn, false, false>), grid, block, 0, st, a);
   return hipGetLastError();
 }
 
-hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, bool init_select, hipStream_t st) {
+hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, bool init_select, uint8_t* side,
+                        hipStream_t st) {
   uint8_t* w = static_cast<uint8_t*>(ws);
   StatsArgs a;
   a.x = static_cast<const uint8_t*>(x);
   a.h = h_out;
+  a.side = side;
+  a.tau = pl.tau;
   a.ls = reinterpret_cast<float2*>(w + pl.ws_LS);
   a.hist = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
   a.tiles = pl.tiles;
