@@ -309,7 +309,11 @@ static tah_status_t launch_encode_path(Plan& pl, const void* x, tah_dtype_t x_dt
   pl.x_dtype = x_dtype;
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* w = static_cast<uint8_t*>(ws);
-  const int mode = pl.tiles > 0 ? pl.mode : 0;
+  // greedy with every tile at one level and allocation tiles of one
+  // quantization tile: no select, and the uniform encoder writes the any-width
+  // layout itself (its width map and block table are closed-form)
+  const bool one_level = pl.mode == 2 && pl.glevel >= 0 && pl.kA == 1;
+  const int mode = (pl.tiles > 0 && !one_level) ? pl.mode : 0;
   // mixed layouts: the statistics pass also writes the side bytes (Eq. 3)
   uint8_t* side = payload ? static_cast<uint8_t*>(payload) + pl.off_side : w + pl.ws_side;
   if (mode == 1) {

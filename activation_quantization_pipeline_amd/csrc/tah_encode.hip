@@ -34,6 +34,10 @@ struct EncArgs {
   uint32_t* bitmap;  // width map (payload or workspace)
   float* H;          // per-tile entropies (workspace)
   const uint8_t* side_in;  // mixed layouts: the side bytes the statistics pass wrote
+  // one width everywhere: the width map's words per 64 tiles, their value, and
+  // the block table's step per 64 tiles
+  int32_t map_words;
+  uint32_t map_fill, table_step;
   int64_t tiles;
   int64_t off_side, off_scale, off_zero, off_codes;
   int32_t b_lo, b_hi, sz_lo, sz_hi;
@@ -347,11 +351,18 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
       code_off += (int64_t)hb * (a.sz_hi - a.sz_lo);
     } else {
       // uniform allocation: no tile has b_hi
-      if (lane == 0 && a.bitmap) {
+      if (lane < a.map_words && a.bitmap) {
+        // one width everywhere: the width map's words are constant and the
+        // block table is closed-form (no b_hi tile in the two-width layout;
+        // 64 times the width per run in the any-width layout)
         const int64_t blk = t0 >> 6;
-        a.bitmap[2 * blk] = 0u;
-        a.bitmap[2 * blk + 1] = 0u;
-        a.table[blk] = 0u;
+        // entries past the last tile stay zero
+        const int per_word = 64 / a.map_words;
+        const int64_t left = a.tiles - t0 - (int64_t)lane * per_word;
+        uint32_t fill = a.map_fill;
+        if (left < per_word) fill = left <= 0 ? 0u : fill & ((1u << (left * (a.map_words >> 1))) - 1u);
+        a.bitmap[a.map_words * blk + lane] = fill;
+        if (lane == 0) a.table[blk] = (uint32_t)blk * a.table_step;
       }
     }
 
@@ -661,11 +672,18 @@ __global__ __launch_bounds__(64, 2) void k_encode128(EncArgs a) {
       const uint32_t hb = a.table[t0 >> 6] + lanes_below(hmask);
       code_off += (int64_t)hb * (a.sz_hi - a.sz_lo);
     } else {
-      if (lane == 0 && a.bitmap) {
+      if (lane < a.map_words && a.bitmap) {
+        // one width everywhere: the width map's words are constant and the
+        // block table is closed-form (no b_hi tile in the two-width layout;
+        // 64 times the width per run in the any-width layout)
         const int64_t blk = t0 >> 6;
-        a.bitmap[2 * blk] = 0u;
-        a.bitmap[2 * blk + 1] = 0u;
-        a.table[blk] = 0u;
+        // entries past the last tile stay zero
+        const int per_word = 64 / a.map_words;
+        const int64_t left = a.tiles - t0 - (int64_t)lane * per_word;
+        uint32_t fill = a.map_fill;
+        if (left < per_word) fill = left <= 0 ? 0u : fill & ((1u << (left * (a.map_words >> 1))) - 1u);
+        a.bitmap[a.map_words * blk + lane] = fill;
+        if (lane == 0) a.table[blk] = (uint32_t)blk * a.table_step;
       }
     }
     const int b = MODE == 2 ? bw : (hi ? a.b_hi : a.b_lo);
@@ -805,8 +823,20 @@ hipError_t launch_encode(const Plan& pl, const void* x, void* payload, void* y, 
   a.off_codes = pl.off_codes;
   a.b_lo = pl.b_lo;
   a.b_hi = pl.b_hi;
-  a.sz_lo = pl.G * pl.b_lo / 8;
-  a.sz_hi = pl.G * pl.b_hi / 8;
+  a.map_words = 2;  // two-width layout: 1 bit per tile, none at b_hi
+  a.map_fill = 0u;
+  a.table_step = 0u;
+  if (pl.allocator == TAH_ALLOC_GREEDY && mode == 0) {
+    // any-width layout with every tile at level glevel: 2-bit map entries all
+    // glevel, and the block table's running width sums grow by 64 widths a run
+    const int c = pl.candidates[pl.glevel];
+    a.b_lo = a.b_hi = c;
+    a.map_words = 4;
+    a.map_fill = (uint32_t)pl.glevel * 0x55555555u;
+    a.table_step = 64u * (uint32_t)c;
+  }
+  a.sz_lo = pl.G * a.b_lo / 8;
+  a.sz_hi = pl.G * a.b_hi / 8;
   a.cands = 0;
   for (int i = 0; i < pl.n_candidates; ++i) a.cands |= (uint32_t)pl.candidates[i] << (8 * i);
   a.wtotal = reinterpret_cast<const uint32_t*>(w + pl.ws_wtotal);

@@ -52,6 +52,19 @@ def test_degenerate_budgets(budget, cands, want):
 
 
 @pytest.mark.parametrize("tile", [32, 64, 128])
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+def test_one_level_ragged(tile, dtype):
+    """Every tile at one level (nothing fits, everything fits, one candidate)
+    on tile counts that end inside a 64-tile run: the level map's entries past
+    the last tile stay zero, the width-sum table is 64 widths a run."""
+    for tokens, mult in ((1, 5), (7, 9), (65, 3)):
+        x = synth.random_tensor(tokens, tile * mult, dtype, 11 + tokens, n_out=2, mult=25)
+        for budget, cands in ((2.0, (2, 3, 4, 8)), (8.0, (2, 3, 4, 8)), (4.0, (4,)), (9.0, (1, 5))):
+            run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=budget, candidates=cands, tau=2.0,
+                          allocator=GREEDY), f"greedy one level t{tokens} m{mult} {budget} {cands}")
+
+
+@pytest.mark.parametrize("tile", [32, 64, 128])
 def test_every_key_ties(tile):
     """A tensor of identical tiles: every entropy is equal, so every upgrade of
     a level ties and the upgrade index alone orders them (the lower tile first)."""
