@@ -211,6 +211,9 @@ static tah_status_t make_plan(int64_t tokens, int64_t hidden, const tah_params_t
   w = align256(w + (o->mode == 2 ? 4 : 0));
   o->ws_side = w;  // mixed layouts without a payload: the side bytes of the statistics pass
   w = align256(w + (mixed ? o->tiles : 0));
+  // top-p% over quantization tiles in samples of whole runs, selected grid-wide
+  o->fold = (o->mode == 1 && o->kA == 1 && o->N % 64 == 0 && o->N > kLdsSelect && o->N / 64 <= kFoldMaxRuns)
+                ? 1 : 0;
   o->ws_total = w;
 
   // radix-select passes: three digits of the 32-bit entropy key, then enough

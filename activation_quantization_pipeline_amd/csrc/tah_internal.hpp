@@ -19,6 +19,14 @@ constexpr int kMaxPasses = 6;
 // and kMaxCand per sample.
 constexpr int kCandPerChunk = 512;
 constexpr int64_t kMaxCand = 4096;
+// Keys per workgroup of the grid-wide select passes (64 runs of 64 tiles), and
+// the largest samples selected by one workgroup with the keys in LDS.
+constexpr int64_t kHistChunk = 4096;
+constexpr int64_t kLdsSelect = 4096;
+// Two-width layouts whose width map and block table the select's last two
+// launches write (no marking or scan launch): at most this many runs of 64
+// tiles per sample, whose counts the resolve workgroup scans in LDS.
+constexpr int64_t kFoldMaxRuns = 16384;
 
 struct SelectPass {
   int32_t kind;   // 0: entropy key digit, 1: tile-index digit among tied entropies
@@ -59,6 +67,11 @@ struct Plan {
   // workspace layout
   int64_t ws_status, ws_state, ws_hist, ws_H, ws_LS, ws_blockcnt, ws_table, ws_bitmap, ws_cand, ws_wtotal, ws_side,
       ws_total;
+  // two-width layout built without the marking and scan launches: the last
+  // entropy pass writes the width map's sure bits and the count of each run
+  // of 64 tiles, the resolve kernel adds the tiles decided at the threshold
+  // and scans the counts into the block table
+  int32_t fold;
   int64_t ncand, cand_stride;  // capacity of a sample's candidate list; its uint32 words
   int32_t npasses;
   SelectPass passes[kMaxPasses];

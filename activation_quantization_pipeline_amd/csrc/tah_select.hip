@@ -176,9 +176,13 @@ struct HistArgs {
   uint32_t* hist_cur;          // this pass's histograms (zero on entry)
   uint32_t* hist_clear;        // the next pass's histograms, cleared here
   uint32_t* cand;  // per sample: count, pad, then up to ncand (key, index) pairs
+  // fold (last entropy pass only): the width map's sure bits and the count
+  // of each run of 64 tiles
+  uint32_t* fold_bitmap;
+  uint32_t* fold_run;
   int64_t N, nsamples, chunks_per_sample, k, ncand, cand_stride;
   SelectPass pass, prev;
-  int32_t has_prev;
+  int32_t has_prev, fold;
 };
 
 // Large workgroups, 4 keys per thread: 256 of them for a million keys fill the
@@ -186,7 +190,8 @@ struct HistArgs {
 // into the same global bins.
 constexpr int kHistThreads = 1024;
 constexpr int kHistPerThread = 4;
-constexpr int kHistChunk = kHistThreads * kHistPerThread;
+static_assert(kHistChunk == kHistThreads * kHistPerThread, "a histogram workgroup takes one chunk of keys");
+static_assert(kHistChunk % 64 == 0, "a chunk is whole runs of 64 tiles");
 
 // Apply one pass to a sample's state: one wavefront scans the pass's histogram
 // in order (descending digits for the entropy key, ascending for the tile
@@ -316,6 +321,19 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
         const uint32_t pos = base + lanes_below(wm);
         if (want && pos < (uint32_t)kCandPerChunk) lc[pos] = make_uint2(orderable(hv[i]), (uint32_t)u);
       }
+      if (a.fold) {
+        // keys above the threshold's prefix are selected whatever the last
+        // digit: the run's width-map words and count (the keys matching the
+        // prefix are added by k_resolve); a wavefront's 64 keys are one run
+        const bool sure = u < a.N && hs < 32 && (orderable(hv[i]) >> hs) > (S.key >> hs);
+        const uint64_t m = ballot(sure);
+        const int64_t ub = u0 + i * kHistThreads + (tid & ~63);
+        if (ub < a.N) {
+          const int64_t run = (s * a.N + ub) >> 6;
+          if (lane < 2) a.fold_bitmap[2 * run + lane] = (uint32_t)(m >> (32 * lane));
+          if (lane == 0) a.fold_run[run] = (uint32_t)__popcll(m);
+        }
+      }
     }
     // lanes with the same digit as the first remaining lane add together (twice),
     // the rest one by one
@@ -367,18 +385,26 @@ struct ResolveArgs {
   SampleState* st_out;
   const uint32_t* hist_last;
   const uint32_t* cand;
-  int64_t N, ncand, cand_stride;
+  // fold: the selected tiles among those matching the threshold's prefix go
+  // into the width map and the run counts, which are then scanned into the
+  // block table
+  uint32_t* fold_bitmap;
+  const uint32_t* fold_run;
+  uint32_t* table;
+  int64_t N, ncand, cand_stride, k;
   SelectPass last;
-  int32_t nidx;
+  int32_t nidx, fold;
   SelectPass idx[kMaxPasses];
 };
 
 constexpr int kResolveThreads = 1024;
 
 __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t rc[];  // fold: the sample's run counts
   __shared__ uint32_t lh[kBins];
   __shared__ SampleState ss;
   __shared__ uint2 lk[kMaxCand];  // the sample's candidate list
+  __shared__ uint32_t wsum[kResolveThreads / 64];
   const int tid = threadIdx.x;
   const int64_t s = blockIdx.x;
   if (tid < 64) {
@@ -387,16 +413,16 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
   }
   __syncthreads();
   SampleState S = ss;
+  const float* h = a.H + s * a.N;
+  const uint32_t* cl = a.cand + s * a.cand_stride;
+  const int64_t nc = cl[0];
+  const bool listed = nc <= a.ncand;  // else scan the whole sample
+  const int64_t n = listed ? nc : a.N;
+  if (listed && (!S.tie_all || a.fold)) {
+    for (int64_t i = tid; i < nc; i += kResolveThreads) lk[i] = reinterpret_cast<const uint2*>(cl + 2)[i];
+    __syncthreads();
+  }
   if (!S.tie_all) {
-    const float* h = a.H + s * a.N;
-    const uint32_t* cl = a.cand + s * a.cand_stride;
-    const int64_t nc = cl[0];
-    const bool listed = nc <= a.ncand;  // else scan the whole sample
-    const int64_t n = listed ? nc : a.N;
-    if (listed) {
-      for (int64_t i = tid; i < nc; i += kResolveThreads) lk[i] = reinterpret_cast<const uint2*>(cl + 2)[i];
-      __syncthreads();
-    }
     for (int p = 0; p < a.nidx; ++p) {
       const SelectPass ps = a.idx[p];
       for (int i = tid; i < kBins; i += kResolveThreads) lh[i] = 0u;
@@ -424,6 +450,83 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
       S = ss;
     }
   }
+  if (a.fold) {
+    // the sample's run counts in LDS, plus the selected tiles among those
+    // matching the threshold's prefix (the sure ones are counted already)
+    // (an LDS array of nr times kRound counts, zero past the sample's runs)
+    const int64_t runs = a.N / 64, r0 = s * runs;
+    constexpr int kRound = 4 * kResolveThreads;
+    const int nr = (int)((runs + kRound - 1) / kRound);
+    {
+      uint32_t v[kFoldMaxRuns / kResolveThreads];  // every load in flight before the first LDS store
+#pragma unroll
+      for (int i = 0; i < (int)(kFoldMaxRuns / kResolveThreads); ++i) {
+        const int64_t j = (int64_t)i * kResolveThreads + tid;
+        v[i] = 0u;
+        if (i < 4 * nr && j < runs) v[i] = a.fold_run[r0 + j];
+      }
+#pragma unroll
+      for (int i = 0; i < (int)(kFoldMaxRuns / kResolveThreads); ++i)
+        if (i < 4 * nr) rc[i * kResolveThreads + tid] = v[i];
+    }
+    __syncthreads();
+    const int hs = a.last.shift + a.last.width;  // the prefix the last entropy pass matched
+    for (int64_t i = tid; i < n; i += kResolveThreads) {
+      uint32_t key, uu;
+      if (listed) {
+        key = lk[i].x;
+        uu = lk[i].y;
+      } else {
+        key = orderable(h[i]);
+        uu = (uint32_t)i;
+      }
+      if ((key >> hs) == (S.key >> hs) && (key > S.key || (key == S.key && uu <= S.upos))) {
+        const int64_t t = s * a.N + uu;
+        atomicOr(&a.fold_bitmap[t >> 5], 1u << (t & 31));
+        atomicAdd(&rc[uu >> 6], 1u);
+      }
+    }
+    __syncthreads();
+    // block table: every earlier sample holds k upgraded tiles, then the
+    // exclusive scan of this sample's run counts; thread tid owns the 4 nr
+    // consecutive counts from 4 nr tid (nr 16-byte words)
+    constexpr int kMaxQ = (int)(kFoldMaxRuns / kRound);
+    uint4* seg = reinterpret_cast<uint4*>(rc) + tid * nr;
+    uint32_t c[4 * kMaxQ];
+#pragma unroll
+    for (int q = 0; q < kMaxQ; ++q) {
+      const uint4 w4 = q < nr ? seg[q] : make_uint4(0u, 0u, 0u, 0u);
+      c[4 * q] = w4.x;
+      c[4 * q + 1] = w4.y;
+      c[4 * q + 2] = w4.z;
+      c[4 * q + 3] = w4.w;
+    }
+    uint32_t tot = 0u;
+#pragma unroll
+    for (int i = 0; i < 4 * kMaxQ; ++i) tot += c[i];
+    const int lane = tid & 63, wave = tid >> 6;
+    uint32_t incl = tot;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const uint32_t o = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += o;
+    }
+    if (lane == 63) wsum[wave] = incl;
+    __syncthreads();
+    uint32_t run = (uint32_t)s * (uint32_t)a.k + incl - tot;
+    for (int w = 0; w < wave; ++w) run += wsum[w];
+#pragma unroll
+    for (int i = 0; i < 4 * kMaxQ; ++i) {
+      const uint32_t ci = c[i];
+      c[i] = run;
+      run += ci;
+    }
+#pragma unroll
+    for (int q = 0; q < kMaxQ; ++q)
+      if (q < nr) seg[q] = make_uint4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
+    __syncthreads();
+    for (int64_t j = tid; j < runs; j += kResolveThreads) a.table[r0 + j] = rc[j];  // coalesced
+  }
   if (tid == 0) a.st_out[s] = S;
 }
 
@@ -444,7 +547,6 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
 // every sample has k upgraded allocation tiles, so the block table at the
 // sample's first run is s * k * kA, and the runs inside the sample add their
 // own counts. Otherwise it writes the final state for k_mark.
-constexpr int64_t kLdsSelect = 4096;
 constexpr int64_t kLdsMarkRuns = 4096;
 constexpr int kLdsThreads = 1024;
 
@@ -724,6 +826,8 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   h.cand = reinterpret_cast<uint32_t*>(w + pl.ws_cand);
   h.ncand = pl.ncand;
   h.cand_stride = pl.cand_stride;
+  h.fold_bitmap = reinterpret_cast<uint32_t*>(P ? P + pl.off_bitmap : w + pl.ws_bitmap);
+  h.fold_run = reinterpret_cast<uint32_t*>(w + pl.ws_blockcnt);
   const int64_t nwg = h.chunks_per_sample * pl.nsamples;
   // entropy-key passes; pass p: state p in states[p % 2], histogram p in
   // hists[p % 3] (zeroed by k_stats for p = 0). The tile-index passes that
@@ -739,6 +843,7 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
     h.hist_prev = hists + ((p + 2) % 3) * hsz;
     h.hist_cur = hists + (p % 3) * hsz;
     h.hist_clear = hists + ((p + 1) % 3) * hsz;
+    h.fold = pl.fold && h.pass.last_h;
     hipLaunchKernelGGL(k_hist, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -756,9 +861,21 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   rs.last = pl.passes[nkey - 1];
   rs.nidx = pl.npasses - nkey;
   for (int i = 0; i < rs.nidx; ++i) rs.idx[i] = pl.passes[nkey + i];
-  hipLaunchKernelGGL(k_resolve, dim3((unsigned)pl.nsamples), dim3(kResolveThreads), 0, st, rs);
+  rs.fold_bitmap = h.fold_bitmap;
+  rs.fold_run = h.fold_run;
+  rs.table = reinterpret_cast<uint32_t*>(P ? P + pl.off_table : w + pl.ws_table);
+  rs.k = pl.k;
+  rs.fold = pl.fold;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_resolve),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                     (int)(4 * kFoldMaxRuns));
+  if (attr != hipSuccess) return attr;
+  // the run counts in whole rounds of 4 per thread
+  const int64_t rc_round = 4 * kResolveThreads;
+  const size_t rc_bytes = pl.fold ? (size_t)(4 * ((pl.N / 64 + rc_round - 1) / rc_round) * rc_round) : 0;
+  hipLaunchKernelGGL(k_resolve, dim3((unsigned)pl.nsamples), dim3(kResolveThreads), rc_bytes, st, rs);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || pl.fold) return e;  // fold: width map and block table are complete
   return mark_and_table(pl, P, w, rs.st_out, st);
 }
 

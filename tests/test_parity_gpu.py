@@ -526,6 +526,31 @@ def test_threshold_inside_a_tie_in_a_large_sample(n_tied):
     assert hi[tied_idx[:n_sel]].all() and not hi[tied_idx[n_sel:]].any()
 
 
+@pytest.mark.parametrize("S,ns", [(65, 5), (193, 3), (1024, 2)])
+def test_counts_in_place_of_the_block_table(S, ns):
+    """Samples of whole runs of 64 tiles above the one-workgroup select: the
+    last select pass writes the width map's sure bits and the counts per run
+    and per chunk of 64 runs, the resolve step adds the tiles at the
+    threshold, and the encoder sums the counts into the block table. Chunks
+    that end inside a sample (65 and 193 runs), several samples, and a
+    threshold inside a class of equal tiles spread over every sample."""
+    G, M = 64, 64
+    T = S * ns
+    x = synth.random_tensor(T, G * M, synth.BF16, 70 + S, n_out=3, mult=40)
+    p = P(tile=G, tokens_per_sample=S, bit_budget=3.4, candidates=(3, 4), tau=2.0)
+    assert oracle.plan(T, G * M, p)["atiles_per_sample"] == S * M
+    run_case(x, p, f"counts S={S} samples={ns}")
+    # a third of the tiles one repeated tile whose entropy sits in the middle
+    rng = np.random.default_rng(S)
+    tiles = rng.standard_normal((T * M, G)) * rng.choice([0.01, 1.0], (T * M, 1))
+    tied = np.where(np.arange(G) % 2 == 0, 1.0, 0.0) * np.linspace(0.5, 1.5, G)
+    tiles[rng.random(T * M) < 0.33] = tied
+    xt = tiles.reshape(T, G * M).astype(np.float32)
+    for budget in (3.2, 3.5, 3.8):
+        run_case(xt, P(tile=G, tokens_per_sample=S, bit_budget=budget, candidates=(3, 4), tau=2.0),
+                 f"counts ties S={S} samples={ns} budget {budget}")
+
+
 def random_config_large(seed):
     """A seeded random configuration of up to 3000 tokens and 64 tiles per
     token: samples above the one-workgroup select's 4096 keys, several groups
