@@ -19,9 +19,7 @@ constexpr int kMaxPasses = 6;
 // and kMaxCand per sample.
 constexpr int kCandPerChunk = 512;
 constexpr int64_t kMaxCand = 4096;
-// Keys per workgroup of the grid-wide select passes (64 runs of 64 tiles), and
-// the largest samples selected by one workgroup with the keys in LDS.
-constexpr int64_t kHistChunk = 4096;
+// The largest samples selected by one workgroup with the keys in LDS.
 constexpr int64_t kLdsSelect = 4096;
 // Two-width layouts whose width map and block table the select's last two
 // launches write (no marking or scan launch): at most this many runs of 64

@@ -185,13 +185,16 @@ struct HistArgs {
   int32_t has_prev, fold;
 };
 
-// Large workgroups, 4 keys per thread: 256 of them for a million keys fill the
-// chip (16 keys per thread left three quarters of it idle), and few enough add
-// into the same global bins.
+// Large workgroups of P keys per thread (a chunk of 1024 P keys each, whole
+// runs of 64 tiles). The launch takes the smallest P in {1, 2, 4} that keeps
+// the grid within kHistMaxWgs workgroups: a million keys at P = 4 (256
+// workgroups) fill the chip and few enough add into the same global bins
+// (P = 16 left three quarters of it idle; P = 2 and 1 add too many global
+// atomics: 125.3 -> 135.4 us per 80/20 round trip at 8192 x 8192), while
+// 131,072 keys run best as 128 workgroups of P = 1 (4096 x 2048 round trip:
+// 45.5 us at P = 4, 42.8 at P = 2, 42.0 at P = 1).
 constexpr int kHistThreads = 1024;
-constexpr int kHistPerThread = 4;
-static_assert(kHistChunk == kHistThreads * kHistPerThread, "a histogram workgroup takes one chunk of keys");
-static_assert(kHistChunk % 64 == 0, "a chunk is whole runs of 64 tiles");
+constexpr int64_t kHistMaxWgs = 256;
 
 // Apply one pass to a sample's state: one wavefront scans the pass's histogram
 // in order (descending digits for the entropy key, ascending for the tile
@@ -254,6 +257,7 @@ __device__ __forceinline__ SampleState apply_pass(SampleState S, const uint32_t*
   return S;
 }
 
+template <int P>
 __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
   __shared__ uint32_t lh[kBins];
   __shared__ SampleState ss;
@@ -262,11 +266,11 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t s = blockIdx.x / a.chunks_per_sample;
   const int64_t c = blockIdx.x % a.chunks_per_sample;
-  const int64_t u0 = c * kHistChunk;
+  const int64_t u0 = c * (int64_t)(kHistThreads * P);
   // the keys first: their loads are in flight while the previous pass is applied
-  float hv[kHistPerThread];
+  float hv[P];
 #pragma unroll
-  for (int i = 0; i < kHistPerThread; ++i) {
+  for (int i = 0; i < P; ++i) {
     const int64_t u = u0 + i * kHistThreads + tid;
     hv[i] = u < a.N ? a.H[s * a.N + u] : 0.0f;
   }
@@ -300,7 +304,7 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
   const int hs = a.pass.shift + a.pass.width;  // bits above the current digit
   const uint32_t dmask = (1u << a.pass.width) - 1u;
 #pragma unroll
-  for (int i = 0; i < kHistPerThread; ++i) {
+  for (int i = 0; i < P; ++i) {
     const int64_t u = u0 + i * kHistThreads + tid;
     bool want = false;
     uint32_t digit = 0;
@@ -536,9 +540,9 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
 // threshold key is shared by more tiles than remain to be selected, the
 // tile-index digits: the same passes and apply_pass as the grid-wide form, so
 // the same final state, from one read of the keys and one launch instead of
-// one launch per digit, k_resolve, k_mark and k_table. The limit is one
-// histogram chunk of the grid-wide passes, which would run one workgroup per
-// sample as well: with 32768-key samples a workgroup per sample is
+// one launch per digit, k_resolve, k_mark and k_table. The limit is 4096
+// keys, where the grid-wide passes run at most four workgroups per sample
+// anyway: with 32768-key samples a workgroup per sample is
 // latency-bound (32 dependent rounds per thread and pass) and the 4096 x 2048
 // round trip took 76.1 us against 47.7 us grid-wide, with the keys in LDS as
 // when they were re-read from global memory in every pass (78.2 us).
@@ -822,7 +826,10 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   h.N = pl.N;
   h.nsamples = pl.nsamples;
   h.k = pl.k;
-  h.chunks_per_sample = (pl.N + kHistChunk - 1) / kHistChunk;
+  int per = 1;  // keys per thread
+  while (per < 4 && pl.nsamples * ((pl.N + kHistThreads * per - 1) / (kHistThreads * per)) > kHistMaxWgs) per *= 2;
+  const int64_t chunk = (int64_t)kHistThreads * per;
+  h.chunks_per_sample = (pl.N + chunk - 1) / chunk;
   h.cand = reinterpret_cast<uint32_t*>(w + pl.ws_cand);
   h.ncand = pl.ncand;
   h.cand_stride = pl.cand_stride;
@@ -844,7 +851,9 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
     h.hist_cur = hists + (p % 3) * hsz;
     h.hist_clear = hists + ((p + 1) % 3) * hsz;
     h.fold = pl.fold && h.pass.last_h;
-    hipLaunchKernelGGL(k_hist, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
+    if (per == 1) hipLaunchKernelGGL(k_hist<1>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
+    else if (per == 2) hipLaunchKernelGGL(k_hist<2>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
+    else hipLaunchKernelGGL(k_hist<4>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
