@@ -157,6 +157,22 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
   }
 }
 
+// Whether the receiver's H then 1/G (Eq. 4 inverted) may take the 1/G first,
+// as fmaf(q, s/G, lo/G), with bit-identical results. G is a power of two, so
+// scaling by 1/G commutes with every rounding that stays in the normal range.
+// With s = 0 or s >= 2^-112 (s has 8 significant bits) and lo = 0 or
+// |lo| >= 2^-96, every q s + lo is a multiple of 2^-119, and so is every sum
+// and difference of the butterflies; divided by G <= 128 such a value is 0 or
+// at least 2^-126, never subnormal, so each scaled result is the unscaled one
+// over G, exactly, and so is the last product by 1/G. With |lo|, |hv| < 2^120
+// no unscaled sum of at most 128 values overflows either. Anything else (NaN,
+// infinities, tiny or huge tiles) keeps the product by 1/G after H.
+__device__ __forceinline__ bool prescale_exact(float s, float lo, float hv) {
+  const float alo = fabsf(lo);
+  return (s == 0.0f || s >= 0x1p-112f) && (lo == 0.0f || alo >= 0x1p-96f) && alo < 0x1p120f &&
+         fabsf(hv) < 0x1p120f;
+}
+
 // Step s rounded up to bf16 and its reciprocal (§3.3 asymmetric quantizer).
 __device__ __forceinline__ void step_of(float lo, float hv, int b, float& s, float& inv) {
   const float L = (float)((1 << b) - 1);
@@ -174,8 +190,12 @@ __device__ __forceinline__ void step_of(float lo, float hv, int b, float& s, flo
 // Algorithm 1, from the codes in registers).
 // GUARD: skip a code block that would end past the code section (the
 // any-width layout, whose offsets come from the allocator's tables).
+// tr: the tile was transformed, so its dequantized values go through H and
+// the 1/G. Returns true when the 1/G is already applied here, as the step
+// s/G and zero-point lo/G of the dequantization (exact, see prescale_exact).
 template <int G, int OUT, bool GUARD = false>
-__device__ __forceinline__ void quantize_tile(const EncArgs& a, float (&v)[G], int64_t t, int b, int64_t code_off) {
+__device__ __forceinline__ bool quantize_tile(const EncArgs& a, float (&v)[G], int64_t t, int b, int64_t code_off,
+                                              bool tr = false) {
   float lo = v[0], hv = v[0];
 #pragma unroll
   for (int k = 1; k < G; ++k) {
@@ -194,10 +214,14 @@ __device__ __forceinline__ void quantize_tile(const EncArgs& a, float (&v)[G], i
     reinterpret_cast<uint16_t*>(a.payload + a.off_scale)[t] = (uint16_t)(__float_as_uint(s) >> 16);
     reinterpret_cast<float*>(a.payload + a.off_zero)[t] = lo;
   }
+  bool pre = false;
   if constexpr (OUT != 0) {
+    pre = tr && prescale_exact(s, lo, hv);
+    const float sd = pre ? s * (1.0f / G) : s, ld = pre ? lo * (1.0f / G) : lo;
 #pragma unroll
-    for (int k = 0; k < G; ++k) v[k] = __builtin_fmaf(__uint_as_float(mq[k]) - 0x1p23f, s, lo);
+    for (int k = 0; k < G; ++k) v[k] = __builtin_fmaf(__uint_as_float(mq[k]) - 0x1p23f, sd, ld);
   }
+  return pre;
 }
 
 // OUT: 0 = no reconstruction, 1 = fp32, 2 = bf16.
@@ -411,12 +435,16 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
         lds_read_tile<G, TIn>(row, v);
         fwht<G>(v);
       }
-      quantize_tile<G, OUT, MODE == 2>(a, v, t, b, code_off);
+      const bool scaled = quantize_tile<G, OUT, MODE == 2>(a, v, t, b, code_off, flag != 0);
       if constexpr (OUT != 0) {
-        if (flag) {  // H^T = H, the 1/G
-          fwht<G>(v);
+        if (flag) fwht<G>(v);  // H^T = H
+        // the 1/G where the dequantization did not take it (rare: skipped by
+        // the whole wavefront when no lane needs it)
+        if (ballot(flag && !scaled) != 0) {
+          if (flag && !scaled) {
 #pragma unroll
-          for (int k = 0; k < G; ++k) v[k] = v[k] * (1.0f / G);
+            for (int k = 0; k < G; ++k) v[k] = v[k] * (1.0f / G);
+          }
         }
         uint8_t* orow = ys + lane * RO::kStride;
         lds_write_tile<G, TOut>(orow, v);

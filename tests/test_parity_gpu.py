@@ -438,6 +438,29 @@ def test_threshold_inside_a_tie_across_workgroups():
     assert hi[tied_idx[:80]].all() and not hi[tied_idx[80:]].any()
 
 
+@pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
+@pytest.mark.parametrize("tile", [32, 64, 128])
+def test_transformed_tiles_at_extreme_magnitudes(dtype, tile):
+    """Transformed tiles whose dequantized values are subnormal, tiny, huge or
+    ordinary, mixed within every wavefront: the round trip may take the
+    receiver's 1/G into the dequantization only where that is exact, and
+    must match the oracle's H then 1/G bit for bit everywhere."""
+    rng = np.random.default_rng(41 + tile)
+    T, M = 96, 12
+    x = rng.standard_normal((T, tile * M))
+    x[:, ::tile] *= 40.0  # a spike in every tile: flagged at tau = 2
+    # the transformed values of a tile reach about 200 times its scale: the
+    # largest scales straddle 2^120 there while no sum of the inverse overflows
+    scales = np.array([1e-38, 2.0 ** -120, 1e-30, 2.0 ** -97, 2.0 ** -96, 2.0 ** -90, 1e-3, 1.0,
+                       2.0 ** 100, 2.0 ** 110, 2.0 ** 112.5, 2.0 ** 113])
+    idx = (np.arange(T)[:, None] + np.arange(M)[None, :]) % len(scales)
+    x = (x.reshape(T, M, tile) * scales[idx][:, :, None]).reshape(T, tile * M)
+    x = x.astype(np.float32) if dtype == synth.F32 else synth.f32_to_bf16_bits(x)
+    for tau in (2.0, 0.0):
+        run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=tau),
+                 f"extreme magnitudes tile {tile} tau {tau}")
+
+
 def random_config(seed):
     """A seeded random shape and parameter set within the library's limits."""
     r = np.random.default_rng(1000 + seed)
