@@ -479,9 +479,10 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
 // does (code k at stream bits [kB, kB + B), LSB first), each code dequantized
 // into v (OUT) as soon as its last bit is in a word; stores the code block at
 // dst (GUARD: unless it would end past the code section). The same code
-// values, words and dequantized values as quantize_tile.
+// values, words and dequantized values as quantize_tile (sd, ld: the step and
+// zero-point of the dequantization, s and lo or both over G).
 template <int G, int B, int OUT, bool GUARD>
-__device__ __forceinline__ void quant_pack(const EncArgs& a, float (&v)[G], float lo, float s, float inv,
+__device__ __forceinline__ void quant_pack(const EncArgs& a, float (&v)[G], float lo, float inv, float sd, float ld,
                                            int64_t code_off) {
   constexpr int W = G * B / 32;
   uint32_t w[W];
@@ -498,7 +499,7 @@ __device__ __forceinline__ void quant_pack(const EncArgs& a, float (&v)[G], floa
       const uint32_t q = (k * B < lo_bit) ? carry : __float_as_uint(__builtin_fmaf(v[k] - lo, inv, 0x1p23f));
       acc = __builtin_amdgcn_alignbit(q, acc, (uint32_t)n);
       if ((k + 1) * B <= lo_bit + 32) {
-        if constexpr (OUT != 0) v[k] = __builtin_fmaf(__uint_as_float(q) - 0x1p23f, s, lo);
+        if constexpr (OUT != 0) v[k] = __builtin_fmaf(__uint_as_float(q) - 0x1p23f, sd, ld);
       } else {
         carry = q;
       }
@@ -513,8 +514,10 @@ __device__ __forceinline__ void quant_pack(const EncArgs& a, float (&v)[G], floa
   }
 }
 
+// tr and the result: as for quantize_tile.
 template <int G, int OUT, bool GUARD>
-__device__ __forceinline__ void quantize_stream(const EncArgs& a, float (&v)[G], int64_t t, int b, int64_t code_off) {
+__device__ __forceinline__ bool quantize_stream(const EncArgs& a, float (&v)[G], int64_t t, int b, int64_t code_off,
+                                                bool tr) {
   float lo = v[0], hv = v[0];
 #pragma unroll
   for (int k = 1; k < G; ++k) {
@@ -525,20 +528,23 @@ __device__ __forceinline__ void quantize_stream(const EncArgs& a, float (&v)[G],
   hv = hv + 0.0f;
   float s, inv;
   step_of(lo, hv, b, s, inv);
+  const bool pre = OUT != 0 && tr && prescale_exact(s, lo, hv);
+  const float sd = pre ? s * (1.0f / G) : s, ld = pre ? lo * (1.0f / G) : lo;
   switch (b) {
-    case 1: quant_pack<G, 1, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
-    case 2: quant_pack<G, 2, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
-    case 3: quant_pack<G, 3, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
-    case 4: quant_pack<G, 4, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
-    case 5: quant_pack<G, 5, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
-    case 6: quant_pack<G, 6, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
-    case 7: quant_pack<G, 7, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
-    default: quant_pack<G, 8, OUT, GUARD>(a, v, lo, s, inv, code_off); break;
+    case 1: quant_pack<G, 1, OUT, GUARD>(a, v, lo, inv, sd, ld, code_off); break;
+    case 2: quant_pack<G, 2, OUT, GUARD>(a, v, lo, inv, sd, ld, code_off); break;
+    case 3: quant_pack<G, 3, OUT, GUARD>(a, v, lo, inv, sd, ld, code_off); break;
+    case 4: quant_pack<G, 4, OUT, GUARD>(a, v, lo, inv, sd, ld, code_off); break;
+    case 5: quant_pack<G, 5, OUT, GUARD>(a, v, lo, inv, sd, ld, code_off); break;
+    case 6: quant_pack<G, 6, OUT, GUARD>(a, v, lo, inv, sd, ld, code_off); break;
+    case 7: quant_pack<G, 7, OUT, GUARD>(a, v, lo, inv, sd, ld, code_off); break;
+    default: quant_pack<G, 8, OUT, GUARD>(a, v, lo, inv, sd, ld, code_off); break;
   }
   if (a.payload) {
     reinterpret_cast<uint16_t*>(a.payload + a.off_scale)[t] = (uint16_t)(__float_as_uint(s) >> 16);
     reinterpret_cast<float*>(a.payload + a.off_zero)[t] = lo;
   }
+  return pre;
 }
 
 // n (<= 32) contiguous tiles of BYTES bytes between global memory and LDS rows
@@ -735,14 +741,18 @@ __global__ __launch_bounds__(64, 2) void k_encode128(EncArgs a) {
     if (act && flag) fwht<G>(v);
 
     // ---- quantize, pack, dequantize
-    if (act) quantize_stream<G, OUT, MODE == 2>(a, v, t, b, code_off);
+    bool scaled = false;
+    if (act) scaled = quantize_stream<G, OUT, MODE == 2>(a, v, t, b, code_off, flag != 0);
 
     // ---- inverse and out: two rounds of 32 rebuilt tiles through LDS
     if constexpr (OUT != 0) {
-      if (act && flag) {  // H^T = H, the 1/G
-        fwht<G>(v);
+      if (act && flag) fwht<G>(v);  // H^T = H
+      // the 1/G where the dequantization did not take it
+      if (ballot(act && flag && !scaled) != 0) {
+        if (act && flag && !scaled) {
 #pragma unroll
-        for (int k = 0; k < G; ++k) v[k] = v[k] * (1.0f / G);
+          for (int k = 0; k < G; ++k) v[k] = v[k] * (1.0f / G);
+        }
       }
 #pragma unroll
       for (int r = 0; r < 2; ++r) {
