@@ -574,6 +574,25 @@ def test_counts_in_place_of_the_block_table(S, ns):
                  f"counts ties S={S} samples={ns} budget {budget}")
 
 
+def test_one_sample_past_the_in_place_table_limit():
+    """One sample of 1,064,960 tiles (16,640 runs of 64, more than the resolve
+    workgroup scans in LDS): the select marks and scans in separate launches;
+    payload and round trip against the oracle, checked at sampled tiles of
+    the whole width map and every block-table entry."""
+    T, H = 8320, 8192
+    x = synth.random_tensor(T, H, synth.BF16, 77, n_out=8, mult=60)
+    p = P(tile=64, tokens_per_sample=0, bit_budget=3.8, candidates=(3, 4), tau=2.0)
+    pl = oracle.plan(T, H, p)
+    assert pl["tiles_per_sample"] // 64 > 16384
+    say("[edge] one sample past the in-place table limit: oracle")
+    R = oracle.encode(x, p)
+    say("[edge] one sample past the in-place table limit: GPU")
+    y, P_ = tah.roundtrip(to_dev(x), p, torch.bfloat16)
+    assert_payload_equal(to_host(P_), R, pl, "one sample past the in-place table limit")
+    y_ref = oracle.decode(R, T, H, p, oracle.BF16)
+    assert_decoded_equal(to_host(y), y_ref, R, pl, "one sample past the in-place table limit")
+
+
 def random_config_large(seed):
     """A seeded random configuration of up to 3000 tokens and 64 tiles per
     token: samples above the one-workgroup select's 4096 keys, several groups
