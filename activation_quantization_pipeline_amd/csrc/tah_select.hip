@@ -416,6 +416,18 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
   __shared__ uint32_t wsum[kResolveThreads / 64];
   const int tid = threadIdx.x;
   const int64_t s = blockIdx.x;
+  // fold: the sample's run counts, loaded first (in flight during the rest)
+  constexpr int kRound = 4 * kResolveThreads;
+  constexpr int kPer = (int)(kFoldMaxRuns / kResolveThreads);
+  const int64_t runs = a.N / 64, r0 = s * runs;
+  const int nr = a.fold ? (int)((runs + kRound - 1) / kRound) : 0;
+  uint32_t rv[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int64_t j = (int64_t)i * kResolveThreads + tid;
+    rv[i] = 0u;
+    if (i < 4 * nr && j < runs) rv[i] = a.fold_run[r0 + j];
+  }
   if (tid < 64) {
     const SampleState S = apply_pass(a.st_prev[s], a.hist_last + s * kBins, a.last);
     if (tid == 0) ss = S;
@@ -431,7 +443,47 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
     for (int64_t i = tid; i < nc; i += kResolveThreads) lk[i] = reinterpret_cast<const uint2*>(cl + 2)[i];
     __syncthreads();
   }
-  if (!S.tie_all) {
+  // Few tied keys (at most 64, listed): one wavefront gathers their tile
+  // indexes and takes the r-th lowest directly, the same index the digit
+  // passes below would find.
+  __shared__ int few_done;
+  if (!S.tie_all && listed) {
+    if (tid < 64) {
+      const int lane = tid;
+      int cnt = 0;  // tied keys gathered so far (uniform)
+      for (int64_t i0 = 0; i0 < nc && cnt <= 64; i0 += 64) {
+        const int64_t i = i0 + lane;
+        const bool tied = i < nc && lk[i].x == S.key;
+        const uint64_t m = ballot(tied);
+        const int pos = cnt + (int)lanes_below(m);
+        if (tied && pos < 64) lh[pos] = lk[i].y;
+        cnt += __popcll(m);
+      }
+      __threadfence_block();
+      int ok = 0;
+      if (cnt <= 64) {
+        const uint32_t mine = lane < cnt ? lh[lane] : 0xffffffffu;
+        int rank = 0;  // tied indexes below this one (indexes are unique)
+        for (int j = 0; j < cnt; ++j) rank += (uint32_t)__shfl((int)mine, j, 64) < mine ? 1 : 0;
+        const uint64_t hit = ballot(lane < cnt && (int64_t)rank == S.r - 1);
+        if (hit != 0) {
+          const int src = __ffsll((unsigned long long)hit) - 1;
+          const uint32_t up = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
+          if (lane == 0) {
+            SampleState T = S;
+            T.upos = up;
+            T.r = 1;
+            ss = T;
+          }
+          ok = 1;
+        }
+      }
+      if (lane == 0) few_done = ok;
+    }
+    __syncthreads();
+    if (few_done) S = ss;
+  }
+  if (!S.tie_all && !(listed && few_done)) {
     for (int p = 0; p < a.nidx; ++p) {
       const SelectPass ps = a.idx[p];
       for (int i = tid; i < kBins; i += kResolveThreads) lh[i] = 0u;
@@ -463,21 +515,9 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
     // the sample's run counts in LDS, plus the selected tiles among those
     // matching the threshold's prefix (the sure ones are counted already)
     // (an LDS array of nr times kRound counts, zero past the sample's runs)
-    const int64_t runs = a.N / 64, r0 = s * runs;
-    constexpr int kRound = 4 * kResolveThreads;
-    const int nr = (int)((runs + kRound - 1) / kRound);
-    {
-      uint32_t v[kFoldMaxRuns / kResolveThreads];  // every load in flight before the first LDS store
 #pragma unroll
-      for (int i = 0; i < (int)(kFoldMaxRuns / kResolveThreads); ++i) {
-        const int64_t j = (int64_t)i * kResolveThreads + tid;
-        v[i] = 0u;
-        if (i < 4 * nr && j < runs) v[i] = a.fold_run[r0 + j];
-      }
-#pragma unroll
-      for (int i = 0; i < (int)(kFoldMaxRuns / kResolveThreads); ++i)
-        if (i < 4 * nr) rc[i * kResolveThreads + tid] = v[i];
-    }
+    for (int i = 0; i < kPer; ++i)
+      if (i < 4 * nr) rc[i * kResolveThreads + tid] = rv[i];
     __syncthreads();
     const int hs = a.last.shift + a.last.width;  // the prefix the last entropy pass matched
     for (int64_t i = tid; i < n; i += kResolveThreads) {

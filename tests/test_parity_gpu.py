@@ -515,14 +515,15 @@ def test_full_size_other_seed(name, seed):
     assert_decoded_equal(to_host(y), y_ref, R, pl, f"{name} seed {seed}")
 
 
-@pytest.mark.parametrize("n_tied", [200, 6000])
+@pytest.mark.parametrize("n_tied", [3, 40, 64, 65, 200, 6000])
 def test_threshold_inside_a_tie_in_a_large_sample(n_tied):
     """One sample of 163840 tiles, above the size that one workgroup selects
     alone, so the select runs grid-wide (40 histogram workgroups, then the tie
     step): half the tiles flat (above), n_tied copies of one tile spread over
     the sample, the rest spiky (below); k = 81920 lands inside the tied class.
-    With 200 tied tiles the tie is broken from the listed candidates; with
-    6000 the list overflows and the whole sample is scanned."""
+    Up to 64 tied tiles are ranked by one wavefront; with 65 and 200 the tie
+    is broken by digit passes over the listed candidates; with 6000 the list
+    overflows and the whole sample is scanned."""
     rng = np.random.default_rng(31 + n_tied)
     T, H, G = 2560, 4096, 64
     n = T * H // G
