@@ -132,8 +132,18 @@ def to_dev(x, torch):
     return torch.from_numpy(x).cuda()
 
 
-def time_launches(torch, launch, n_sets, steps, warmup):
-    """Times `steps` back-to-back launches after `warmup` untimed ones.
+# Extra legs (not the headline step): at least this much untimed back-to-back
+# work before each timed window. The round trip's duration follows the part's
+# power management: after an idle spell it runs slower for the first
+# milliseconds of sustained load (about 65 us, then 75-83 us, before settling
+# at 61-63 us on the headline kernel), so short warm-ups would time each leg in
+# a different state.
+EXTRA_WARM_MS = 40.0
+
+
+def time_launches(torch, launch, n_sets, steps, warmup, warm_ms=0.0):
+    """Times `steps` back-to-back launches after `warmup` untimed ones (and,
+    with warm_ms, more untimed launches until that much wall time has passed).
 
     The timed region is bracketed by synchronize on both sides (wall clock) and
     by one pair of HIP events recorded on the launch stream: their interval / steps
@@ -145,6 +155,15 @@ def time_launches(torch, launch, n_sets, steps, warmup):
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         launch(i % n_sets)
+    if warm_ms > 0:
+        torch.cuda.synchronize()
+        t_w = time.perf_counter()
+        i = warmup
+        while (time.perf_counter() - t_w) * 1e3 < warm_ms:
+            for _ in range(10):
+                launch(i % n_sets)
+                i += 1
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
@@ -164,6 +183,12 @@ def time_launches(torch, launch, n_sets, steps, warmup):
     torch.cuda.synchronize()
     per = [a.elapsed_time(b) for a, b in ev]
     return wall / steps * 1e3, mean, statistics.median(per), min(per)
+
+
+def time_extra(torch, launch, n_sets, args):
+    """An extra leg: at least 50 warm-up launches and EXTRA_WARM_MS of warm-up
+    work, then at least 100 timed launches."""
+    return time_launches(torch, launch, n_sets, max(args.steps, 100), max(args.warmup, 50), warm_ms=EXTRA_WARM_MS)
 
 
 def roundtrip_leg_fn(torch, tah, synth, dev, stream_h, n_sets, args):
@@ -186,10 +211,9 @@ def roundtrip_leg_fn(torch, tah, synth, dev, stream_h, n_sets, args):
         wsl = torch.empty(cl.workspace_bytes, dtype=torch.uint8, device=dev)
         xb = x_sets[0].numel() * x_sets[0].element_size()
         nbytes = 2 * xb + cl.payload_bytes
-        # extra legs: at least 50 untimed and 100 timed launches (a freshly allocated
-        # buffer set of up to 2 GB runs its first launches slower)
-        l_ms, l_mean, _, _ = time_launches(torch, lambda i: cl.roundtrip(x_sets[i], pl_[i], yl[i], wsl, stream_h),
-                                           n_sets, max(args.steps, 100), max(args.warmup, 50))
+        # extra legs: at least 50 untimed launches and EXTRA_WARM_MS of untimed
+        # work, then at least 100 timed launches
+        l_ms, l_mean, _, _ = time_extra(torch, lambda i: cl.roundtrip(x_sets[i], pl_[i], yl[i], wsl, stream_h), n_sets, args)
         del yl, pl_, wsl
         gbps = nbytes / (l_mean * 1e-3) / 1e9
         return {"shape": f"{wl.tokens}x{wl.hidden} {'bf16' if wl.dtype == synth.BF16 else 'fp32'} tile {prm.tile}",
@@ -306,7 +330,8 @@ def main():
     roundtrip_leg = roundtrip_leg_fn(torch, tah, synth, dev, stream_h, n_sets, args)
 
     if not args.no_extras:
-        extras = {}
+        extras = {"timing": f"each extra leg: >= 50 warm-up launches and >= {EXTRA_WARM_MS:.0f} ms of warm-up "
+                            "work, then >= 100 timed launches (the headline: exactly --warmup and --steps)"}
         # the fused round trip of every workload shape (c5 is the headline, timed above)
         legs = {}
         for name in ("c1_256x512_f32_g32", "c2_4096x2048_bf16_g64", "c3_16384x4096_bf16_g64",
@@ -320,11 +345,9 @@ def main():
         extras["general_path_c5_k1"] = roundtrip_leg(
             WORKLOAD, params=dataclasses.replace(p, bit_budget=3.000001), x_sets=xs)
         # encode only and decode only on the same tensor
-        _, e_mean, _, _ = time_launches(torch, lambda i: codec.encode(xs[i], ps[i], ws, stream_h), n_sets,
-                                        args.steps, args.warmup)
+        _, e_mean, _, _ = time_extra(torch, lambda i: codec.encode(xs[i], ps[i], ws, stream_h), n_sets, args)
         extras["encode_gbps"] = round((x_bytes + codec.payload_bytes) / (e_mean * 1e-3) / 1e9, 1)
-        _, d_mean, _, _ = time_launches(torch, lambda i: codec.decode(ps[i], ys[i], ws, stream_h), n_sets,
-                                        args.steps, args.warmup)
+        _, d_mean, _, _ = time_extra(torch, lambda i: codec.decode(ps[i], ys[i], ws, stream_h), n_sets, args)
         extras["decode_gbps"] = round((x_bytes + codec.payload_bytes) / (d_mean * 1e-3) / 1e9, 1)
         extras["activation_gbps_roundtrip"] = round(x_bytes / (ms * 1e-3) / 1e9, 1)
         # general path with a mixed allocation (80% INT4 / 20% INT3) at the same shape
@@ -332,8 +355,7 @@ def main():
         cm = tah.Codec(T, C, wm.params, torch.bfloat16, torch.bfloat16)
         pm = [torch.empty(cm.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
         wsm = torch.empty(cm.workspace_bytes, dtype=torch.uint8, device=dev)
-        m_ms, _, _, _ = time_launches(torch, lambda i: cm.roundtrip(xs[i], pm[i], ys[i], wsm, stream_h), n_sets,
-                                      args.steps, args.warmup)
+        m_ms, _, _, _ = time_extra(torch, lambda i: cm.roundtrip(xs[i], pm[i], ys[i], wsm, stream_h), n_sets, args)
         extras["mixed_80_20_roundtrip_gbps"] = round((2 * x_bytes + cm.payload_bytes) / (m_ms * 1e-3) / 1e9, 1)
         extras["mixed_80_20_ms_per_step"] = round(m_ms, 5)
         del pm, wsm
@@ -343,8 +365,7 @@ def main():
             ca = tah.Codec(T, C, dataclasses.replace(wm.params, alloc_tile=A), torch.bfloat16, torch.bfloat16)
             pa = [torch.empty(ca.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
             wsa = torch.empty(ca.workspace_bytes, dtype=torch.uint8, device=dev)
-            a_ms, _, _, _ = time_launches(torch, lambda i: ca.roundtrip(xs[i], pa[i], ys[i], wsa, stream_h), n_sets,
-                                          args.steps, args.warmup)
+            a_ms, _, _, _ = time_extra(torch, lambda i: ca.roundtrip(xs[i], pa[i], ys[i], wsa, stream_h), n_sets, args)
             extras[f"mixed_80_20_{label}_roundtrip_gbps"] = round((2 * x_bytes + ca.payload_bytes) / (a_ms * 1e-3) / 1e9,
                                                                  1)
             del pa, wsa
@@ -354,8 +375,7 @@ def main():
         cgd = tah.Codec(T, C, wg.params, torch.bfloat16, torch.bfloat16)
         pgd = [torch.empty(cgd.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
         wsgd = torch.empty(cgd.workspace_bytes, dtype=torch.uint8, device=dev)
-        gd_ms, _, _, _ = time_launches(torch, lambda i: cgd.roundtrip(xs[i], pgd[i], ys[i], wsgd, stream_h), n_sets,
-                                       args.steps, args.warmup)
+        gd_ms, _, _, _ = time_extra(torch, lambda i: cgd.roundtrip(xs[i], pgd[i], ys[i], wsgd, stream_h), n_sets, args)
         extras["greedy_3_4_8_roundtrip_gbps"] = round((2 * x_bytes + cgd.payload_bytes) / (gd_ms * 1e-3) / 1e9, 1)
         extras["greedy_3_4_8_ms_per_step"] = round(gd_ms, 5)
         del pgd, wsgd
@@ -364,8 +384,7 @@ def main():
         for tau in (0.0, 4.0, math.inf):
             ct = tah.Codec(T, C, dataclasses.replace(p, tau=tau), torch.bfloat16, torch.bfloat16)
             pt = [torch.empty(ct.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
-            t_ms, _, _, _ = time_launches(torch, lambda i: ct.roundtrip(xs[i], pt[i], ys[i], ws, stream_h), n_sets,
-                                          args.steps, args.warmup)
+            t_ms, _, _, _ = time_extra(torch, lambda i: ct.roundtrip(xs[i], pt[i], ys[i], ws, stream_h), n_sets, args)
             taus[str(tau)] = round(bytes_step / (t_ms * 1e-3) / 1e9, 1)
             del pt
         extras["tau_sweep_roundtrip_gbps"] = taus
@@ -380,8 +399,7 @@ def main():
             rc = Lb.tah_hadamard(*h_args[0])
             if rc != 0:
                 raise RuntimeError(f"tah_hadamard({label}): {tah.status_string(rc)}")
-            _, h_mean, _, _ = time_launches(torch, lambda i: Lb.tah_hadamard(*h_args[i]), n_sets, args.steps,
-                                            args.warmup)
+            _, h_mean, _, _ = time_extra(torch, lambda i: Lb.tah_hadamard(*h_args[i]), n_sets, args)
             had[label] = round((x_bytes + 4 * T * C) / (h_mean * 1e-3) / 1e9, 1)
         extras["hadamard_alone_gbps"] = had
         del yh
@@ -399,23 +417,20 @@ def main():
         ne_args = [(gs[i].data_ptr(), 1, n_el, nb, nc, nps[i].data_ptr(), npb, stream_h) for i in range(n_sets)]
         nd_args = [(nps[i].data_ptr(), npb, n_el, nb, nc, ys[i].data_ptr(), 1, wsn.data_ptr(), 256, stream_h)
                    for i in range(n_sets)]
-        _, ne_mean, _, _ = time_launches(torch, lambda i: Lb.tah_naive_encode(*ne_args[i]), n_sets, args.steps,
-                                         args.warmup)
-        _, nd_mean, _, _ = time_launches(torch, lambda i: Lb.tah_naive_decode(*nd_args[i]), n_sets, args.steps,
-                                         args.warmup)
+        _, ne_mean, _, _ = time_extra(torch, lambda i: Lb.tah_naive_encode(*ne_args[i]), n_sets, args)
+        _, nd_mean, _, _ = time_extra(torch, lambda i: Lb.tah_naive_decode(*nd_args[i]), n_sets, args)
         extras["bw_naive8_encode_gbps"] = round((2 * n_el + npb) / (ne_mean * 1e-3) / 1e9, 1)
         extras["bw_naive8_decode_gbps"] = round((npb + 2 * n_el) / (nd_mean * 1e-3) / 1e9, 1)
         cg = tah.Codec(gw.tokens, gw.hidden, gw.params, torch.bfloat16, torch.bfloat16)
         pg = [torch.empty(cg.payload_bytes, dtype=torch.uint8, device=dev) for _ in range(n_sets)]
         wsg = torch.empty(cg.workspace_bytes, dtype=torch.uint8, device=dev)
-        g_ms, _, _, _ = time_launches(torch, lambda i: cg.roundtrip(gs[i], pg[i], ys[i], wsg, stream_h), n_sets,
-                                      args.steps, args.warmup)
+        g_ms, _, _, _ = time_extra(torch, lambda i: cg.roundtrip(gs[i], pg[i], ys[i], wsg, stream_h), n_sets, args)
         extras["bw_tah4_roundtrip_gbps"] = round((2 * 2 * n_el + cg.payload_bytes) / (g_ms * 1e-3) / 1e9, 1)
         del gs, nps, pg, wsg
         # achievable bandwidth of a plain 512 MB device copy
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
-        _, c_mean, _, _ = time_launches(torch, lambda i: dst.copy_(src), 1, 50, 5)
+        _, c_mean, _, _ = time_extra(torch, lambda i: dst.copy_(src), 1, args)
         extras["copy_512MB_gbps"] = round(2 * (512 << 20) / (c_mean * 1e-3) / 1e9, 1)
         del src, dst
         out["extras"] = extras
