@@ -130,9 +130,16 @@ struct GHistArgs {
   uint32_t* hist_cur;         // this pass's histograms (zero on entry)
   uint32_t* hist_clear;       // the next pass's histograms, cleared here
   uint32_t* cand;  // per sample: count, pad, then up to ncand (key, index) pairs
+  // fold (last key digit, one sample): each tile's level from the upgrades
+  // whose key lies above the 22-bit prefix, the 2-bit level map and each
+  // run's width sum; the upgrades that match the prefix are added by k_gresolve
+  uint32_t* fold_map;
+  uint32_t* fold_run;
   int64_t chunks_per_sample, R, ncand, cand_stride;
   GPass pass, prev;
   int32_t has_prev, last_key;  // last_key: the last of the three key digits
+  int32_t fold;
+  uint32_t cands;  // candidate widths, one byte each, c_1 lowest
 };
 
 // 4 tiles per thread: 256 workgroups for a million tiles fill the chip (with
@@ -183,6 +190,9 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
     const int64_t u = u0 + i * kGThreads + tid;
     hv[i] = u < a.g.N ? a.g.H[s * a.g.N + u] : 0.0f;
   }
+  int lv[kGPerThread];  // fold: upgrades of the tile above the prefix
+#pragma unroll
+  for (int i = 0; i < kGPerThread; ++i) lv[i] = 0;
   for (int j = 0; j < a.g.nl; ++j) {
     const uint32_t cost = (uint32_t)a.g.cost[j];
 #pragma unroll
@@ -195,6 +205,7 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
         C = composite(a.g, hv[i], u, j);
         want = hs >= 64 || (C >> hs) == want_hi;
         digit = (uint32_t)((C >> a.pass.shift) & dmask);
+        if (a.fold && hs < 64 && (C >> hs) > want_hi) ++lv[i];
       }
       if (a.last_key) {
         // upgrades whose key matches the prefix, a superset of the ties at
@@ -225,6 +236,27 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
         want = want && !same;
       }
       if (want) atomicAdd(&lh[digit], cost);
+    }
+  }
+  if (a.fold) {
+    // a wavefront's 64 tiles are one run: its level-map words and width sum
+    // (one sample, so the tile index is the upgrade's tile index)
+#pragma unroll
+    for (int i = 0; i < kGPerThread; ++i) {
+      const int64_t ub = u0 + i * kGThreads + (tid & ~63);
+      if (ub < a.g.N) {
+        const bool in = ub + lane < a.g.N;
+        const int l = in ? lv[i] : 0;
+        uint32_t f = (uint32_t)l << (2 * (lane & 15));
+#pragma unroll
+        for (int off = 1; off < 16; off <<= 1) f |= (uint32_t)__shfl_xor((int)f, off, 64);
+        int w = in ? (int)((a.cands >> (8 * l)) & 255u) : 0;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) w += __shfl_xor(w, off, 64);
+        const int64_t run = ub >> 6;
+        if ((lane & 15) == 0) a.fold_map[4 * run + (lane >> 4)] = f;
+        if (lane == 0) a.fold_run[run] = (uint32_t)w;
+      }
     }
   }
   __syncthreads();
@@ -258,15 +290,24 @@ struct GResolveArgs {
   GState* st_out;
   const uint32_t* hist_last;
   const uint32_t* cand;
+  // fold (one sample): the selected upgrades among those matching the 22-bit
+  // key prefix raise their tile's level and their run's width sum, which are
+  // then scanned into the block table and the total width
+  uint32_t* fold_map;
+  const uint32_t* fold_run;
+  uint32_t* table;
+  uint32_t* wtotal;
   int64_t ncand, cand_stride;
   GPass last;
-  int32_t nidx;
+  int32_t nidx, fold;
   GPass idx[3];  // digits of the upgrade index, top first
 };
 
 constexpr int kGResolveThreads = 1024;
 
 __global__ __launch_bounds__(kGResolveThreads) void k_gresolve(GResolveArgs a) {
+  extern __shared__ __attribute__((aligned(16))) uint32_t rs[];  // fold: the run width sums
+  __shared__ uint32_t wsum[kGResolveThreads / 64];
   __shared__ uint32_t lh[kBins];
   __shared__ GState ss;
   __shared__ uint32_t ipre_s;
@@ -323,6 +364,48 @@ __global__ __launch_bounds__(kGResolveThreads) void k_gresolve(GResolveArgs a) {
       r -= before;  // only wavefront 0's r is used
     }
     __syncthreads();
+  }
+  if (a.fold) {
+    // run width sums in LDS (kRound per round, zero past the runs), then the
+    // selected upgrades that match the prefix; e* itself is not selected
+    constexpr int kRound = 4 * kGResolveThreads;
+    constexpr int kPer = (int)(kFoldMaxRuns / kGResolveThreads);
+    const int64_t runs = (a.g.N + 63) / 64;
+    const int nr = (int)((runs + kRound - 1) / kRound);
+    {
+      uint32_t v[kPer];
+#pragma unroll
+      for (int i = 0; i < kPer; ++i) {
+        const int64_t j = (int64_t)i * kGResolveThreads + tid;
+        v[i] = 0u;
+        if (i < 4 * nr && j < runs) v[i] = a.fold_run[j];
+      }
+#pragma unroll
+      for (int i = 0; i < kPer; ++i)
+        if (i < 4 * nr) rs[i * kGResolveThreads + tid] = v[i];
+    }
+    __syncthreads();
+    const uint32_t ip = ipre_s;
+    for (int64_t i = tid; i < n; i += kGResolveThreads) {
+      uint32_t key, idx;
+      if (listed) {
+        key = lk[i].x;
+        idx = lk[i].y;
+      } else {
+        const int64_t u = i / a.g.nl;
+        const int j = (int)(i - u * a.g.nl);
+        key = (uint32_t)(composite(a.g, h[u], u, j) >> a.g.ib);
+        idx = (uint32_t)i;
+      }
+      if ((key >> 10) == (K >> 10) && (key > K || (key == K && idx < ip))) {
+        const uint32_t u = idx / (uint32_t)a.g.nl;
+        atomicAdd(&a.fold_map[u >> 4], 1u << (2 * (u & 15)));
+        atomicAdd(&rs[u >> 6], (uint32_t)a.g.cost[idx - u * (uint32_t)a.g.nl]);
+      }
+    }
+    __syncthreads();
+    const uint32_t total = lds_scan_store<kGResolveThreads, (int)(kFoldMaxRuns / kRound)>(rs, nr, 0u, a.table, runs, wsum);
+    if (tid == 0) *a.wtotal = total;
   }
   if (tid == 0) {
     GState T;
@@ -509,10 +592,21 @@ hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st
     if (e != hipSuccess) return e;
     final_st = states;
   } else if (pl.glevel < 0) {
+    // one sample of quantization tiles, few enough runs for one resolve
+    // workgroup: the level map, width sums, block table and total are built
+    // by the last key digit and k_gresolve (no k_glevel or k_table launch)
+    const bool fold = pl.kA == 1 && ns == 1 && (pl.N + 63) / 64 <= kFoldMaxRuns;
+    uint32_t* map = reinterpret_cast<uint32_t*>(P ? P + pl.off_bitmap : w + pl.ws_bitmap);
+    uint32_t* run_sums = reinterpret_cast<uint32_t*>(w + pl.ws_blockcnt);
+    uint32_t cands = 0;
+    for (int i = 0; i < pl.n_candidates; ++i) cands |= (uint32_t)pl.candidates[i] << (8 * i);
     uint32_t* hists = reinterpret_cast<uint32_t*>(w + pl.ws_hist);
     const int64_t hsz = ns * kBins;
     GHistArgs h;
     h.g = g;
+    h.fold_map = map;
+    h.fold_run = run_sums;
+    h.cands = cands;
     h.cand = reinterpret_cast<uint32_t*>(w + pl.ws_cand);
     h.chunks_per_sample = (pl.N + kGChunk - 1) / kGChunk;
     h.R = pl.R;
@@ -531,6 +625,7 @@ hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st
       h.hist_prev = hists + ((p + 2) % 3) * hsz;
       h.hist_cur = hists + (p % 3) * hsz;
       h.hist_clear = hists + ((p + 1) % 3) * hsz;
+      h.fold = fold && h.last_key;
       hipLaunchKernelGGL(k_ghist, dim3((unsigned)(h.chunks_per_sample * ns)), dim3(kGThreads), 0, st, h);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
@@ -547,9 +642,21 @@ hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st
     rs.last = pl.gpasses[np - 1];
     rs.nidx = pl.ngidx;
     for (int i = 0; i < 3; ++i) rs.idx[i] = pl.gidx[i];
-    hipLaunchKernelGGL(k_gresolve, dim3((unsigned)ns), dim3(kGResolveThreads), 0, st, rs);
+    rs.fold_map = map;
+    rs.fold_run = run_sums;
+    rs.table = reinterpret_cast<uint32_t*>(P ? P + pl.off_table : w + pl.ws_table);
+    rs.wtotal = reinterpret_cast<uint32_t*>(w + pl.ws_wtotal);
+    rs.fold = fold;
+    static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_gresolve),
+                                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                                       (int)(4 * kFoldMaxRuns));
+    if (attr != hipSuccess) return attr;
+    // the run width sums in whole rounds of 4 per thread
+    const int64_t round = 4 * kGResolveThreads;
+    const size_t rs_bytes = fold ? (size_t)(4 * (((pl.N + 63) / 64 + round - 1) / round) * round) : 0;
+    hipLaunchKernelGGL(k_gresolve, dim3((unsigned)ns), dim3(kGResolveThreads), rs_bytes, st, rs);
     const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || fold) return e;  // fold: level map, table and total are complete
   }
   LevelArgs L;
   L.g = g;

@@ -537,44 +537,9 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
     }
     __syncthreads();
     // block table: every earlier sample holds k upgraded tiles, then the
-    // exclusive scan of this sample's run counts; thread tid owns the 4 nr
-    // consecutive counts from 4 nr tid (nr 16-byte words)
-    constexpr int kMaxQ = (int)(kFoldMaxRuns / kRound);
-    uint4* seg = reinterpret_cast<uint4*>(rc) + tid * nr;
-    uint32_t c[4 * kMaxQ];
-#pragma unroll
-    for (int q = 0; q < kMaxQ; ++q) {
-      const uint4 w4 = q < nr ? seg[q] : make_uint4(0u, 0u, 0u, 0u);
-      c[4 * q] = w4.x;
-      c[4 * q + 1] = w4.y;
-      c[4 * q + 2] = w4.z;
-      c[4 * q + 3] = w4.w;
-    }
-    uint32_t tot = 0u;
-#pragma unroll
-    for (int i = 0; i < 4 * kMaxQ; ++i) tot += c[i];
-    const int lane = tid & 63, wave = tid >> 6;
-    uint32_t incl = tot;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const uint32_t o = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += o;
-    }
-    if (lane == 63) wsum[wave] = incl;
-    __syncthreads();
-    uint32_t run = (uint32_t)s * (uint32_t)a.k + incl - tot;
-    for (int w = 0; w < wave; ++w) run += wsum[w];
-#pragma unroll
-    for (int i = 0; i < 4 * kMaxQ; ++i) {
-      const uint32_t ci = c[i];
-      c[i] = run;
-      run += ci;
-    }
-#pragma unroll
-    for (int q = 0; q < kMaxQ; ++q)
-      if (q < nr) seg[q] = make_uint4(c[4 * q], c[4 * q + 1], c[4 * q + 2], c[4 * q + 3]);
-    __syncthreads();
-    for (int64_t j = tid; j < runs; j += kResolveThreads) a.table[r0 + j] = rc[j];  // coalesced
+    // exclusive scan of this sample's run counts
+    lds_scan_store<kResolveThreads, (int)(kFoldMaxRuns / kRound)>(rc, nr, (uint32_t)s * (uint32_t)a.k,
+                                                                    a.table + r0, runs, wsum);
   }
   if (tid == 0) a.st_out[s] = S;
 }

@@ -51,6 +51,24 @@ def test_degenerate_budgets(budget, cands, want):
         assert set(levels_used(R, pl).tolist()) == want
 
 
+@pytest.mark.parametrize("tokens,mult", [(97, 64), (130, 33), (257, 40)])
+def test_one_sample_levels_in_place(tokens, mult):
+    """One sample above the one-workgroup select (more than 4096 upgrades):
+    the last key digit writes the levels of the upgrades above the threshold's
+    prefix and each run's width sum, the resolve step adds the selected ones
+    that match the prefix and scans the sums into the table and the total;
+    tile counts that end inside a run, and a tensor of equal tiles (the list
+    of candidates overflows and the resolve step goes through every upgrade)."""
+    x = synth.random_tensor(tokens, 64 * mult, synth.BF16, tokens + mult, n_out=3, mult=40)
+    for budget, cands in ((3.37, (2, 3, 4, 8)), (4.6, (3, 4, 8)), (2.2, (2, 5))):
+        run_case(x, P(tile=64, tokens_per_sample=0, bit_budget=budget, candidates=cands, tau=2.0, allocator=GREEDY),
+                 f"greedy one sample t{tokens} m{mult} {budget} {cands}")
+    row = synth.random_tensor(1, 64, synth.F32, 7, n_out=1, mult=10)
+    z = np.tile(row, (tokens, mult)).astype(np.float32)
+    run_case(z, P(tile=64, tokens_per_sample=0, bit_budget=3.37, candidates=(2, 3, 4, 8), tau=2.0, allocator=GREEDY),
+             f"greedy one sample of equal tiles t{tokens} m{mult}")
+
+
 @pytest.mark.parametrize("tile", [32, 64, 128])
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
 def test_one_level_ragged(tile, dtype):
