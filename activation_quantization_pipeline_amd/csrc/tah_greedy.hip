@@ -334,7 +334,49 @@ __global__ __launch_bounds__(kGResolveThreads) void k_gresolve(GResolveArgs a) {
   }
   __syncthreads();
   const float* h = a.g.H + s * a.g.N;
-  for (int p = 0; p < a.nidx; ++p) {
+  // At most 64 listed upgrades with e*'s key: one wavefront gathers them and
+  // takes e* directly, the upgrade whose running cost in index order (lowest
+  // first) reaches r, the same upgrade the digit passes below would find.
+  __shared__ int few_done;
+  if (listed) {
+    if (tid < 64) {
+      const int lane = tid;
+      int cnt = 0;  // upgrades with key K gathered so far (uniform)
+      for (int64_t i0 = 0; i0 < nc && cnt <= 64; i0 += 64) {
+        const int64_t i = i0 + lane;
+        const bool tied = i < nc && lk[i].x == K;
+        const uint64_t m = ballot(tied);
+        const int pos = cnt + (int)lanes_below(m);
+        if (tied && pos < 64) lh[pos] = lk[i].y;
+        cnt += __popcll(m);
+      }
+      __threadfence_block();
+      int ok = 0;
+      if (cnt <= 64) {
+        const uint32_t mine = lane < cnt ? lh[lane] : 0xffffffffu;
+        const int64_t cost = lane < cnt ? (int64_t)a.g.cost[mine % (uint32_t)a.g.nl] : 0;
+        int64_t before = 0;  // cost of the tied upgrades with a lower index
+        for (int j = 0; j < cnt; ++j) {
+          const uint32_t o = (uint32_t)__shfl((int)mine, j, 64);
+          if (o < mine) before += (int64_t)a.g.cost[o % (uint32_t)a.g.nl];
+        }
+        const uint64_t hit = ballot(lane < cnt && before < r && r <= before + cost);
+        if (hit != 0) {
+          const int src = __ffsll((unsigned long long)hit) - 1;
+          const uint32_t e = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
+          const int64_t b = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(before >> 32), src) << 32) |
+                                      (uint32_t)__builtin_amdgcn_readlane((int)before, src));
+          r -= b;
+          if (lane == 0) ipre_s = e;
+          ok = 1;
+        }
+      }
+      if (lane == 0) few_done = ok;
+    }
+    __syncthreads();
+  }
+  const bool skip_idx = listed && few_done;
+  for (int p = 0; p < (skip_idx ? 0 : a.nidx); ++p) {
     const GPass ps = a.idx[p];
     for (int i = tid; i < kBins; i += kGResolveThreads) lh[i] = 0u;
     __syncthreads();

@@ -69,6 +69,30 @@ def test_one_sample_levels_in_place(tokens, mult):
              f"greedy one sample of equal tiles t{tokens} m{mult}")
 
 
+@pytest.mark.parametrize("budget", [2.86875, 3.84375, 7.475])
+def test_threshold_inside_a_small_tie(budget):
+    """One sample of 6144 tiles over {2, 3, 4, 8} with 40 copies of one tile:
+    at these budgets e*, the first upgrade that does not fit, is one of the
+    copies' equal upgrades, so the copies split between two levels by tile
+    index (a class of at most 64 upgrades, ranked by one wavefront)."""
+    rng = np.random.default_rng(5)
+    T, M, G = 96, 64, 64
+    tiles = rng.standard_normal((T * M, G)) * rng.choice([0.05, 1.0], (T * M, 1))
+    tiles[rng.integers(0, T * M, size=T * M // 8), rng.integers(0, G, size=T * M // 8)] *= 30
+    copy = rng.standard_normal(G)
+    copy[3] *= 5
+    idx = rng.choice(T * M, size=40, replace=False)
+    tiles[idx] = copy
+    x = tiles.reshape(T, M * G).astype(np.float32)
+    p = P(tile=G, tokens_per_sample=0, bit_budget=budget, candidates=(2, 3, 4, 8), tau=2.0, allocator=GREEDY)
+    R, _ = run_case(x, p, f"greedy small tie budget {budget}")
+    pl = oracle.plan(T, M * G, p)
+    words = R[pl["off_bitmap"]:pl["off_bitmap"] + 16 * pl["nblocks"]].view(np.uint32)
+    t = np.arange(pl["tiles"])
+    lv = (words[t // 16] >> (2 * (t % 16)).astype(np.uint32)) & 3
+    assert len(set(lv[idx].tolist())) == 2  # the threshold lies inside the copies' class
+
+
 @pytest.mark.parametrize("tile", [32, 64, 128])
 @pytest.mark.parametrize("dtype", [synth.F32, synth.BF16])
 def test_one_level_ragged(tile, dtype):
