@@ -142,13 +142,16 @@ struct GHistArgs {
   uint32_t cands;  // candidate widths, one byte each, c_1 lowest
 };
 
-// 4 tiles per thread: 256 workgroups for a million tiles fill the chip (with
-// five grid-wide digits, 16 per thread ran 29 us slower on an 8192 x 8192
-// tensor; 2 and 1 per thread, 15 and 43 us slower).
+// P tiles per thread (a chunk of 1024 P allocation tiles per workgroup), the
+// smallest P in {1, 2, 4} that keeps the grid within kGMaxWgs workgroups: a
+// million tiles at P = 4 fill the chip (with five grid-wide digits, 16 per
+// thread ran 29 us slower on an 8192 x 8192 tensor; 2 and 1 per thread, 15
+// and 43 us slower), while the four samples of 32,768 tiles of the 4096 x 2048
+// tensor take 128 workgroups at P = 1.
 constexpr int kGThreads = 1024;
-constexpr int kGPerThread = 4;
-constexpr int kGChunk = kGThreads * kGPerThread;  // allocation tiles per workgroup
+constexpr int64_t kGMaxWgs = 256;
 
+template <int P>
 __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
   __shared__ uint32_t lh[kBins];
   __shared__ GState ss;
@@ -157,7 +160,7 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int64_t s = blockIdx.x / a.chunks_per_sample;
   const int64_t c = blockIdx.x % a.chunks_per_sample;
-  const int64_t u0 = c * kGChunk;
+  const int64_t u0 = c * (int64_t)(kGThreads * P);
   {  // the next pass's histogram of this sample, cleared in slices by the sample's blocks
     const int64_t per = (kBins + a.chunks_per_sample - 1) / a.chunks_per_sample;
     const int64_t b0 = c * per, b1 = b0 + per < kBins ? b0 + per : kBins;
@@ -184,19 +187,19 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
   const int hs = a.pass.shift + a.pass.width;  // composite bits above the current digit
   const uint64_t dmask = (1ull << a.pass.width) - 1ull;
   const uint64_t want_hi = hs >= 64 ? 0ull : (S.prefix >> hs);
-  float hv[kGPerThread];  // all loads in flight before the first use
+  float hv[P];  // all loads in flight before the first use
 #pragma unroll
-  for (int i = 0; i < kGPerThread; ++i) {
+  for (int i = 0; i < P; ++i) {
     const int64_t u = u0 + i * kGThreads + tid;
     hv[i] = u < a.g.N ? a.g.H[s * a.g.N + u] : 0.0f;
   }
-  int lv[kGPerThread];  // fold: upgrades of the tile above the prefix
+  int lv[P];  // fold: upgrades of the tile above the prefix
 #pragma unroll
-  for (int i = 0; i < kGPerThread; ++i) lv[i] = 0;
+  for (int i = 0; i < P; ++i) lv[i] = 0;
   for (int j = 0; j < a.g.nl; ++j) {
     const uint32_t cost = (uint32_t)a.g.cost[j];
 #pragma unroll
-    for (int i = 0; i < kGPerThread; ++i) {
+    for (int i = 0; i < P; ++i) {
       const int64_t u = u0 + i * kGThreads + tid;
       bool want = false;
       uint32_t digit = 0;
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
     // a wavefront's 64 tiles are one run: its level-map words and width sum
     // (one sample, so the tile index is the upgrade's tile index)
 #pragma unroll
-    for (int i = 0; i < kGPerThread; ++i) {
+    for (int i = 0; i < P; ++i) {
       const int64_t ub = u0 + i * kGThreads + (tid & ~63);
       if (ub < a.g.N) {
         const bool in = ub + lane < a.g.N;
@@ -461,7 +464,7 @@ __global__ __launch_bounds__(kGResolveThreads) void k_gresolve(GResolveArgs a) {
 // key digits and the index digits of the select in LDS (the same composites,
 // costs and find_bin as k_ghist and k_gresolve) in one launch. Up to this size
 // the grid-wide digits would run one workgroup per sample as well.
-constexpr int64_t kGSmall = kGChunk;
+constexpr int64_t kGSmall = 4096;
 
 struct GSmallArgs {
   GArgs g;
@@ -650,7 +653,10 @@ hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st
     h.fold_run = run_sums;
     h.cands = cands;
     h.cand = reinterpret_cast<uint32_t*>(w + pl.ws_cand);
-    h.chunks_per_sample = (pl.N + kGChunk - 1) / kGChunk;
+    int per = 1;  // tiles per thread
+    while (per < 4 && ns * ((pl.N + kGThreads * per - 1) / (kGThreads * per)) > kGMaxWgs) per *= 2;
+    const int64_t chunk = (int64_t)kGThreads * per;
+    h.chunks_per_sample = (pl.N + chunk - 1) / chunk;
     h.R = pl.R;
     h.ncand = pl.ncand;
     h.cand_stride = pl.cand_stride;
@@ -668,7 +674,10 @@ hipError_t launch_greedy(const Plan& pl, void* payload, void* ws, hipStream_t st
       h.hist_cur = hists + (p % 3) * hsz;
       h.hist_clear = hists + ((p + 1) % 3) * hsz;
       h.fold = fold && h.last_key;
-      hipLaunchKernelGGL(k_ghist, dim3((unsigned)(h.chunks_per_sample * ns)), dim3(kGThreads), 0, st, h);
+      const dim3 grid((unsigned)(h.chunks_per_sample * ns));
+      if (per == 1) hipLaunchKernelGGL(k_ghist<1>, grid, dim3(kGThreads), 0, st, h);
+      else if (per == 2) hipLaunchKernelGGL(k_ghist<2>, grid, dim3(kGThreads), 0, st, h);
+      else hipLaunchKernelGGL(k_ghist<4>, grid, dim3(kGThreads), 0, st, h);
       const hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
