@@ -35,6 +35,7 @@
 // (k_gselect_small) in one launch.
 #include "tah_device.hpp"
 #include "tah_internal.hpp"
+#include "tah_scan.hpp"
 
 namespace tah {
 

@@ -44,6 +44,7 @@
 
 #include "tah_device.hpp"
 #include "tah_internal.hpp"
+#include "tah_scan.hpp"
 
 namespace tah {
 
