@@ -224,6 +224,12 @@ __device__ __forceinline__ bool quantize_tile(const EncArgs& a, float (&v)[G], i
   return pre;
 }
 
+// The quantizer that forms, packs and stores the codes word by word (defined
+// with the 128-channel kernel below).
+template <int G, int OUT, bool GUARD>
+__device__ __forceinline__ bool quantize_stream(const EncArgs& a, float (&v)[G], int64_t t, int b, int64_t code_off,
+                                                bool tr);
+
 // OUT: 0 = no reconstruction, 1 = fp32, 2 = bf16.
 // MODE: the width layout: 0 one width (the entropy is computed here), 1 two
 // widths from the 1-bit width map and the count table, 2 any candidate from
@@ -425,7 +431,10 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
           __syncthreads();
         }
       }
-      if (act) quantize_tile<G, OUT, MODE == 2>(a, v, t, b, code_off);
+      // codes packed word by word: the 64 codes never sit in registers at
+      // once (137 against 168 VGPRs with a spill; 43.5 -> 41.9 us for the
+      // 8192 x 8192 encode)
+      if (act) quantize_stream<G, OUT, MODE == 2>(a, v, t, b, code_off, false);
     } else if (act) {
       if (flag) {  // P_d in the lane's own row, then H of Eq. (4) in registers
         uint8_t* row = xs + lane * RI::kStride;
@@ -507,10 +516,21 @@ __device__ __forceinline__ void quant_pack(const EncArgs& a, float (&v)[G], floa
     w[i] = acc;
   }
   if (a.payload && (!GUARD || code_off + (int64_t)(G / 8) * B <= a.code_end)) {
-    static_assert(W % 4 == 0, "whole 16-byte stores");
-    uint4* dst = reinterpret_cast<uint4*>(a.payload + code_off);
+    // 16-, 8- or 4-byte stores by the block's size (every offset is a
+    // multiple of G/8 bytes)
+    if constexpr (W % 4 == 0) {
+      uint4* dst = reinterpret_cast<uint4*>(a.payload + code_off);
 #pragma unroll
-    for (int i = 0; i < W / 4; ++i) dst[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+      for (int i = 0; i < W / 4; ++i) dst[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+    } else if constexpr (W % 2 == 0) {
+      uint2* dst = reinterpret_cast<uint2*>(a.payload + code_off);
+#pragma unroll
+      for (int i = 0; i < W / 2; ++i) dst[i] = make_uint2(w[2 * i], w[2 * i + 1]);
+    } else {
+      uint32_t* dst = reinterpret_cast<uint32_t*>(a.payload + code_off);
+#pragma unroll
+      for (int i = 0; i < W; ++i) dst[i] = w[i];
+    }
   }
 }
 
