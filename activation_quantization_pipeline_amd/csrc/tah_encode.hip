@@ -3,8 +3,8 @@
 // A workgroup is one wavefront; it takes groups of 64 consecutive tiles, one
 // tile per lane:
 //  1. stage:   the 64 tiles (contiguous in HBM) arrive with 16-byte coalesced
-//              loads (in the round trip prefetched one group ahead) and go into
-//              padded LDS rows;
+//              loads (in the round trip and the mixed-width encoder prefetched
+//              one group ahead) and go into padded LDS rows;
 //  2. phase A: lane i reads tile i from LDS and computes the outlier ratio of
 //              Eq. (3) (top-2 magnitudes, pivot d, flag) and, for a uniform
 //              allocation, the tile entropy of Eq. (1)-(2); with a mixed
@@ -235,9 +235,9 @@ __device__ __forceinline__ bool quantize_stream(const EncArgs& a, float (&v)[G],
 // widths from the 1-bit width map and the count table, 2 any candidate from
 // the 2-bit level map and the width-sum table.
 // A workgroup is one wavefront with LDS rows of its own, and it is persistent:
-// group g of 64 tiles goes to workgroup g mod gridDim.x. In the round trip,
-// groups of small tiles are prefetched into registers while the current group
-// is processed.
+// group g of 64 tiles goes to workgroup g mod gridDim.x. In the round trip
+// and the mixed-width encoder, groups of small tiles are prefetched into
+// registers while the current group is processed.
 //
 // In the round trip a flagged tile (Eq. 3) is transformed by its own lane
 // with fwht<G>, the stage order of the oracle. The wavefront runs the
@@ -252,10 +252,12 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
   using RI = TileRow<G, TIn>;
   using TOut = typename std::conditional<OUT == 1, float, bf16_t>::type;
   using RO = TileRow<G, TOut>;
-  // The next group is prefetched into registers in the round trip; the
-  // encode-only kernel leaves those 32 registers to its three waves per SIMD
-  // (41.4 us against 44.4 us at two waves with the prefetch).
-  constexpr bool kPrefetch = RI::kChunks <= 8 && OUT != 0;
+  // The next group is prefetched into registers in the round trip and in the
+  // encode-only kernel of the mixed layouts (8192 x 8192 at the 80/20 split:
+  // 107.7 -> 100.7 us per encode). The encode-only kernel with one width,
+  // which also computes the entropies, runs faster without it (41.9 against
+  // 45.4 us at 8192 x 8192, three waves per SIMD either way).
+  constexpr bool kPrefetch = RI::kChunks <= 8 && (OUT != 0 || MIXED);
   // Each LDS row is read and rewritten only by its own lane, so a rebuilt tile
   // goes back into its own row when rows have the same width; otherwise
   // rebuilt tiles get rows of their own.
