@@ -358,6 +358,15 @@ def main():
         m_ms, _, _, _ = time_extra(torch, lambda i: cm.roundtrip(xs[i], pm[i], ys[i], wsm, stream_h), n_sets, args)
         extras["mixed_80_20_roundtrip_gbps"] = round((2 * x_bytes + cm.payload_bytes) / (m_ms * 1e-3) / 1e9, 1)
         extras["mixed_80_20_ms_per_step"] = round(m_ms, 5)
+        # the sender's and the receiver's side of that allocation apart (one stage
+        # encodes, the next decodes): the encode runs the statistics pass, the
+        # select and the encoder; the decode reads the payload it wrote
+        _, me_mean, _, _ = time_extra(torch, lambda i: cm.encode(xs[i], pm[i], wsm, stream_h), n_sets, args)
+        extras["mixed_80_20_encode_gbps"] = round((x_bytes + cm.payload_bytes) / (me_mean * 1e-3) / 1e9, 1)
+        extras["mixed_80_20_encode_ms"] = round(me_mean, 5)
+        _, md_mean, _, _ = time_extra(torch, lambda i: cm.decode(pm[i], ys[i], wsm, stream_h), n_sets, args)
+        extras["mixed_80_20_decode_gbps"] = round((x_bytes + cm.payload_bytes) / (md_mean * 1e-3) / 1e9, 1)
+        extras["mixed_80_20_decode_ms"] = round(md_mean, 5)
         del pm, wsm
         # allocation tiles of several quantization tiles (Sec. 3.2), up to token-level
         # allocation (A = hidden), at the same 80/20 split
