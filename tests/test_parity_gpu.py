@@ -626,3 +626,17 @@ def test_random_larger_configurations(seed):
         y16, _ = tah.roundtrip(to_dev(x), p, torch.bfloat16)
         assert_decoded_equal(to_host(y16), oracle.decode(R, tokens, hidden, p, oracle.BF16), R,
                              oracle.plan(tokens, hidden, p), f"larger random config {seed} bf16 out")
+
+
+@pytest.mark.parametrize("tile,dtype", [(64, synth.BF16), (32, synth.F32), (32, synth.BF16)])
+def test_ragged_tail_with_several_groups_per_workgroup(tile, dtype):
+    # 9001 tokens of 37 tiles: 333,037 tiles, more 64-tile groups than the
+    # encoder has resident workgroups, so workgroups prefetch further groups
+    # and one of them ends on a group of 45 tiles; uniform, top-p and greedy
+    x = synth.random_tensor(9001, tile * 37, dtype, 4242 + tile, n_out=3, mult=40)
+    run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=3.0, candidates=(3, 4, 8), tau=2.0),
+             f"ragged tail t{tile} uniform")
+    run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0),
+             f"ragged tail t{tile} top-p")
+    run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=3.3, candidates=(2, 3, 4, 8), tau=2.0, allocator=1),
+             f"ragged tail t{tile} greedy")
