@@ -640,3 +640,53 @@ def test_ragged_tail_with_several_groups_per_workgroup(tile, dtype):
              f"ragged tail t{tile} top-p")
     run_case(x, P(tile=tile, tokens_per_sample=0, bit_budget=3.3, candidates=(2, 3, 4, 8), tau=2.0, allocator=1),
              f"ragged tail t{tile} greedy")
+
+
+@pytest.mark.parametrize("budget", [3.0, 3.8])
+def test_beyond_2_31_elements(budget):
+    # 513 samples of one 64 x 65536 bf16 block: 2,151,677,952 elements (past 2^31;
+    # input and output offsets past 2^32 bytes). Every sample is the same
+    # block, so each sample's allocation, payload sections and rebuilt rows are the
+    # oracle's encoding of that block, shifted by the sample's position; sampled
+    # samples (first, middle, last) are compared byte for byte. Uniform 3-bit and
+    # the 80/20 split (the grid-wide select with the width map written in place).
+    reps, T, C = 513, 64, 65536
+    B = synth.random_tensor(T, C, synth.BF16, 31, n_out=3, mult=40)
+    p = P(tile=64, tokens_per_sample=T, bit_budget=budget, candidates=(3, 4, 8), tau=2.0)
+    say(f"[large] {reps * T}x{C} bf16, budget {budget}")
+    R = oracle.encode(B, p)
+    plb = oracle.plan(T, C, p)
+    y_ref = oracle.decode(R, T, C, p, oracle.BF16)
+    pl = oracle.plan(reps * T, C, p)
+    assert pl["tiles"] * 64 > 2 ** 31 and pl["total"] < 2 ** 32
+    xt = to_dev(B).repeat(reps, 1)
+    y, Pg = tah.roundtrip(xt, p, torch.bfloat16)
+    y2 = tah.decode(Pg, reps * T, C, p, torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(y.view(torch.int16), y2.view(torch.int16)), "decode of the payload differs from the round trip"
+    del xt, y2
+    n = plb["tiles"]  # tiles per sample
+    k = plb["k"]
+    sz_lo, sz_hi = 8 * plb["b_lo"], 8 * plb["b_hi"]
+    code_b = n * sz_lo + k * (sz_hi - sz_lo)  # code bytes of one sample
+    assert code_b == plb["code_bytes"]
+
+    def sec(t, off, width, count):
+        return to_host(Pg[off + width * t: off + width * (t + count)])
+
+    for s in (0, reps // 2, reps - 1):
+        t0 = s * n
+        what = f"sample {s} of {reps}, budget {budget}"
+        for name, w in (("side", 1), ("scale", 2), ("zero", 4)):
+            got = sec(t0, pl[f"off_{name}"], w, n)
+            want = R[plb[f"off_{name}"]: plb[f"off_{name}"] + w * n]
+            assert np.array_equal(got, want), f"{what}: {name} differs"
+        got = to_host(Pg[pl["off_bitmap"] + t0 // 8: pl["off_bitmap"] + (t0 + n) // 8])
+        assert np.array_equal(got, R[plb["off_bitmap"]: plb["off_bitmap"] + n // 8]), f"{what}: width map differs"
+        tab = to_host(Pg[pl["off_table"] + 4 * (t0 // 64): pl["off_table"] + 4 * ((t0 + n) // 64)]).view(np.uint32)
+        tab_b = R[plb["off_table"]: plb["off_table"] + 4 * (n // 64)].view(np.uint32)
+        assert np.array_equal(tab, tab_b + np.uint32(s * k)), f"{what}: block table differs"
+        c0 = pl["off_codes"] + s * code_b
+        got = to_host(Pg[c0: c0 + code_b])
+        assert np.array_equal(got, R[plb["off_codes"]: plb["off_codes"] + code_b]), f"{what}: codes differ"
+        assert np.array_equal(to_host(y[s * T:(s + 1) * T]), y_ref), f"{what}: rebuilt rows differ"
