@@ -197,15 +197,15 @@ struct HistArgs {
 };
 
 // Large workgroups of P keys per thread (a chunk of 1024 P keys each, whole
-// runs of 64 tiles). The launch takes the smallest P in {1, 2, 4} that keeps
-// the grid within kHistMaxWgs workgroups: a million keys at P = 4 (256
-// workgroups) fill the chip and few enough add into the same global bins
-// (P = 16 left three quarters of it idle; P = 2 and 1 add too many global
-// atomics: 125.3 -> 135.4 us per 80/20 round trip at 8192 x 8192), while
-// 131,072 keys run best as 128 workgroups of P = 1 (4096 x 2048 round trip:
-// 45.5 us at P = 4, 42.8 at P = 2, 42.0 at P = 1).
+// runs of 64 tiles). The launch takes the smallest P in {1, 2, 4, 8} that
+// keeps the grid within kHistMaxWgs workgroups: a million keys at P = 8 (128
+// workgroups) add fewer partial histograms into the same global bins than at
+// P = 4 (80/20 round trip at 8192 x 8192: 121.4 -> 120.8 us; P = 16 left most
+// of the chip idle; P = 2 and 1 added too many global atomics: 125.3 -> 135.4
+// us against P = 4), while 131,072 keys run best as 128 workgroups of P = 1
+// (4096 x 2048 round trip: 45.5 us at P = 4, 42.8 at P = 2, 42.0 at P = 1).
 constexpr int kHistThreads = 1024;
-constexpr int64_t kHistMaxWgs = 256;
+constexpr int64_t kHistMaxWgs = 128;
 
 // Apply one pass to a sample's state: one wavefront scans the pass's histogram
 // in order (descending digits for the entropy key, ascending for the tile
@@ -843,7 +843,7 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   h.nsamples = pl.nsamples;
   h.k = pl.k;
   int per = 1;  // keys per thread
-  while (per < 4 && pl.nsamples * ((pl.N + kHistThreads * per - 1) / (kHistThreads * per)) > kHistMaxWgs) per *= 2;
+  while (per < 8 && pl.nsamples * ((pl.N + kHistThreads * per - 1) / (kHistThreads * per)) > kHistMaxWgs) per *= 2;
   const int64_t chunk = (int64_t)kHistThreads * per;
   h.chunks_per_sample = (pl.N + chunk - 1) / chunk;
   h.cand = reinterpret_cast<uint32_t*>(w + pl.ws_cand);
@@ -869,7 +869,8 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
     h.fold = pl.fold && h.pass.last_h;
     if (per == 1) hipLaunchKernelGGL(k_hist<1>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
     else if (per == 2) hipLaunchKernelGGL(k_hist<2>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
-    else hipLaunchKernelGGL(k_hist<4>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
+    else if (per == 4) hipLaunchKernelGGL(k_hist<4>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
+    else hipLaunchKernelGGL(k_hist<8>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
