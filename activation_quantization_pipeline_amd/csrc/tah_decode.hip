@@ -1,7 +1,8 @@
 // Decode kernel of the TAH-Quant codec for gfx950 (Algorithm 1, the receiver's step: the
-// receiving stage dequantizes). A workgroup is one wavefront and is
-// persistent: group g of 64 consecutive tiles (one per lane) goes to
-// workgroup g mod gridDim.x.
+// receiving stage dequantizes). A workgroup is one wavefront: group g of 64
+// consecutive tiles (one per lane) goes to workgroup g mod gridDim.x (one
+// workgroup per group for tiles of up to 64 channels, a persistent grid of
+// the resident workgroups for 128, see launch_dec_b).
 //  - the payload header is checked once against the expected one (shape,
 //    params, section offsets); on a mismatch the status word is set and
 //    nothing is written;
@@ -326,12 +327,20 @@ static int dec_cu_count() {
   return cus;
 }
 
+// Tiles of up to 64 channels: one workgroup per group (8192 x 8192 bf16
+// decode 29.9 -> 27.2 us, the 80/20 one 31.8 -> 30.2 us against a persistent
+// grid of the resident workgroups, one box, interleaved); tiles of 128 fp32
+// channels keep the persistent grid and its pipeline across groups (16384 x
+// 5120: 100.4 against 108.3 us with a workgroup per group).
 template <int G, typename TOut, int MAXB, bool MULTI>
 static hipError_t launch_dec_b(const DecArgs& a, hipStream_t st) {
-  static const int per_cu = dec_wgs_per_cu(k_decode<G, TOut, MAXB, MULTI>);
   const int64_t ngroups = a.tiles > 0 ? (a.tiles + 63) / 64 : 1;
-  const int64_t resident = (int64_t)per_cu * dec_cu_count();
-  const int64_t nwg = ngroups < resident ? ngroups : resident;
+  int64_t nwg = ngroups;
+  if constexpr (G > 64) {
+    static const int per_cu = dec_wgs_per_cu(k_decode<G, TOut, MAXB, MULTI>);
+    const int64_t resident = (int64_t)per_cu * dec_cu_count();
+    nwg = ngroups < resident ? ngroups : resident;
+  }
   hipLaunchKernelGGL((k_decode<G, TOut, MAXB, MULTI>), dim3((unsigned)nwg), dim3(64), 0, st, a);
   return hipGetLastError();
 }
