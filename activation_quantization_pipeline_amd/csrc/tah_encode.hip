@@ -49,15 +49,22 @@ struct EncArgs {
   PadRanges pads;
 };
 
-template <int G, typename T>
-constexpr int tiles_per_wg() {
-  return TileRow<G, T>::kBytes <= 128 ? 256 : (TileRow<G, T>::kBytes <= 256 ? 128 : 64);
+// The one-width round trip of bf16 tiles of up to 64 channels with a bf16
+// output runs four wavefronts per SIMD (at most 128 VGPRs, and 10 KB of LDS
+// per workgroup, so sixteen share a compute unit): its statistics and entropy
+// are formed from the LDS row chunk by chunk, the tile is read again to be
+// quantized, and no next group is prefetched into registers. 8192 x 8192:
+// 57.2 -> 55.3 us (58.7 against 60.8 us in the first launches after an idle
+// spell), 16384 x 4096 59.0 -> 57.2 us, one box, interleaved.
+template <int G, typename T, int OUT, int MODE>
+constexpr bool kFourWaves() {
+  return G <= 64 && Elem<T>::kBytes == 2 && OUT == 2 && MODE == 0;
 }
 
 // Minimum waves per SIMD the register allocator must leave room for.
-template <int G, typename T, int OUT>
+template <int G, typename T, int OUT, int MODE>
 constexpr int kMinWaves() {
-  return (G <= 64 && Elem<T>::kBytes == 2) ? 3 : (G <= 64 ? 2 : 1);
+  return kFourWaves<G, T, OUT, MODE>() ? 4 : ((G <= 64 && Elem<T>::kBytes == 2) ? 3 : (G <= 64 ? 2 : 1));
 }
 
 template <int G, int B>
@@ -157,6 +164,45 @@ __device__ __forceinline__ void tile_stats(const uint8_t* row, float (&v)[G], fl
   }
 }
 
+// Phase-A statistics and entropy of a bf16 tile read from its LDS row chunk
+// by chunk: the same m1, m2, d as tile_stats and the same entropy as
+// tile_entropy (L and S summed left to right from 0), without the G values
+// held in registers at once.
+template <int G>
+__device__ __forceinline__ float tile_stats_entropy_bf16(const uint8_t* row, const float* lt, float& m1, float& m2,
+                                                         int& d) {
+  const uint4* p = reinterpret_cast<const uint4*>(row);
+  float l1 = 0.0f, S = 0.0f;
+  uint32_t k1 = 0u, k2 = 0u;
+#pragma unroll
+  for (int c = 0; c < G / 8; ++c) {
+    const uint4 q = p[c];
+    const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int k = 8 * c + 2 * i;
+      uint32_t xl, xh;  // opaque widened values (see tile_stats)
+      asm("v_lshlrev_b32 %0, 16, %1" : "=v"(xl) : "v"(u[i]));
+      asm("v_and_b32 %0, 0xffff0000, %1" : "=v"(xh) : "v"(u[i]));
+      const float vl = __uint_as_float(xl), vh = __uint_as_float(xh);
+      const uint32_t kl = (xl & 0x7fff0000u) | (uint32_t)(G - 1 - k);
+      const uint32_t kh = (u[i] & 0x7fff0000u) | (uint32_t)(G - 2 - k);
+      l1 = l1 + fabsf(vl);
+      k2 = umed3(k2, kl, k1);
+      k1 = max(k1, kl);
+      S = __builtin_fmaf(fabsf(vl), log2_node(vl, lt), S);
+      l1 = l1 + fabsf(vh);
+      k2 = umed3(k2, kh, k1);
+      k1 = max(k1, kh);
+      S = __builtin_fmaf(fabsf(vh), log2_node(vh, lt), S);
+    }
+  }
+  m1 = __uint_as_float(k1 & 0xffff0000u);
+  m2 = __uint_as_float(k2 & 0xffff0000u);
+  d = G - 1 - (int)(k1 & 0xffffu);
+  return entropy_from_sums(l1, S, lt);
+}
+
 // Whether the receiver's H then 1/G (Eq. 4 inverted) may take the 1/G first,
 // as fmaf(q, s/G, lo/G), with bit-identical results. G is a power of two, so
 // scaling by 1/G commutes with every rounding that stays in the normal range.
@@ -248,7 +294,7 @@ __device__ __forceinline__ bool quantize_stream(const EncArgs& a, float (&v)[G],
 // through LDS (barriers and round trips per group), forward and inverse or
 // forward alone. The encode-only kernel does hand them over (see kCoopH).
 template <int G, typename TIn, int OUT, int MODE>
-__global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncArgs a) {
+__global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT, MODE>())) void k_encode(EncArgs a) {
   constexpr int NT = 64;
   constexpr bool MIXED = MODE != 0;
   using RI = TileRow<G, TIn>;
@@ -259,15 +305,13 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
   // 107.7 -> 100.7 us per encode). The encode-only kernel with one width,
   // which also computes the entropies, runs faster without it (41.9 against
   // 45.4 us at 8192 x 8192, three waves per SIMD either way).
-  constexpr bool kPrefetch = RI::kChunks <= 8 && (OUT != 0 || MIXED);
+  constexpr bool kFour = kFourWaves<G, TIn, OUT, MODE>();
+  constexpr bool kPrefetch = RI::kChunks <= 8 && (OUT != 0 || MIXED) && !kFour;
   // Each LDS row is read and rewritten only by its own lane, so a rebuilt tile
   // goes back into its own row when rows have the same width; otherwise
   // rebuilt tiles get rows of their own.
   constexpr bool kSameRow = OUT == 0 || RO::kStride == RI::kStride;
 
-  __shared__ __attribute__((aligned(16))) uint8_t xs[NT * RI::kStride];
-  __shared__ __attribute__((aligned(16))) uint8_t ys_own[kSameRow ? 16 : NT * RO::kStride];
-  __shared__ __attribute__((aligned(16))) float lt[256];  // log2 tables of the entropy
   // Encode only (OUT == 0): flagged tiles go through H by 16-lane groups, kCoop
   // tiles per round through fp32 slots (44.7 us against 47.7 us per-lane for
   // the 8192 x 8192 encode). The round trip keeps the per-lane butterflies
@@ -277,9 +321,21 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
   constexpr int V = G / 16;     // elements per lane in a 16-lane transform group
   constexpr int kCoop = 8;      // flagged tiles per round
   constexpr int kSlot = G + 4;  // fp32 slot stride
-  __shared__ __attribute__((aligned(16))) float ts[kCoopH ? kCoop * kSlot : 4];
-  __shared__ uint32_t flist[kCoopH ? NT : 1];
-  uint8_t* ys = kSameRow ? xs : ys_own;
+  // One LDS block with only what this instantiation uses: the tile rows, rows
+  // for rebuilt tiles of another width, the transform slots and list of the
+  // encode-only kernel, the log2 tables of the entropy (one width only).
+  constexpr int kXs = NT * RI::kStride;
+  constexpr int kYs = kSameRow ? 0 : NT * RO::kStride;
+  constexpr int kTs = kCoopH ? 4 * kCoop * kSlot : 0;
+  constexpr int kFl = kCoopH ? 4 * NT : 0;
+  constexpr int kLt = MIXED ? 0 : 4 * 256;
+  static_assert(!kFour || kXs + kLt <= 10240, "sixteen workgroups per compute unit");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[kXs + kYs + kTs + kFl + kLt];
+  uint8_t* xs = smem;
+  uint8_t* ys = kSameRow ? xs : smem + kXs;
+  float* ts = reinterpret_cast<float*>(smem + kXs + kYs);
+  uint32_t* flist = reinterpret_cast<uint32_t*>(smem + kXs + kYs + kTs);
+  float* lt = reinterpret_cast<float*>(smem + kXs + kYs + kTs + kFl);
 
   const int lane = threadIdx.x;
   const int q4 = lane >> 4, r16 = lane & 15;
@@ -343,12 +399,17 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
     float v[G];
     if (act) {
       if constexpr (!MIXED) {
-        float m1, m2, l1;
+        float m1, m2;
         int d;
-        tile_stats<G, TIn>(xs + lane * RI::kStride, v, m1, m2, d, l1);
+        if constexpr (kFour) {
+          a.H[t] = tile_stats_entropy_bf16<G>(xs + lane * RI::kStride, lt, m1, m2, d);  // Eq. (1)-(2)
+        } else {
+          float l1;
+          tile_stats<G, TIn>(xs + lane * RI::kStride, v, m1, m2, d, l1);
+          a.H[t] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);  // Eq. (1)-(2)
+        }
         flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
         piv = d;
-        a.H[t] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);  // Eq. (1)-(2)
         // side byte: the flag, and the pivot of a transformed tile (0 for the others)
         if (a.payload) a.payload[a.off_side + t] = (uint8_t)(flag ? (0x80 | piv) : 0);
       } else {
@@ -445,9 +506,10 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT>())) void k_encode(EncAr
         const uint32_t x0 = lds_elem_bits<TIn>(row, 0), xd = lds_elem_bits<TIn>(row, piv);
         lds_elem_set<TIn>(row, 0, xd);
         lds_elem_set<TIn>(row, piv, x0);
-        lds_read_tile<G, TIn>(row, v);
-        fwht<G>(v);
+        if constexpr (!kFour) lds_read_tile<G, TIn>(row, v);
       }
+      if constexpr (kFour) lds_read_tile<G, TIn>(xs + lane * RI::kStride, v);  // the tile again
+      if (flag) fwht<G>(v);
       const bool scaled = quantize_tile<G, OUT, MODE == 2>(a, v, t, b, code_off, flag != 0);
       if constexpr (OUT != 0) {
         if (flag) fwht<G>(v);  // H^T = H
