@@ -49,16 +49,18 @@ struct EncArgs {
   PadRanges pads;
 };
 
-// The one-width round trip of bf16 tiles of up to 64 channels with a bf16
-// output runs four wavefronts per SIMD (at most 128 VGPRs, and 10 KB of LDS
-// per workgroup, so sixteen share a compute unit): its statistics and entropy
-// are formed from the LDS row chunk by chunk, the tile is read again to be
-// quantized, and no next group is prefetched into registers. 8192 x 8192:
-// 57.2 -> 55.3 us (58.7 against 60.8 us in the first launches after an idle
-// spell), 16384 x 4096 59.0 -> 57.2 us, one box, interleaved.
+// The round trip of bf16 tiles of up to 64 channels with a bf16 output runs
+// four wavefronts per SIMD (at most 128 VGPRs, and at most 10 KB of LDS per
+// workgroup, so sixteen share a compute unit): with one width its statistics
+// and entropy are formed from the LDS row chunk by chunk, every layout reads
+// the tile from its row when it quantizes it (the mixed layouts with the
+// word-by-word quantizer), and no next group is prefetched into registers.
+// 8192 x 8192 one width: 57.2 -> 55.3 us (58.7 against 60.8 us in the first
+// launches after an idle spell), 16384 x 4096 59.0 -> 57.2 us; at the 80/20
+// split 118.6 -> 116.6 us, greedy 124.7 -> 123.4 us (one box, interleaved).
 template <int G, typename T, int OUT, int MODE>
 constexpr bool kFourWaves() {
-  return G <= 64 && Elem<T>::kBytes == 2 && OUT == 2 && MODE == 0;
+  return G <= 64 && Elem<T>::kBytes == 2 && OUT == 2;
 }
 
 // Minimum waves per SIMD the register allocator must leave room for.
@@ -417,7 +419,7 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT, MODE>())) void k_encode
         const uint32_t sb = a.side_in[t];
         flag = (int)(sb >> 7);
         piv = (int)(sb & 127u);
-        lds_read_tile<G, TIn>(xs + lane * RI::kStride, v);
+        if constexpr (!kFour) lds_read_tile<G, TIn>(xs + lane * RI::kStride, v);
         if constexpr (MODE == 1) {
           hi = (a.bitmap[t >> 5] >> (t & 31)) & 1u;
         } else {
@@ -508,9 +510,11 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT, MODE>())) void k_encode
         lds_elem_set<TIn>(row, piv, x0);
         if constexpr (!kFour) lds_read_tile<G, TIn>(row, v);
       }
-      if constexpr (kFour) lds_read_tile<G, TIn>(xs + lane * RI::kStride, v);  // the tile again
+      if constexpr (kFour) lds_read_tile<G, TIn>(xs + lane * RI::kStride, v);  // the tile from its row
       if (flag) fwht<G>(v);
-      const bool scaled = quantize_tile<G, OUT, MODE == 2>(a, v, t, b, code_off, flag != 0);
+      bool scaled;
+      if constexpr (kFour && MIXED) scaled = quantize_stream<G, OUT, MODE == 2>(a, v, t, b, code_off, flag != 0);
+      else scaled = quantize_tile<G, OUT, MODE == 2>(a, v, t, b, code_off, flag != 0);
       if constexpr (OUT != 0) {
         if (flag) fwht<G>(v);  // H^T = H
         // the 1/G where the dequantization did not take it (rare: skipped by
