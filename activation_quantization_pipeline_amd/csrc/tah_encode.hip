@@ -49,18 +49,23 @@ struct EncArgs {
   PadRanges pads;
 };
 
-// The round trip of bf16 tiles of up to 64 channels with a bf16 output runs
-// four wavefronts per SIMD (at most 128 VGPRs, and at most 10 KB of LDS per
-// workgroup, so sixteen share a compute unit): with one width its statistics
-// and entropy are formed from the LDS row chunk by chunk, every layout reads
-// the tile from its row when it quantizes it (the mixed layouts with the
-// word-by-word quantizer), and no next group is prefetched into registers.
-// 8192 x 8192 one width: 57.2 -> 55.3 us (58.7 against 60.8 us in the first
-// launches after an idle spell), 16384 x 4096 59.0 -> 57.2 us; at the 80/20
-// split 118.6 -> 116.6 us, greedy 124.7 -> 123.4 us (one box, interleaved).
+// The round trip of bf16 tiles of up to 64 channels with a bf16 output, and
+// the encode-only kernel of such tiles with one width, run four wavefronts per
+// SIMD (at most 128 VGPRs, and at most 10 KB of LDS per workgroup, so sixteen
+// share a compute unit): with one width the statistics and entropy are formed
+// from the LDS row chunk by chunk, every layout reads the tile from its row
+// when it quantizes it (with the word-by-word quantizer unless one width is
+// rebuilt), the flagged tiles are transformed by their own lanes, and no next
+// group is prefetched into registers. 8192 x 8192 one width: round trip 57.2
+// -> 55.3 us (58.7 against 60.8 us in the first launches after an idle
+// spell), encode only 41.3 -> 40.1 us; 16384 x 4096: round trip 59.0 -> 57.2
+// us, encode only 49.4 -> 41.7 us; round trip at the 80/20 split 118.6 ->
+// 116.6 us, greedy 124.7 -> 123.4 us (one box, interleaved). The mixed-width
+// encode-only kernel stays at three wavefronts (the 80/20 encode at 8192 x
+// 8192: 100.1 against 101.1 us at four).
 template <int G, typename T, int OUT, int MODE>
 constexpr bool kFourWaves() {
-  return G <= 64 && Elem<T>::kBytes == 2 && OUT == 2;
+  return G <= 64 && Elem<T>::kBytes == 2 && (OUT == 2 || (OUT == 0 && MODE == 0));
 }
 
 // Minimum waves per SIMD the register allocator must leave room for.
@@ -314,12 +319,13 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT, MODE>())) void k_encode
   // rebuilt tiles get rows of their own.
   constexpr bool kSameRow = OUT == 0 || RO::kStride == RI::kStride;
 
-  // Encode only (OUT == 0): flagged tiles go through H by 16-lane groups, kCoop
-  // tiles per round through fp32 slots (44.7 us against 47.7 us per-lane for
-  // the 8192 x 8192 encode). The round trip keeps the per-lane butterflies
-  // (60.8 us against 63.5 us): there the cooperative form, forward and
-  // inverse, cost more in registers and barriers than it saved.
-  constexpr bool kCoopH = OUT == 0;
+  // Encode only at three wavefronts (the mixed layouts): flagged tiles go
+  // through H by 16-lane groups, kCoop tiles per round through fp32 slots
+  // (44.7 us against 47.7 us per-lane for the 8192 x 8192 encode at the time).
+  // The round trip keeps the per-lane butterflies (60.8 us against 63.5 us):
+  // there the cooperative form, forward and inverse, cost more in registers
+  // and barriers than it saved; so does the four-wave encode-only kernel.
+  constexpr bool kCoopH = OUT == 0 && !kFourWaves<G, TIn, OUT, MODE>();
   constexpr int V = G / 16;     // elements per lane in a 16-lane transform group
   constexpr int kCoop = 8;      // flagged tiles per round
   constexpr int kSlot = G + 4;  // fp32 slot stride
@@ -513,7 +519,7 @@ __global__ __launch_bounds__(64, (kMinWaves<G, TIn, OUT, MODE>())) void k_encode
       if constexpr (kFour) lds_read_tile<G, TIn>(xs + lane * RI::kStride, v);  // the tile from its row
       if (flag) fwht<G>(v);
       bool scaled;
-      if constexpr (kFour && MIXED) scaled = quantize_stream<G, OUT, MODE == 2>(a, v, t, b, code_off, flag != 0);
+      if constexpr (kFour && (MIXED || OUT == 0)) scaled = quantize_stream<G, OUT, MODE == 2>(a, v, t, b, code_off, flag != 0);
       else scaled = quantize_tile<G, OUT, MODE == 2>(a, v, t, b, code_off, flag != 0);
       if constexpr (OUT != 0) {
         if (flag) fwht<G>(v);  // H^T = H
