@@ -69,47 +69,14 @@ __device__ __forceinline__ uint64_t composite(const GArgs& g, float h, int64_t u
 // below the cost of all upgrades.
 template <bool DESC>
 __device__ __forceinline__ void find_bin(const uint32_t* h, int64_t r, uint32_t& digit, int64_t& before_out) {
-  const int lane = threadIdx.x & 63;
-  constexpr int PER = kBins / 64;
-  uint32_t c[PER];
-  uint64_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    c[i] = h[DESC ? kBins - 1 - (lane * PER + i) : lane * PER + i];
-    sum += c[i];
+  // the plan keeps a sample's cost of all upgrades below 2^32, so r and every
+  // partial sum of a histogram fit in 32 bits
+  uint32_t cnt, before = 0;
+  if (r < 1 || r > (int64_t)0xffffffff || !find_rank<kBins>(h, DESC, (uint32_t)r, digit, cnt, before)) {
+    digit = 0u;  // cannot happen for 1 <= r <= total
+    before = 0u;
   }
-  uint64_t incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  const uint64_t excl = incl - sum;
-  const bool here = (int64_t)excl < r && r <= (int64_t)incl;
-  const uint64_t hm = ballot(here);
-  if (hm == 0) {  // cannot happen for 1 <= r <= total
-    digit = 0u;
-    before_out = 0;
-    return;
-  }
-  const int src = __ffsll((unsigned long long)hm) - 1;
-  int ord = 0;
-  int64_t before = 0;
-  if (here) {
-    before = (int64_t)excl;
-    ord = lane * PER;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (before + (int64_t)c[i] >= r) {
-        ord = lane * PER + i;
-        break;
-      }
-      before += c[i];
-    }
-  }
-  ord = __shfl(ord, src, 64);
-  before_out = (int64_t)__shfl((long long)before, src, 64);
-  digit = (uint32_t)(DESC ? kBins - 1 - ord : ord);
+  before_out = (int64_t)before;
 }
 
 // Narrows a sample's state to the bin of a composite digit.
@@ -154,7 +121,7 @@ constexpr int64_t kGMaxWgs = 256;
 
 template <int P>
 __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
-  __shared__ uint32_t lh[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kBins];
   __shared__ GState ss;
   __shared__ uint2 lc[kCandPerChunk];  // candidates of the last key digit
   __shared__ uint32_t lcn, lbase;
@@ -312,7 +279,7 @@ constexpr int kGResolveThreads = 1024;
 __global__ __launch_bounds__(kGResolveThreads) void k_gresolve(GResolveArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t rs[];  // fold: the run width sums
   __shared__ uint32_t wsum[kGResolveThreads / 64];
-  __shared__ uint32_t lh[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kBins];
   __shared__ GState ss;
   __shared__ uint32_t ipre_s;
   __shared__ uint2 lk[kMaxCand];
@@ -477,7 +444,7 @@ struct GSmallArgs {
 };
 
 __global__ __launch_bounds__(kGThreads) void k_gselect_small(GSmallArgs a) {
-  __shared__ uint32_t lh[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kBins];
   __shared__ GState ss;
   __shared__ uint32_t ipre_s;
   const int tid = threadIdx.x, lane = tid & 63;

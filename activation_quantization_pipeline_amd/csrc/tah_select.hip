@@ -10,8 +10,9 @@
 //              sums (L, S) instead and k_alloc_entropy adds them up per
 //              allocation tile, left to right, into its entropy;
 //   k_hist   - one launch per digit pass. Each workgroup first applies the
-//              previous pass (one wavefront scans that pass's histogram of the
-//              sample in order and finds the digit that holds rank r), then
+//              previous pass (one wavefront reads that pass's histogram of the
+//              sample in coalesced slices and finds the digit that holds rank
+//              r), then
 //              builds a 2048-bin LDS histogram of the current digit over the
 //              keys that still match the prefix (lanes of a wavefront that
 //              share a digit add once: entropy keys cluster) and adds it into
@@ -207,55 +208,16 @@ struct HistArgs {
 constexpr int kHistThreads = 1024;
 constexpr int64_t kHistMaxWgs = 128;
 
-// Apply one pass to a sample's state: one wavefront scans the pass's histogram
-// in order (descending digits for the entropy key, ascending for the tile
-// index) and finds the digit where the running count reaches r.
+// Apply one pass to a sample's state: one wavefront finds the bin of the
+// pass's histogram where the running count, bins in order (descending digits
+// for the entropy key, ascending for the tile index), reaches r.
 __device__ __forceinline__ SampleState apply_pass(SampleState S, const uint32_t* h, const SelectPass& ps) {
-  const int lane = threadIdx.x & 63;
   if (ps.kind == 1 && S.tie_all) return S;
-  constexpr int PER = kBins / 64;
-  uint32_t c[PER];
-  uint32_t sum = 0;
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int ord = lane * PER + i;
-    const int bin = ps.kind == 0 ? (kBins - 1 - ord) : ord;
-    c[i] = h[bin];
-    sum += c[i];
-  }
-  // inclusive prefix of the per-lane sums over the wave
-  uint64_t incl = sum;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const uint64_t o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
-  }
-  const uint64_t excl = incl - sum;
-  const bool here = (int64_t)excl < S.r && S.r <= (int64_t)incl;
-  const uint64_t hm = ballot(here);
-  if (hm == 0) return S;  // rank beyond the histogram: cannot happen for 1 <= r <= count
-  const int src = __ffsll((unsigned long long)hm) - 1;
-  uint32_t digit = 0, cnt = 0;
-  int64_t before = 0;
-  if (here) {
-    before = (int64_t)excl;
-    int ord = lane * PER;
-#pragma unroll
-    for (int i = 0; i < PER; ++i) {
-      if (before + (int64_t)c[i] >= S.r) {
-        ord = lane * PER + i;
-        cnt = c[i];
-        break;
-      }
-      before += c[i];
-    }
-    digit = (uint32_t)(ps.kind == 0 ? (kBins - 1 - ord) : ord);
-  }
-  digit = (uint32_t)__builtin_amdgcn_readlane((int)digit, src);
-  cnt = (uint32_t)__builtin_amdgcn_readlane((int)cnt, src);
-  before = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(before >> 32), src) << 32) |
-                     (uint32_t)__builtin_amdgcn_readlane((int)before, src));
-  S.r -= before;
+  uint32_t digit, cnt, before;
+  // a sample holds fewer than 2^31 keys, so r and every count fit in 32 bits
+  if (!find_rank<kBins>(h, ps.kind == 0, (uint32_t)S.r, digit, cnt, before))
+    return S;  // rank beyond the histogram: cannot happen for 1 <= r <= count
+  S.r -= (int64_t)before;
   if (ps.kind == 0) {
     S.key |= digit << ps.shift;
     if (ps.last_h) {
@@ -270,7 +232,7 @@ __device__ __forceinline__ SampleState apply_pass(SampleState S, const uint32_t*
 
 template <int P>
 __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
-  __shared__ uint32_t lh[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kBins];
   __shared__ SampleState ss;
   __shared__ uint2 lc[kCandPerChunk];  // candidates of the last entropy pass
   __shared__ uint32_t lcn, lbase;
@@ -416,7 +378,7 @@ constexpr int kResolveThreads = 1024;
 
 __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
   extern __shared__ __attribute__((aligned(16))) uint32_t rc[];  // fold: the sample's run counts
-  __shared__ uint32_t lh[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kBins];
   __shared__ SampleState ss;
   __shared__ uint2 lk[kMaxCand];  // the sample's candidate list
   __shared__ uint32_t wsum[kResolveThreads / 64];
@@ -583,7 +545,7 @@ struct LdsSelectArgs {
 
 __global__ __launch_bounds__(kLdsThreads) void k_select_lds(LdsSelectArgs a) {
   extern __shared__ uint32_t keys[];  // the sample's N keys
-  __shared__ uint32_t lh[kBins];
+  __shared__ __attribute__((aligned(16))) uint32_t lh[kBins];
   __shared__ SampleState ss;
   __shared__ uint32_t wsum[kLdsThreads / 64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
