@@ -193,10 +193,10 @@ __global__ __launch_bounds__(kGThreads) void k_ghist(GHistArgs a) {
             lc[pos] = make_uint2((uint32_t)(C >> a.g.ib), (uint32_t)((uint64_t)u * (uint64_t)a.g.nl + (uint64_t)j));
         }
       }
-      // lanes with the same digit as the first remaining lane add together
-      // (twice), the rest one by one
+      // first digit: lanes with the same digit as the first remaining lane
+      // add together (twice), the rest one by one (later digits spread)
 #pragma unroll
-      for (int round = 0; round < 2; ++round) {
+      for (int round = 0; !a.has_prev && round < 2; ++round) {
         const uint64_t wm = ballot(want);
         if (wm == 0) break;
         const int leader = __ffsll((unsigned long long)wm) - 1;
@@ -285,6 +285,15 @@ __global__ __launch_bounds__(kGResolveThreads) void k_gresolve(GResolveArgs a) {
   __shared__ uint2 lk[kMaxCand];
   const int tid = threadIdx.x;
   const int64_t s = blockIdx.x;
+  // the listed pairs into LDS by the other wavefronts while the first one
+  // applies the last key digit
+  const uint32_t* cl = a.cand + s * a.cand_stride;
+  if (tid >= 64) {
+    const int64_t nc0 = cl[0];
+    if (nc0 <= a.ncand)
+      for (int64_t i = tid - 64; i < nc0; i += kGResolveThreads - 64)
+        lk[i] = reinterpret_cast<const uint2*>(cl + 2)[i];
+  }
   if (tid < 64) {
     const GState S = apply_gpass(a.st_prev[s], a.hist_last + s * kBins, a.last);
     if (tid == 0) {
@@ -296,14 +305,9 @@ __global__ __launch_bounds__(kGResolveThreads) void k_gresolve(GResolveArgs a) {
   const GState S = ss;
   const uint32_t K = (uint32_t)(S.prefix >> a.g.ib);
   int64_t r = S.r;
-  const uint32_t* cl = a.cand + s * a.cand_stride;
   const int64_t nc = cl[0];
   const bool listed = nc <= a.ncand;  // else go through every upgrade of the sample
   const int64_t n = listed ? nc : a.g.N * a.g.nl;
-  if (listed) {
-    for (int64_t i = tid; i < nc; i += kGResolveThreads) lk[i] = reinterpret_cast<const uint2*>(cl + 2)[i];
-  }
-  __syncthreads();
   const float* h = a.g.H + s * a.g.N;
   // At most 64 listed upgrades with e*'s key: one wavefront gathers them and
   // takes e* directly, the upgrade whose running cost in index order (lowest
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(kGThreads) void k_gselect_small(GSmallArgs a) {
           digit = (uint32_t)((C >> ps.shift) & dmask);
         }
 #pragma unroll
-        for (int round = 0; round < 2; ++round) {
+        for (int round = 0; p == 0 && round < 2; ++round) {  // first digit only, as in k_ghist
           const uint64_t wm = ballot(want);
           if (wm == 0) break;
           const int leader = __ffsll((unsigned long long)wm) - 1;

@@ -14,8 +14,9 @@
 //              sample in coalesced slices and finds the digit that holds rank
 //              r), then
 //              builds a 2048-bin LDS histogram of the current digit over the
-//              keys that still match the prefix (lanes of a wavefront that
-//              share a digit add once: entropy keys cluster) and adds it into
+//              keys that still match the prefix (on the first digit, where
+//              entropy keys cluster, lanes of a wavefront that share a digit
+//              add once) and adds it into
 //              the sample's global histogram. Three passes cover the 32-bit
 //              order-preserving entropy key. Histograms rotate over three
 //              buffers (read the previous, add to the current, clear the next)
@@ -312,10 +313,12 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
         }
       }
     }
-    // lanes with the same digit as the first remaining lane add together (twice),
-    // the rest one by one
+    // first digit (entropy keys cluster there): lanes with the same digit as
+    // the first remaining lane add together (twice), the rest one by one; the
+    // later digits spread over the bins, and every lane adds its own key
+    // (80/20 round trip at 8192 x 8192: 114.0 -> 111.6 us)
 #pragma unroll
-    for (int round = 0; round < 2; ++round) {
+    for (int round = 0; !a.has_prev && round < 2; ++round) {
       const uint64_t wm = ballot(want);
       if (wm == 0) break;
       const int leader = __ffsll((unsigned long long)wm) - 1;
@@ -396,6 +399,14 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
     rv[i] = 0u;
     if (i < 4 * nr && j < runs) rv[i] = a.fold_run[r0 + j];
   }
+  // the listed pairs into LDS by the other wavefronts while the first one
+  // applies the last pass
+  const uint32_t* cl = a.cand + s * a.cand_stride;
+  if (tid >= 64) {
+    const int64_t nc0 = cl[0];
+    if (nc0 <= a.ncand)
+      for (int64_t i = tid - 64; i < nc0; i += kResolveThreads - 64) lk[i] = reinterpret_cast<const uint2*>(cl + 2)[i];
+  }
   if (tid < 64) {
     const SampleState S = apply_pass(a.st_prev[s], a.hist_last + s * kBins, a.last);
     if (tid == 0) ss = S;
@@ -403,14 +414,9 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
   __syncthreads();
   SampleState S = ss;
   const float* h = a.H + s * a.N;
-  const uint32_t* cl = a.cand + s * a.cand_stride;
   const int64_t nc = cl[0];
   const bool listed = nc <= a.ncand;  // else scan the whole sample
   const int64_t n = listed ? nc : a.N;
-  if (listed && (!S.tie_all || a.fold)) {
-    for (int64_t i = tid; i < nc; i += kResolveThreads) lk[i] = reinterpret_cast<const uint2*>(cl + 2)[i];
-    __syncthreads();
-  }
   // Few tied keys (at most 64, listed): one wavefront gathers their tile
   // indexes and takes the r-th lowest directly, the same index the digit
   // passes below would find.
@@ -594,10 +600,10 @@ __global__ __launch_bounds__(kLdsThreads) void k_select_lds(LdsSelectArgs a) {
           digit = (u >> ps.shift) & dmask;
         }
       }
-      // lanes with the same digit as the first remaining lane add together
-      // (twice: entropy keys cluster), the rest one by one
+      // first digit: lanes with the same digit as the first remaining lane
+      // add together (twice: entropy keys cluster), the rest one by one
 #pragma unroll
-      for (int round = 0; round < 2; ++round) {
+      for (int round = 0; p == 0 && round < 2; ++round) {
         const uint64_t wm = ballot(want);
         if (wm == 0) break;
         const int leader = __ffsll((unsigned long long)wm) - 1;
