@@ -12,12 +12,11 @@
 //   k_hist   - one launch per digit pass. Each workgroup first applies the
 //              previous pass (one wavefront reads that pass's histogram of the
 //              sample in coalesced slices and finds the digit that holds rank
-//              r), then
-//              builds a 2048-bin LDS histogram of the current digit over the
-//              keys that still match the prefix (on the first digit, where
-//              entropy keys cluster, lanes of a wavefront that share a digit
-//              add once) and adds it into
-//              the sample's global histogram. Three passes cover the 32-bit
+//              r), then builds a 2048-bin LDS histogram of the current digit
+//              over the keys that still match the prefix (on the first digit,
+//              where entropy keys cluster, lanes of a wavefront that share a
+//              digit add once) and adds it into the sample's global
+//              histogram. Three passes cover the 32-bit
 //              order-preserving entropy key. Histograms rotate over three
 //              buffers (read the previous, add to the current, clear the next)
 //              and states over two, so kernel boundaries are the only
