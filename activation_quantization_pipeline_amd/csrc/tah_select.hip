@@ -67,14 +67,15 @@ struct StatsArgs {
   int32_t init;
 };
 
-// Tiles (= threads) per workgroup of the statistics pass. Rows of up to 128
-// bytes take one-wavefront workgroups: 4096 x 2048 bf16 (131,072 tiles) then
+// Tiles (= threads) per workgroup of the statistics pass for rows of up to 128
+// bytes: one-wavefront workgroups, so 4096 x 2048 bf16 (131,072 tiles)
 // spreads over 2,048 workgroups instead of 512, eight per compute unit (round
 // trip 43.0 -> 41.6 us; 8192 x 8192 within 0.3 us; 128 and 512 tiles per
-// workgroup were no faster).
+// workgroup were no faster). Wider rows take k_stats_rounds below.
 template <int G, typename TIn>
 constexpr int stats_tiles_per_wg() {
-  return TileRow<G, TIn>::kBytes <= 128 ? 64 : (TileRow<G, TIn>::kBytes <= 256 ? 128 : 64);
+  static_assert(TileRow<G, TIn>::kBytes <= 128, "wider rows are staged in rounds");
+  return 64;
 }
 
 // SIDE: also the outlier test of Eq. (3), m1 > tau (m2 + rho), and the side
@@ -118,6 +119,151 @@ __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsA
   }
 }
 
+// Tiles wider than 128 bytes (fp32 tiles of 64 or 128 elements, bf16 tiles of
+// 128): a whole tile row per lane needs 272 or 528 bytes of LDS per tile and
+// up to 128 registers for its values, which left one or two wavefronts per
+// SIMD. Here a one-wavefront workgroup of 64 tiles stages each tile 128 bytes
+// at a time (rounds r = 0, 1, ...: bytes 128 r ... 128 r + 127 of every tile
+// into 144-byte LDS rows, 10 KB with the log2 table, so 16 workgroups share a
+// compute unit), the next round's loads in flight while the lane streams the
+// current one, and carries the statistics from round to round in element
+// order: the same operations in the same order as tile_stats_regs,
+// tile_logsum and tile_entropy over the whole tile.
+template <int G, typename TIn>
+constexpr int stats_rounds() { return G * Elem<TIn>::kBytes / 128; }
+
+template <int G, typename TIn, bool SUMS, bool SIDE>
+__global__ __launch_bounds__(64) void k_stats_rounds(StatsArgs a) {
+  constexpr int NT = 64;
+  constexpr int EB = Elem<TIn>::kBytes;
+  constexpr int kBytes = G * EB;
+  constexpr int R = stats_rounds<G, TIn>();
+  constexpr int kStride = 128 + 16;
+  static_assert(R >= 2 && R * 128 == kBytes, "rows of whole 128-byte rounds");
+  __shared__ __attribute__((aligned(16))) uint8_t xs[NT * kStride];
+  __shared__ __attribute__((aligned(16))) float lt[256];  // log2 tables of the entropy
+  const int tid = threadIdx.x;
+  const int64_t t0 = (int64_t)blockIdx.x * NT;
+  if (a.init) {  // the first selection pass's histograms start at zero
+    const int64_t gid = (int64_t)blockIdx.x * NT + tid, gsz = (int64_t)gridDim.x * NT;
+    for (int64_t i = gid; i < a.hist_words; i += gsz) a.hist[i] = 0u;
+  }
+  const int n = (int)((a.tiles - t0) < NT ? (a.tiles - t0) : NT);
+  if (n <= 0) return;
+  load_log2_tab(lt);
+  // chunk c = tid + 64 i of a round: tile c / 8, 16-byte part c % 8 of the
+  // round's 128 bytes (eight lanes read one 128-byte line)
+  const uint8_t* base = a.x + t0 * kBytes;
+  uint4 cur[8], nxt[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int c = tid + 64 * i;
+    cur[i] = (c >> 3) < n ? *reinterpret_cast<const uint4*>(base + (int64_t)(c >> 3) * kBytes + (c & 7) * 16)
+                          : make_uint4(0u, 0u, 0u, 0u);
+  }
+  float s = 0.0f, S = 0.0f, a1 = 0.0f, a2 = 0.0f;  // fp32: sums, top two magnitudes
+  int dd = 0;
+  uint32_t k1 = 0u, k2 = 0u;  // bf16: top-two keys
+  const uint4* rd = reinterpret_cast<const uint4*>(xs + tid * kStride);
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    if (r > 0) __syncthreads();  // every lane is done with the previous round's rows
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int c = tid + 64 * i;
+      *reinterpret_cast<uint4*>(xs + (c >> 3) * kStride + (c & 7) * 16) = cur[i];
+    }
+    __syncthreads();
+    if (r + 1 < R) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int c = tid + 64 * i;
+        nxt[i] = (c >> 3) < n ? *reinterpret_cast<const uint4*>(base + (int64_t)(c >> 3) * kBytes + (r + 1) * 128 +
+                                                                 (c & 7) * 16)
+                              : make_uint4(0u, 0u, 0u, 0u);
+      }
+    }
+    if (tid < n) {
+#pragma unroll
+      for (int cc = 0; cc < 8; ++cc) {
+        const uint4 q = rd[cc];
+        const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+        if constexpr (EB == 2) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k = 64 * r + 8 * cc + 2 * i;
+            uint32_t xl, xh;  // the widened values, opaque (one bit-field extract for the table)
+            asm("v_lshlrev_b32 %0, 16, %1" : "=v"(xl) : "v"(u[i]));
+            asm("v_and_b32 %0, 0xffff0000, %1" : "=v"(xh) : "v"(u[i]));
+            const float vl = __uint_as_float(xl), vh = __uint_as_float(xh);
+            s = s + fabsf(vl);
+            if constexpr (SIDE) {
+              const uint32_t kl = (xl & 0x7fff0000u) | (uint32_t)(G - 1 - k);
+              k2 = umed3(k2, kl, k1);
+              k1 = max(k1, kl);
+            }
+            S = __builtin_fmaf(fabsf(vl), log2_node(vl, lt), S);
+            s = s + fabsf(vh);
+            if constexpr (SIDE) {
+              const uint32_t kh = (u[i] & 0x7fff0000u) | (uint32_t)(G - 2 - k);
+              k2 = umed3(k2, kh, k1);
+              k1 = max(k1, kh);
+            }
+            S = __builtin_fmaf(fabsf(vh), log2_node(vh, lt), S);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int k = 32 * r + 4 * cc + i;
+            const float av = fabsf(__uint_as_float(u[i]));
+            s = s + av;
+            if constexpr (SIDE) {
+              if (k == 0) {
+                a1 = av;
+                a2 = 0.0f;
+                dd = 0;
+              } else {
+                const bool c = av > a1;
+                a2 = __builtin_amdgcn_fmed3f(a2, av, a1);
+                a1 = fmaxf(a1, av);
+                dd = c ? k : dd;
+              }
+            }
+            S = __builtin_fmaf(av, log2_full(av, lt), S);
+          }
+        }
+      }
+    }
+    if (r + 1 < R) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
+    }
+  }
+  if (tid < n) {
+    if constexpr (SIDE) {
+      float m1, m2;
+      int d;
+      if constexpr (EB == 2) {
+        m1 = __uint_as_float(k1 & 0xffff0000u);
+        m2 = __uint_as_float(k2 & 0xffff0000u);
+        d = G - 1 - (int)(k1 & 0xffffu);
+      } else {
+        m1 = a1;
+        m2 = a2;
+        d = dd;
+      }
+      const bool flag = m1 > a.tau * (m2 + kRho);  // Eq. (3) without the division
+      a.side[t0 + tid] = (uint8_t)(flag ? (0x80 | d) : 0);
+    }
+    if constexpr (SUMS) {
+      asm volatile("" : "+v"(S));  // the sum is complete here
+      a.ls[t0 + tid] = make_float2(s, S);
+    } else {
+      a.h[t0 + tid] = entropy_from_sums(s, S, lt);  // Eq. (1)-(2)
+    }
+  }
+}
+
 // Entropy of each allocation tile u of kA quantization tiles (u * kA ...
 // u * kA + kA - 1): their sums added left to right from 0, then the identity
 // H = log2 L - S / L.
@@ -142,13 +288,22 @@ __global__ __launch_bounds__(256) void k_alloc_entropy(const float2* ls, float* 
 
 template <int G, typename TIn>
 static hipError_t launch_stats_t(const StatsArgs& a, bool sums, hipStream_t st) {
-  constexpr int NT = stats_tiles_per_wg<G, TIn>();
-  const int64_t nwg = a.tiles > 0 ? (a.tiles + NT - 1) / NT : 1;
-  const dim3 grid((unsigned)nwg), block(NT);
-  if (sums && a.side) hipLaunchKernelGGL((k_stats<G, TIn, true, true>), grid, block, 0, st, a);
-  else if (sums) hipLaunchKernelGGL((k_stats<G, TIn, true, false>), grid, block, 0, st, a);
-  else if (a.side) hipLaunchKernelGGL((k_stats<G, TIn, false, true>), grid, block, 0, st, a);
-  else hipLaunchKernelGGL((k_stats<G, TIn, false, false>), grid, block, 0, st, a);
+  if constexpr (G * Elem<TIn>::kBytes > 128) {
+    const int64_t nwg = a.tiles > 0 ? (a.tiles + 63) / 64 : 1;
+    const dim3 grid((unsigned)nwg), block(64);
+    if (sums && a.side) hipLaunchKernelGGL((k_stats_rounds<G, TIn, true, true>), grid, block, 0, st, a);
+    else if (sums) hipLaunchKernelGGL((k_stats_rounds<G, TIn, true, false>), grid, block, 0, st, a);
+    else if (a.side) hipLaunchKernelGGL((k_stats_rounds<G, TIn, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_stats_rounds<G, TIn, false, false>), grid, block, 0, st, a);
+  } else {
+    constexpr int NT = stats_tiles_per_wg<G, TIn>();
+    const int64_t nwg = a.tiles > 0 ? (a.tiles + NT - 1) / NT : 1;
+    const dim3 grid((unsigned)nwg), block(NT);
+    if (sums && a.side) hipLaunchKernelGGL((k_stats<G, TIn, true, true>), grid, block, 0, st, a);
+    else if (sums) hipLaunchKernelGGL((k_stats<G, TIn, true, false>), grid, block, 0, st, a);
+    else if (a.side) hipLaunchKernelGGL((k_stats<G, TIn, false, true>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_stats<G, TIn, false, false>), grid, block, 0, st, a);
+  }
   return hipGetLastError();
 }
 
