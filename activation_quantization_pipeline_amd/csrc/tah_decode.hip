@@ -1,16 +1,16 @@
-// Decode kernel of the TAH-Quant codec for gfx950 (Algorithm 1, the receiver's step: the
-// receiving stage dequantizes). A workgroup is one wavefront: group g of 64
-// consecutive tiles (one per lane) goes to workgroup g mod gridDim.x (one
-// workgroup per group for tiles of up to 64 channels, a persistent grid of
-// the resident workgroups for 128, see launch_dec_b).
+// Decode kernels of the TAH-Quant codec for gfx950 (Algorithm 1, the receiver's step: the
+// receiving stage dequantizes). A workgroup is one wavefront and takes one
+// group of 64 consecutive tiles. k_decode (tiles of up to 64 channels) gives
+// each lane a tile; k_decode4 (128 channels, below) rebuilds the tiles by
+// quads of lanes.
 //  - the payload header is checked once against the expected one (shape,
 //    params, section offsets); on a mismatch the status word is set and
 //    nothing is written;
-//  - a software pipeline hides the dependent loads: a group's metadata (side
-//    byte, scale, zero-point, width-map words, block-table entry) is loaded
-//    two groups ahead; its code region (contiguous in the payload, located by
-//    the block table and the width map) one group ahead, with 16-byte
-//    coalesced loads into registers;
+//  - a group's code region (contiguous in the payload, located by the block
+//    table and the width map) arrives by 16-byte coalesced loads; k_decode
+//    also keeps a software pipeline for a grid smaller than the number of
+//    groups (metadata two groups ahead, the region one group ahead), idle
+//    under the launch below, which gives every group a workgroup;
 //  - processing: the region goes to LDS, each lane reads its code block,
 //    unpacks and dequantizes (fmaf(q, s, lo)); flagged tiles get H^T / G and
 //    the swap undone (§3.3) by 16-lane groups through fp32 LDS slots (which
@@ -308,40 +308,180 @@ __global__ __launch_bounds__(64) void k_decode(DecArgs a) {
   if (prev_t0 >= 0) stage_out<G, TOut, NT>(ys, a.y + prev_t0 * RO::kBytes, prev_n);
 }
 
-template <typename K>
-static int dec_wgs_per_cu(K kernel) {
-  int n = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, 64, 0) != hipSuccess || n < 1) n = 1;
-  return n;
+// The unnormalized Sylvester transform of a tile spread over an aligned
+// quad of lanes, lane r holding elements [r V, r V + V): the stages h < V
+// inside the lane, then h = V (partner lane r xor 1) and h = 2V (r xor 2).
+// Every butterfly is the single-rounded a + b / a - b of fwht<G> in the same
+// stage order (the upper lane forms partner - own with one fma), so the
+// result is that of fwht<4 V>.
+template <int V>
+__device__ __forceinline__ void fwht_quad(float (&y)[V], int r) {
+#pragma unroll
+  for (int h = 1; h < V; h <<= 1)
+#pragma unroll
+    for (int j = 0; j < V; ++j)
+      if ((j & h) == 0) {
+        const float a = y[j], b = y[j + h];
+        y[j] = a + b;
+        y[j + h] = a - b;
+      }
+  {
+    const float sg = (r & 1) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) y[i] = __builtin_fmaf(y[i], sg, xor_lane<1>(y[i]));
+  }
+  {
+    const float sg = (r & 2) ? -1.0f : 1.0f;
+#pragma unroll
+    for (int i = 0; i < V; ++i) y[i] = __builtin_fmaf(y[i], sg, xor_lane<2>(y[i]));
+  }
 }
 
-// Compute units of the device current at the first call (initialised once,
-// safe under concurrent first calls).
-static int dec_cu_count() {
-  static const int cus = [] {
-    int dev = 0, n = 0;
-    (void)hipGetDevice(&dev);
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1) n = 256;
-    return n;
-  }();
-  return cus;
+// Tiles of 128 channels: the same group, region and metadata as k_decode, but
+// each tile is rebuilt by a quad of lanes, sixteen tiles per pass: lane r of
+// a quad takes elements 32 r ... 32 r + 31 (its codes are the 4-byte-aligned
+// words r b ... r b + b - 1 of the code block, unpacked as a 32-element
+// block), dequantizes them, a flagged tile applies H^T / G with fwht_quad and
+// the quad undoes the pivot swap with two shuffles; the pass's sixteen rows
+// then leave through LDS with 16-byte coalesced stores. A lane holds 32
+// values instead of a whole tile: about 80 VGPRs and 15-19 KB of LDS per
+// workgroup instead of all 512 registers and 39-43 KB.
+template <int G, typename TOut, int MAXB, bool MULTI>
+__global__ __launch_bounds__(64) void k_decode4(DecArgs a) {
+  constexpr int NT = 64;
+  constexpr int V = G / 4;  // elements per lane of a quad
+  constexpr int TP = NT / 4;  // tiles per pass
+  constexpr int RB = G * Elem<TOut>::kBytes;  // output row bytes
+  using RR = RegionRegs<G, NT, MAXB>;
+  __shared__ __attribute__((aligned(16))) u32x4 region[NT * RR::kChunks];
+  __shared__ __attribute__((aligned(16))) uint8_t ys[TP * RB];
+  __shared__ uint32_t m_off[NT], m_bfp[NT];
+  __shared__ float m_s[NT], m_lo[NT];
+
+  const int lane = threadIdx.x;
+  const int64_t ngroups = (a.tiles + NT - 1) / NT;
+  const int64_t g = blockIdx.x;
+  // the group's metadata first: its loads are in flight during the header check
+  DecMeta m;
+  if (g < ngroups) load_meta<NT, MULTI>(a, g, m);
+  {  // header
+    bool mism = false;
+    if (lane < 32) {
+      uint32_t got = reinterpret_cast<const uint32_t*>(a.payload)[lane];
+      uint32_t want = a.expect.w[lane];
+      if (lane == 1) {  // byte 6 records the encoder's input dtype: 0 or 1
+        mism = ((got >> 16) & 0xffu) > 1u;
+        got &= 0xff00ffffu;
+        want &= 0xff00ffffu;
+      }
+      mism = mism || got != want;
+    }
+    const bool bad = ballot(mism) != 0;
+    if (blockIdx.x == 0 && lane == 0) *a.status = bad ? (int32_t)TAH_ERR_BAD_PAYLOAD : (int32_t)TAH_OK;
+    if (bad) return;
+  }
+  if (g >= ngroups) return;
+  const int64_t t0 = g * NT;
+  const int n = (int)((a.tiles - t0) < NT ? (a.tiles - t0) : NT);
+  int64_t rs;
+  int rlen;
+  region_of<NT, MULTI>(a, g, m, rs, rlen);
+  {
+    RR rr;
+    load_region<G, NT>(a, rs, rlen, rr);
+#pragma unroll
+    for (int i = 0; i < RR::kChunks; ++i) region[lane + i * NT] = rr.c[i];
+  }
+
+  // ---------------- per tile (lane owns tile t0 + lane): width, offset ----------------
+  {
+    const bool act = lane < n;
+    const uint64_t bm = ((uint64_t)m.bm1 << 32) | m.bm0;
+    const int hi = act ? (int)((bm >> lane) & 1u) : 0;
+    const int flag = act ? (int)(m.side >> 7) : 0;
+    const int piv = (int)(m.side & (G - 1));  // a corrupt pivot must not index outside the tile
+    int b, sz, lane_off;
+    if constexpr (MULTI) {
+      const int unit = a.sz_lo / a.b_lo;  // G/8
+      b = act ? level_width(a, m, lane) : 0;
+      int incl = b;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += o;
+      }
+      sz = unit * b;
+      lane_off = unit * (incl - b);
+    } else {
+      b = hi ? a.b_hi : a.b_lo;
+      sz = hi ? a.sz_hi : a.sz_lo;
+      lane_off = lane * a.sz_lo + (int)lanes_below(bm) * (a.sz_hi - a.sz_lo);
+    }
+    int off = (int)(rs & 15) + lane_off;
+    const int cap = RR::kChunks * NT * 16 - sz;
+    off = off < cap ? off : 0;  // stays inside the region buffer on a corrupt table
+    m_off[lane] = (uint32_t)off;
+    m_bfp[lane] = (uint32_t)b | ((uint32_t)flag << 8) | ((uint32_t)piv << 16);
+    m_s[lane] = __uint_as_float(m.scale << 16);
+    m_lo[lane] = m.zero;
+  }
+  __syncthreads();
+
+  // ---------------- quads, sixteen tiles per pass ----------------
+  const int q = lane >> 2, r = lane & 3, qb = lane & ~3;
+  for (int j0 = 0; j0 < n; j0 += TP) {
+    const int j = j0 + q;
+    if (j < n) {  // a whole quad takes a tile or none
+      const uint32_t e = m_bfp[j];
+      const int b = (int)(e & 255u), flag = (int)((e >> 8) & 1u), piv = (int)(e >> 16);
+      float y[V];
+      // block offsets are multiples of G/8 = 16 bytes, so this lane's V b
+      // bits start on a 4-byte boundary
+      load_dequant_b<V>(b, reinterpret_cast<const uint8_t*>(region) + m_off[j] + r * (V * b / 8), m_s[j],
+                        m_lo[j], y);
+      if (flag) {  // the same for the quad's four lanes
+        fwht_quad<V>(y, r);
+#pragma unroll
+        for (int i = 0; i < V; ++i) y[i] = y[i] * (1.0f / G);
+        // element d takes y_0, element 0 takes y_d
+        const int dl = piv / V, ds = piv % V;
+        float mine = y[0];
+#pragma unroll
+        for (int i = 1; i < V; ++i) mine = ds == i ? y[i] : mine;
+        const float y0 = __shfl(y[0], qb, 64);
+        const float yd = __shfl(mine, qb + dl, 64);
+        if (r == 0) y[0] = yd;
+        if (r == dl) {
+#pragma unroll
+          for (int i = 0; i < V; ++i) y[i] = ds == i ? y0 : y[i];
+        }
+      }
+      lds_write_part<V, TOut>(ys + q * RB, r, y);
+    }
+    __syncthreads();
+    // the pass's rows out: 16-byte chunks, consecutive lanes on consecutive chunks
+    const int nrow = n - j0 < TP ? n - j0 : TP;
+    const int nch = nrow * (RB / 16);
+    uint4* dst = reinterpret_cast<uint4*>(a.y + (t0 + j0) * (int64_t)RB);
+#pragma unroll
+    for (int i = 0; i < TP * RB / 16 / NT; ++i) {
+      const int c = lane + i * NT;
+      if (c < nch) store_stream(dst + c, reinterpret_cast<const uint4*>(ys)[c]);
+    }
+    __syncthreads();  // the rows are rewritten by the next pass
+  }
 }
 
-// Tiles of up to 64 channels: one workgroup per group (8192 x 8192 bf16
-// decode 29.9 -> 27.2 us, the 80/20 one 31.8 -> 30.2 us against a persistent
-// grid of the resident workgroups, one box, interleaved); tiles of 128 fp32
-// channels keep the persistent grid and its pipeline across groups (16384 x
-// 5120: 100.4 against 108.3 us with a workgroup per group).
+// One workgroup per group (8192 x 8192 bf16 decode 29.9 -> 27.2 us, the
+// 80/20 one 31.8 -> 30.2 us against a persistent grid of the resident
+// workgroups, one box, interleaved). Tiles of 128 channels take k_decode4.
 template <int G, typename TOut, int MAXB, bool MULTI>
 static hipError_t launch_dec_b(const DecArgs& a, hipStream_t st) {
-  const int64_t ngroups = a.tiles > 0 ? (a.tiles + 63) / 64 : 1;
-  int64_t nwg = ngroups;
-  if constexpr (G > 64) {
-    static const int per_cu = dec_wgs_per_cu(k_decode<G, TOut, MAXB, MULTI>);
-    const int64_t resident = (int64_t)per_cu * dec_cu_count();
-    nwg = ngroups < resident ? ngroups : resident;
-  }
-  hipLaunchKernelGGL((k_decode<G, TOut, MAXB, MULTI>), dim3((unsigned)nwg), dim3(64), 0, st, a);
+  const int64_t nwg = a.tiles > 0 ? (a.tiles + 63) / 64 : 1;
+  if constexpr (G > 64)
+    hipLaunchKernelGGL((k_decode4<G, TOut, MAXB, MULTI>), dim3((unsigned)nwg), dim3(64), 0, st, a);
+  else
+    hipLaunchKernelGGL((k_decode<G, TOut, MAXB, MULTI>), dim3((unsigned)nwg), dim3(64), 0, st, a);
   return hipGetLastError();
 }
 
