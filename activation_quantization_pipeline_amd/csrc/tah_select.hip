@@ -65,7 +65,27 @@ struct StatsArgs {
   float tau;
   int64_t tiles, hist_words;
   int32_t init;
+  // SUMS with kA dividing 64: each workgroup's 64 quantization tiles hold
+  // whole allocation tiles, whose entropies it then forms itself into h
+  int32_t kA_fused;
 };
+
+// An allocation tile's entropy from its kA quantization tiles' sums in LDS
+// (lsum / ssum, the workgroup's tiles in order), added left to right from 0
+// as k_alloc_entropy adds them; lane u < n / kA writes allocation tile
+// t0 / kA + u. Called by every lane of the workgroup.
+__device__ __forceinline__ void fused_alloc_entropy(const StatsArgs& a, const float* lsum, const float* ssum,
+                                                    const float* lt, int64_t t0, int n, int tid) {
+  const int kA = a.kA_fused;
+  if (tid < n / kA) {
+    float L = 0.0f, S = 0.0f;
+    for (int gq = 0; gq < kA; ++gq) {
+      L = L + lsum[tid * kA + gq];
+      S = S + ssum[tid * kA + gq];
+    }
+    a.h[t0 / kA + tid] = entropy_from_sums(L, S, lt);
+  }
+}
 
 // Tiles (= threads) per workgroup of the statistics pass for rows of up to 128
 // bytes: one-wavefront workgroups, so 4096 x 2048 bf16 (131,072 tiles)
@@ -87,6 +107,7 @@ __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsA
   using RI = TileRow<G, TIn>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[NT * RI::kStride];
   __shared__ __attribute__((aligned(16))) float lt[256];  // log2 tables of the entropy
+  __shared__ float lsum[SUMS ? NT : 1], ssum[SUMS ? NT : 1];
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * NT;
   if (a.init) {  // the first selection pass's histograms start at zero
@@ -112,10 +133,23 @@ __global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsA
 #pragma unroll
       for (int k = 0; k < G; ++k) l1 = l1 + fabsf(v[k]);
     }
-    if constexpr (SUMS)
-      a.ls[t0 + tid] = make_float2(l1, tile_logsum<G, Elem<TIn>::kBytes == 2>(v, lt));
-    else
+    if constexpr (SUMS) {
+      const float S = tile_logsum<G, Elem<TIn>::kBytes == 2>(v, lt);
+      if (a.kA_fused) {
+        lsum[tid] = l1;
+        ssum[tid] = S;
+      } else {
+        a.ls[t0 + tid] = make_float2(l1, S);
+      }
+    } else {
       a.h[t0 + tid] = tile_entropy<G, Elem<TIn>::kBytes == 2>(v, l1, lt);  // Eq. (1)-(2)
+    }
+  }
+  if constexpr (SUMS) {
+    if (a.kA_fused) {
+      __syncthreads();
+      fused_alloc_entropy(a, lsum, ssum, lt, t0, n, tid);
+    }
   }
 }
 
@@ -142,6 +176,7 @@ __global__ __launch_bounds__(64) void k_stats_rounds(StatsArgs a) {
   static_assert(R >= 2 && R * 128 == kBytes, "rows of whole 128-byte rounds");
   __shared__ __attribute__((aligned(16))) uint8_t xs[NT * kStride];
   __shared__ __attribute__((aligned(16))) float lt[256];  // log2 tables of the entropy
+  __shared__ float lsum[SUMS ? NT : 1], ssum[SUMS ? NT : 1];
   const int tid = threadIdx.x;
   const int64_t t0 = (int64_t)blockIdx.x * NT;
   if (a.init) {  // the first selection pass's histograms start at zero
@@ -257,9 +292,20 @@ __global__ __launch_bounds__(64) void k_stats_rounds(StatsArgs a) {
     }
     if constexpr (SUMS) {
       asm volatile("" : "+v"(S));  // the sum is complete here
-      a.ls[t0 + tid] = make_float2(s, S);
+      if (a.kA_fused) {
+        lsum[tid] = s;
+        ssum[tid] = S;
+      } else {
+        a.ls[t0 + tid] = make_float2(s, S);
+      }
     } else {
       a.h[t0 + tid] = entropy_from_sums(s, S, lt);  // Eq. (1)-(2)
+    }
+  }
+  if constexpr (SUMS) {
+    if (a.kA_fused) {
+      __syncthreads();
+      fused_alloc_entropy(a, lsum, ssum, lt, t0, n, tid);
     }
   }
 }
@@ -321,6 +367,8 @@ hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, b
   a.hist_words = init_select ? pl.nsamples * kBins : 0;
   a.init = init_select ? 1 : 0;
   const bool bf = pl.x_dtype == TAH_DTYPE_BF16, sums = pl.kA > 1;
+  // every statistics workgroup takes 64 quantization tiles, from a multiple of 64
+  a.kA_fused = (sums && 64 % pl.kA == 0) ? (int32_t)pl.kA : 0;
   hipError_t e;
   switch (pl.G) {
     case 32: e = bf ? launch_stats_t<32, bf16_t>(a, sums, st) : launch_stats_t<32, float>(a, sums, st); break;
@@ -328,7 +376,7 @@ hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, b
     case 128: e = bf ? launch_stats_t<128, bf16_t>(a, sums, st) : launch_stats_t<128, float>(a, sums, st); break;
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess || !sums || pl.atiles == 0) return e;
+  if (e != hipSuccess || !sums || a.kA_fused || pl.atiles == 0) return e;
   hipLaunchKernelGGL(k_alloc_entropy, dim3((unsigned)((pl.atiles + 255) / 256)), dim3(256), 0, st,
                      (const float2*)a.ls, h_out, pl.atiles, pl.kA);
   return hipGetLastError();
