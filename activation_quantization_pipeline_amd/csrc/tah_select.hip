@@ -8,7 +8,8 @@
 //              the selection state and histograms. When an allocation tile
 //              spans kA > 1 quantization tiles, the lane writes the tile's two
 //              sums (L, S) instead and k_alloc_entropy adds them up per
-//              allocation tile, left to right, into its entropy;
+//              allocation tile, left to right, into its entropy (when kA
+//              divides 64 the workgroup adds them itself);
 //   k_hist   - one launch per digit pass. Each workgroup first applies the
 //              previous pass (one wavefront reads that pass's histogram of the
 //              sample in coalesced slices and finds the digit that holds rank
