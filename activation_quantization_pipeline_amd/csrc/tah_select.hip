@@ -399,6 +399,7 @@ struct HistArgs {
   int64_t N, nsamples, chunks_per_sample, k, ncand, cand_stride;
   SelectPass pass, prev;
   int32_t has_prev, fold;
+  int32_t kA;  // fold: quantization tiles per allocation tile (a power of two up to 64)
 };
 
 // Large workgroups of P keys per thread (a chunk of 1024 P keys each, whole
@@ -510,9 +511,26 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
         const uint64_t m = ballot(sure);
         const int64_t ub = u0 + i * kHistThreads + (tid & ~63);
         if (ub < a.N) {
-          const int64_t run = (s * a.N + ub) >> 6;
-          if (lane < 2) a.fold_bitmap[2 * run + lane] = (uint32_t)(m >> (32 * lane));
-          if (lane == 0) a.fold_run[run] = (uint32_t)__popcll(m);
+          if (a.kA == 1) {
+            const int64_t run = (s * a.N + ub) >> 6;
+            if (lane < 2) a.fold_bitmap[2 * run + lane] = (uint32_t)(m >> (32 * lane));
+            if (lane == 0) a.fold_run[run] = (uint32_t)__popcll(m);
+          } else {
+            // the 64 allocation tiles are kA runs of 64 quantization tiles:
+            // each allocation tile's bit kA times, and each run's count
+            const int lk = __ffs(a.kA) - 1, per = 64 >> lk;  // allocation tiles per run
+            const int64_t run0 = ((s * a.N + ub) << lk) >> 6;
+            for (int wv = lane; wv < 2 * a.kA; wv += 64) {
+              uint32_t word = 0u;
+#pragma unroll
+              for (int bq = 0; bq < 32; ++bq) word |= (uint32_t)((m >> ((32 * wv + bq) >> lk)) & 1ull) << bq;
+              a.fold_bitmap[2 * run0 + wv] = word;
+            }
+            if (lane < a.kA) {
+              const uint64_t sel = per == 64 ? m : (m >> (lane * per)) & ((1ull << per) - 1ull);
+              a.fold_run[run0 + lane] = (uint32_t)a.kA * (uint32_t)__popcll(sel);
+            }
+          }
         }
       }
     }
@@ -577,6 +595,7 @@ struct ResolveArgs {
   int64_t N, ncand, cand_stride, k;
   SelectPass last;
   int32_t nidx, fold;
+  int32_t kA;  // fold: quantization tiles per allocation tile
   SelectPass idx[kMaxPasses];
 };
 
@@ -593,7 +612,7 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
   // fold: the sample's run counts, loaded first (in flight during the rest)
   constexpr int kRound = 4 * kResolveThreads;
   constexpr int kPer = (int)(kFoldMaxRuns / kResolveThreads);
-  const int64_t runs = a.N / 64, r0 = s * runs;
+  const int64_t runs = a.N * a.kA / 64, r0 = s * runs;
   const int nr = a.fold ? (int)((runs + kRound - 1) / kRound) : 0;
   uint32_t rv[kPer];
 #pragma unroll
@@ -707,16 +726,24 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
         uu = (uint32_t)i;
       }
       if ((key >> hs) == (S.key >> hs) && (key > S.key || (key == S.key && uu <= S.upos))) {
-        const int64_t t = s * a.N + uu;
-        atomicOr(&a.fold_bitmap[t >> 5], 1u << (t & 31));
-        atomicAdd(&rc[uu >> 6], 1u);
+        // the allocation tile's kA quantization tiles (kA divides 64: one
+        // run, and one word unless kA = 64)
+        const int64_t t = (s * a.N + uu) * a.kA;
+        if (a.kA == 64) {
+          atomicOr(&a.fold_bitmap[t >> 5], ~0u);
+          atomicOr(&a.fold_bitmap[(t >> 5) + 1], ~0u);
+        } else {
+          const uint32_t ones = a.kA == 32 ? ~0u : ((1u << a.kA) - 1u);
+          atomicOr(&a.fold_bitmap[t >> 5], ones << (t & 31));
+        }
+        atomicAdd(&rc[((int64_t)uu * a.kA) >> 6], (uint32_t)a.kA);
       }
     }
     __syncthreads();
     // block table: every earlier sample holds k upgraded tiles, then the
     // exclusive scan of this sample's run counts
-    lds_scan_store<kResolveThreads, (int)(kFoldMaxRuns / kRound)>(rc, nr, (uint32_t)s * (uint32_t)a.k,
-                                                                    a.table + r0, runs, wsum);
+    lds_scan_store<kResolveThreads, (int)(kFoldMaxRuns / kRound)>(
+        rc, nr, (uint32_t)s * (uint32_t)a.k * (uint32_t)a.kA, a.table + r0, runs, wsum);
   }
   if (tid == 0) a.st_out[s] = S;
 }
@@ -1022,6 +1049,12 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   h.cand_stride = pl.cand_stride;
   h.fold_bitmap = reinterpret_cast<uint32_t*>(P ? P + pl.off_bitmap : w + pl.ws_bitmap);
   h.fold_run = reinterpret_cast<uint32_t*>(w + pl.ws_blockcnt);
+  // the fold also covers allocation tiles of kA quantization tiles when kA
+  // divides 64 and samples are whole runs of 64 allocation tiles
+  const bool fold_wide = pl.mode == 1 && pl.kA > 1 && 64 % pl.kA == 0 && pl.N % 64 == 0 && pl.N > kLdsSelect &&
+                         pl.N * pl.kA / 64 <= kFoldMaxRuns;
+  const bool fold = pl.fold || fold_wide;
+  h.kA = fold_wide ? (int32_t)pl.kA : 1;
   const int64_t nwg = h.chunks_per_sample * pl.nsamples;
   // entropy-key passes; pass p: state p in states[p % 2], histogram p in
   // hists[p % 3] (zeroed by k_stats for p = 0). The tile-index passes that
@@ -1037,7 +1070,7 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
     h.hist_prev = hists + ((p + 2) % 3) * hsz;
     h.hist_cur = hists + (p % 3) * hsz;
     h.hist_clear = hists + ((p + 1) % 3) * hsz;
-    h.fold = pl.fold && h.pass.last_h;
+    h.fold = fold && h.pass.last_h;
     if (per == 1) hipLaunchKernelGGL(k_hist<1>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
     else if (per == 2) hipLaunchKernelGGL(k_hist<2>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
     else if (per == 4) hipLaunchKernelGGL(k_hist<4>, dim3((unsigned)nwg), dim3(kHistThreads), 0, st, h);
@@ -1062,17 +1095,19 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   rs.fold_run = h.fold_run;
   rs.table = reinterpret_cast<uint32_t*>(P ? P + pl.off_table : w + pl.ws_table);
   rs.k = pl.k;
-  rs.fold = pl.fold;
+  rs.fold = fold;
+  rs.kA = h.kA;
   static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(k_resolve),
                                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                                      (int)(4 * kFoldMaxRuns));
   if (attr != hipSuccess) return attr;
   // the run counts in whole rounds of 4 per thread
   const int64_t rc_round = 4 * kResolveThreads;
-  const size_t rc_bytes = pl.fold ? (size_t)(4 * ((pl.N / 64 + rc_round - 1) / rc_round) * rc_round) : 0;
+  const int64_t nruns = pl.N * h.kA / 64;
+  const size_t rc_bytes = fold ? (size_t)(4 * ((nruns + rc_round - 1) / rc_round) * rc_round) : 0;
   hipLaunchKernelGGL(k_resolve, dim3((unsigned)pl.nsamples), dim3(kResolveThreads), rc_bytes, st, rs);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || pl.fold) return e;  // fold: width map and block table are complete
+  if (e != hipSuccess || fold) return e;  // fold: width map and block table are complete
   return mark_and_table(pl, P, w, rs.st_out, st);
 }
 

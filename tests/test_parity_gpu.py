@@ -550,6 +550,40 @@ def test_threshold_inside_a_tie_in_a_large_sample(n_tied):
     assert hi[tied_idx[:n_sel]].all() and not hi[tied_idx[n_sel:]].any()
 
 
+@pytest.mark.parametrize("n_tied", [3, 65, 6000])
+def test_threshold_inside_a_tie_with_allocation_tiles(n_tied):
+    """The same construction over allocation tiles of 256 channels (four
+    quantization tiles of 64): one sample of 40960 allocation tiles, whose
+    width-map bits and block table come from the last select pass and the
+    tie step (four bits per allocation tile), with the threshold inside a
+    class of n_tied equal allocation tiles (one wavefront, digit passes over
+    the list, and the list overflowing)."""
+    rng = np.random.default_rng(57 + n_tied)
+    T, H, G, A = 2560, 4096, 64, 256
+    na = T * H // A
+    n_flat = na // 2 - n_tied // 2
+    kind = np.full(na, 2)
+    idx = rng.permutation(na)
+    kind[idx[:n_flat]] = 0
+    kind[idx[n_flat:n_flat + n_tied]] = 1
+    flat = rng.uniform(0.9, 1.1, (na, A)) * rng.choice([-1, 1], (na, A))
+    spiky = rng.standard_normal((na, A)) * 0.01
+    spiky[np.arange(na), rng.integers(A, size=na)] = 5.0
+    tied = np.where(np.arange(A) % 2 == 0, 1.0, 0.0) * np.linspace(0.5, 1.5, A)
+    tiles = np.where((kind == 0)[:, None], flat, np.where((kind == 1)[:, None], tied[None, :], spiky))
+    x = tiles.reshape(T, H).astype(np.float32)
+    p = P(tile=G, tokens_per_sample=0, bit_budget=3.5, candidates=(3, 4), tau=2.0, alloc_tile=A)
+    pl = oracle.plan(T, H, p)
+    assert pl["k"] == na // 2 and pl["atiles_per_sample"] == na
+    R, _ = run_case(x, p, f"tie over allocation tiles, {n_tied} tied")
+    bm = R[pl["off_bitmap"]:pl["off_bitmap"] + 8 * pl["nblocks"]].view(np.uint64)
+    hi = np.unpackbits(bm.view(np.uint8), bitorder="little")[:T * H // G].astype(bool).reshape(na, A // G)
+    tied_idx = np.flatnonzero(kind == 1)
+    n_sel = na // 2 - n_flat
+    assert hi[kind == 0].all() and not hi[kind == 2].any()
+    assert hi[tied_idx[:n_sel]].all() and not hi[tied_idx[n_sel:]].any()
+
+
 @pytest.mark.parametrize("S,ns", [(65, 5), (193, 3), (1024, 2)])
 def test_counts_in_place_of_the_block_table(S, ns):
     """Samples of whole runs of 64 tiles above the one-workgroup select: the
