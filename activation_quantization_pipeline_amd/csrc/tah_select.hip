@@ -33,11 +33,13 @@
 //              selected tie; per-64-tile counts;
 //   k_table  - exclusive scan of those counts: b_hi tiles before each run of
 //              64 tiles, which locates every variable-width code block.
-// When allocation tiles are quantization tiles and samples are whole runs of
-// 64 tiles (at most kFoldMaxRuns of them), k_mark and k_table do not run: the
-// last k_hist pass writes the width-map bits of the keys above the threshold's
-// prefix and each run's count, and k_resolve adds the selected keys that
-// match the prefix and scans the run counts into the block table.
+// When samples are whole runs of 64 allocation tiles (at most kFoldMaxRuns
+// runs of quantization tiles) and an allocation tile is 1, 2, 4, ... or 64
+// quantization tiles, k_mark and k_table do not run: the last k_hist pass
+// writes the width-map bits of the keys above the threshold's prefix (each
+// allocation tile's bit once per quantization tile) and each run's count, and
+// k_resolve adds the selected keys that match the prefix and scans the run
+// counts into the block table.
 // Samples of at most kLdsSelect keys skip k_hist and k_resolve: one
 // workgroup per sample (k_select_lds) holds the keys in LDS, runs every digit
 // pass there and, when samples cover whole runs of 64 tiles, writes the width
