@@ -104,9 +104,8 @@ constexpr int stats_tiles_per_wg() {
 // SIDE: also the outlier test of Eq. (3), m1 > tau (m2 + rho), and the side
 // byte (bit 7 the flag, bits 0-6 the pivot of a transformed tile), which the
 // mixed-width encoder then reads instead of finding the top two magnitudes.
-template <int G, typename TIn, bool SUMS, bool SIDE>
-__global__ __launch_bounds__((stats_tiles_per_wg<G, TIn>())) void k_stats(StatsArgs a) {
-  constexpr int NT = stats_tiles_per_wg<G, TIn>();
+template <int G, typename TIn, bool SUMS, bool SIDE, int NT = stats_tiles_per_wg<G, TIn>()>
+__global__ __launch_bounds__(NT) void k_stats(StatsArgs a) {
   using RI = TileRow<G, TIn>;
   __shared__ __attribute__((aligned(16))) uint8_t xs[NT * RI::kStride];
   __shared__ __attribute__((aligned(16))) float lt[256];  // log2 tables of the entropy
@@ -344,6 +343,13 @@ static hipError_t launch_stats_t(const StatsArgs& a, bool sums, hipStream_t st) 
     else if (sums) hipLaunchKernelGGL((k_stats_rounds<G, TIn, true, false>), grid, block, 0, st, a);
     else if (a.side) hipLaunchKernelGGL((k_stats_rounds<G, TIn, false, true>), grid, block, 0, st, a);
     else hipLaunchKernelGGL((k_stats_rounds<G, TIn, false, false>), grid, block, 0, st, a);
+  } else if (sums && a.kA_fused == 128) {
+    // token-level allocation over 128 quantization tiles: two-wavefront
+    // workgroups of 128 tiles, so that each holds whole allocation tiles
+    const int64_t nwg = a.tiles > 0 ? (a.tiles + 127) / 128 : 1;
+    const dim3 grid((unsigned)nwg), block(128);
+    if (a.side) hipLaunchKernelGGL((k_stats<G, TIn, true, true, 128>), grid, block, 0, st, a);
+    else hipLaunchKernelGGL((k_stats<G, TIn, true, false, 128>), grid, block, 0, st, a);
   } else {
     constexpr int NT = stats_tiles_per_wg<G, TIn>();
     const int64_t nwg = a.tiles > 0 ? (a.tiles + NT - 1) / NT : 1;
@@ -370,8 +376,10 @@ hipError_t launch_stats(const Plan& pl, const void* x, float* h_out, void* ws, b
   a.hist_words = init_select ? pl.nsamples * kBins : 0;
   a.init = init_select ? 1 : 0;
   const bool bf = pl.x_dtype == TAH_DTYPE_BF16, sums = pl.kA > 1;
-  // every statistics workgroup takes 64 quantization tiles, from a multiple of 64
-  a.kA_fused = (sums && 64 % pl.kA == 0) ? (int32_t)pl.kA : 0;
+  // every statistics workgroup takes 64 quantization tiles, from a multiple of
+  // 64 (128 for allocation tiles of 128 rows of at most 128 bytes)
+  const bool narrow = pl.G * (bf ? 2 : 4) <= 128;
+  a.kA_fused = (sums && (64 % pl.kA == 0 || (pl.kA == 128 && narrow))) ? (int32_t)pl.kA : 0;
   hipError_t e;
   switch (pl.G) {
     case 32: e = bf ? launch_stats_t<32, bf16_t>(a, sums, st) : launch_stats_t<32, float>(a, sums, st); break;
@@ -401,7 +409,7 @@ struct HistArgs {
   int64_t N, nsamples, chunks_per_sample, k, ncand, cand_stride;
   SelectPass pass, prev;
   int32_t has_prev, fold;
-  int32_t kA;  // fold: quantization tiles per allocation tile (a power of two up to 64)
+  int32_t kA;  // fold: quantization tiles per allocation tile (a power of two)
 };
 
 // Large workgroups of P keys per thread (a chunk of 1024 P keys each, whole
@@ -520,17 +528,27 @@ __global__ __launch_bounds__(kHistThreads) void k_hist(HistArgs a) {
           } else {
             // the 64 allocation tiles are kA runs of 64 quantization tiles:
             // each allocation tile's bit kA times, and each run's count
-            const int lk = __ffs(a.kA) - 1, per = 64 >> lk;  // allocation tiles per run
+            const int lk = __ffs(a.kA) - 1;
             const int64_t run0 = ((s * a.N + ub) << lk) >> 6;
             for (int wv = lane; wv < 2 * a.kA; wv += 64) {
               uint32_t word = 0u;
+              if (lk >= 5) {  // a word inside one allocation tile
+                word = ((m >> ((32 * wv) >> lk)) & 1ull) ? ~0u : 0u;
+              } else {
 #pragma unroll
-              for (int bq = 0; bq < 32; ++bq) word |= (uint32_t)((m >> ((32 * wv + bq) >> lk)) & 1ull) << bq;
+                for (int bq = 0; bq < 32; ++bq) word |= (uint32_t)((m >> ((32 * wv + bq) >> lk)) & 1ull) << bq;
+              }
               a.fold_bitmap[2 * run0 + wv] = word;
             }
-            if (lane < a.kA) {
-              const uint64_t sel = per == 64 ? m : (m >> (lane * per)) & ((1ull << per) - 1ull);
-              a.fold_run[run0 + lane] = (uint32_t)a.kA * (uint32_t)__popcll(sel);
+            for (int rk = lane; rk < a.kA; rk += 64) {
+              uint32_t cnt;
+              if (lk >= 6) {  // a run inside one allocation tile
+                cnt = ((m >> ((64 * rk) >> lk)) & 1ull) ? 64u : 0u;
+              } else {
+                const int per = 64 >> lk;  // allocation tiles per run
+                cnt = (uint32_t)a.kA * (uint32_t)__popcll((m >> (rk * per)) & ((1ull << per) - 1ull));
+              }
+              a.fold_run[run0 + rk] = cnt;
             }
           }
         }
@@ -731,14 +749,16 @@ __global__ __launch_bounds__(kResolveThreads) void k_resolve(ResolveArgs a) {
         // the allocation tile's kA quantization tiles (kA divides 64: one
         // run, and one word unless kA = 64)
         const int64_t t = (s * a.N + uu) * a.kA;
-        if (a.kA == 64) {
-          atomicOr(&a.fold_bitmap[t >> 5], ~0u);
-          atomicOr(&a.fold_bitmap[(t >> 5) + 1], ~0u);
+        if (a.kA >= 32) {
+          for (int wv = 0; wv < a.kA / 32; ++wv) atomicOr(&a.fold_bitmap[(t >> 5) + wv], ~0u);
         } else {
-          const uint32_t ones = a.kA == 32 ? ~0u : ((1u << a.kA) - 1u);
-          atomicOr(&a.fold_bitmap[t >> 5], ones << (t & 31));
+          atomicOr(&a.fold_bitmap[t >> 5], ((1u << a.kA) - 1u) << (t & 31));
         }
-        atomicAdd(&rc[((int64_t)uu * a.kA) >> 6], (uint32_t)a.kA);
+        if (a.kA >= 64) {
+          for (int rk = 0; rk < a.kA / 64; ++rk) atomicAdd(&rc[(((int64_t)uu * a.kA) >> 6) + rk], 64u);
+        } else {
+          atomicAdd(&rc[((int64_t)uu * a.kA) >> 6], (uint32_t)a.kA);
+        }
       }
     }
     __syncthreads();
@@ -1053,8 +1073,8 @@ hipError_t launch_select(const Plan& pl, void* payload, void* ws, hipStream_t st
   h.fold_run = reinterpret_cast<uint32_t*>(w + pl.ws_blockcnt);
   // the fold also covers allocation tiles of kA quantization tiles when kA
   // divides 64 and samples are whole runs of 64 allocation tiles
-  const bool fold_wide = pl.mode == 1 && pl.kA > 1 && 64 % pl.kA == 0 && pl.N % 64 == 0 && pl.N > kLdsSelect &&
-                         pl.N * pl.kA / 64 <= kFoldMaxRuns;
+  const bool fold_wide = pl.mode == 1 && pl.kA > 1 && (pl.kA & (pl.kA - 1)) == 0 && pl.N % 64 == 0 &&
+                         pl.N > kLdsSelect && pl.N * pl.kA / 64 <= kFoldMaxRuns;
   const bool fold = pl.fold || fold_wide;
   h.kA = fold_wide ? (int32_t)pl.kA : 1;
   const int64_t nwg = h.chunks_per_sample * pl.nsamples;

@@ -550,16 +550,17 @@ def test_threshold_inside_a_tie_in_a_large_sample(n_tied):
     assert hi[tied_idx[:n_sel]].all() and not hi[tied_idx[n_sel:]].any()
 
 
-@pytest.mark.parametrize("n_tied", [3, 65, 6000])
-def test_threshold_inside_a_tie_with_allocation_tiles(n_tied):
-    """The same construction over allocation tiles of 256 channels (four
-    quantization tiles of 64): one sample of 40960 allocation tiles, whose
-    width-map bits and block table come from the last select pass and the
-    tie step (four bits per allocation tile), with the threshold inside a
+@pytest.mark.parametrize("A,T,n_tied", [(256, 2560, 3), (256, 2560, 65), (256, 2560, 6000), (4096, 5120, 3),
+                                         (4096, 5120, 200)])
+def test_threshold_inside_a_tie_with_allocation_tiles(A, T, n_tied):
+    """The same construction over allocation tiles of A channels (4 or 64
+    quantization tiles of 64): one sample of 40960 or 5120 allocation tiles,
+    whose width-map bits and block table come from the last select pass and
+    the tie step (one bit per quantization tile), with the threshold inside a
     class of n_tied equal allocation tiles (one wavefront, digit passes over
     the list, and the list overflowing)."""
-    rng = np.random.default_rng(57 + n_tied)
-    T, H, G, A = 2560, 4096, 64, 256
+    rng = np.random.default_rng(57 + n_tied + A)
+    H, G = 4096, 64
     na = T * H // A
     n_flat = na // 2 - n_tied // 2
     kind = np.full(na, 2)
